@@ -1,0 +1,173 @@
+"""Seeded synthetic inputs for the attention path (no attention arithmetic here).
+
+Both the GPU library's tests/benchmark and the fp64 oracle consume exactly the
+arrays produced here, so an error measures the kernel, not the input cast.
+
+Recipe (stands in for the activations of the model the pages serve; no weights,
+prompts or datasets are involved):
+  * values are drawn with numpy ``default_rng(seed)`` (PCG64) ``standard_normal``
+    in float64, cast to float32, and for bf16 workloads rounded to bfloat16
+    (round to nearest even, done by PyTorch's CPU cast);
+  * draw order: Q, then K, then V (prefill and contiguous decode); for the paged
+    decode workload: Q, sequence lengths, page permutation, K pool, V pool;
+  * big tensors are drawn one head-slab at a time from the same generator, which
+    yields the same stream as one large draw while bounding host memory.
+
+Layouts (all contiguous, row-major):
+  prefill      q, o: [B, Hq, N, d]      k, v: [B, Hkv, N, d]
+  decode       q, o: [B, Hq, d]
+               contiguous cache  k, v: [B, S, Hkv, d]
+               paged cache       k, v: [num_pages, page_size, Hkv, d]
+               block_table int32 [B, max_blocks] (unused slots = -1), seq_lens int32 [B]
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+F32 = "f32"
+BF16 = "bf16"
+
+_SLAB = 1 << 22  # values per draw (32 MiB of float64)
+
+
+def _draw(rng: np.random.Generator, shape, dtype: str) -> torch.Tensor:
+    """N(0,1) draw of `shape`, float64 -> float32 (-> bfloat16 RNE), as a CPU tensor."""
+    n = int(np.prod(shape)) if len(shape) else 1
+    out = torch.empty(n, dtype=torch.float32 if dtype == F32 else torch.bfloat16)
+    pos = 0
+    while pos < n:
+        m = min(_SLAB, n - pos)
+        x = rng.standard_normal(m).astype(np.float32)
+        out[pos:pos + m] = torch.from_numpy(x).to(out.dtype)
+        pos += m
+    return out.view(*shape)
+
+
+@dataclass
+class PrefillInputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    causal: bool
+    scale: float
+    dtype: str
+
+
+def prefill_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype: str,
+                   causal: bool = True, scale: Optional[float] = None) -> PrefillInputs:
+    rng = np.random.default_rng(seed)
+    q = _draw(rng, (B, Hq, N, d), dtype)
+    k = _draw(rng, (B, Hkv, N, d), dtype)
+    v = _draw(rng, (B, Hkv, N, d), dtype)
+    return PrefillInputs(q, k, v, causal, 1.0 / math.sqrt(d) if scale is None else scale, dtype)
+
+
+def worked_example_inputs(d: int = 64) -> PrefillInputs:
+    """The pofe.ai worked example (section "A worked example by hand": scores
+    (2, 1, 4, 3), scalar values (1, 0, 2, -1)) embedded in a 4-token causal
+    prefill: q_i = e0, k_j = s_j e0, v_j = value_j e0, scale 1, float32.
+    Row 3 of the causal output is the page's example; rows 0..2 are its prefixes."""
+    s = [2.0, 1.0, 4.0, 3.0]
+    vals = [1.0, 0.0, 2.0, -1.0]
+    q = torch.zeros(1, 1, 4, d, dtype=torch.float32)
+    k = torch.zeros(1, 1, 4, d, dtype=torch.float32)
+    v = torch.zeros(1, 1, 4, d, dtype=torch.float32)
+    q[0, 0, :, 0] = 1.0
+    k[0, 0, :, 0] = torch.tensor(s)
+    v[0, 0, :, 0] = torch.tensor(vals)
+    return PrefillInputs(q, k, v, True, 1.0, F32)
+
+
+@dataclass
+class DecodeInputs:
+    q: torch.Tensor            # [B, Hq, d]
+    k_cache: torch.Tensor      # [B, S, Hkv, d] or [num_pages, P, Hkv, d]
+    v_cache: torch.Tensor
+    block_table: Optional[torch.Tensor]  # int32 [B, max_blocks] or None (contiguous)
+    seq_lens: torch.Tensor     # int32 [B]
+    page_size: int
+    max_blocks: int
+    scale: float
+    dtype: str
+
+
+def decode_contiguous_inputs(seed: int, B: int, Hq: int, Hkv: int, S: int, d: int,
+                             dtype: str = BF16, page_size: int = 16,
+                             seq_lens: Optional[list] = None) -> DecodeInputs:
+    """One query token per sequence over a contiguous [B, S, Hkv, d] cache."""
+    assert S % page_size == 0
+    rng = np.random.default_rng(seed)
+    q = _draw(rng, (B, Hq, d), dtype)
+    k = _draw(rng, (B, S, Hkv, d), dtype)
+    v = _draw(rng, (B, S, Hkv, d), dtype)
+    sl = torch.tensor(seq_lens if seq_lens is not None else [S] * B, dtype=torch.int32)
+    return DecodeInputs(q, k, v, None, sl, page_size, S // page_size, 1.0 / math.sqrt(d), dtype)
+
+
+def decode_paged_inputs(seed: int, B: int, Hq: int, Hkv: int, d: int, page_size: int,
+                        len_min: int, len_max: int, dtype: str = BF16,
+                        lengths: Optional[list] = None) -> DecodeInputs:
+    """Paged cache: sequence b has L_b ~ U{len_min..len_max} tokens (or `lengths`),
+    stored in ceil(L_b / page_size) pages of a shared pool; a seeded random
+    permutation of the pool assigns logical page p of sequence b to physical
+    page perm[off_b + p].  Unused block-table slots hold -1 (never read)."""
+    rng = np.random.default_rng(seed)
+    q = _draw(rng, (B, Hq, d), dtype)
+    if lengths is None:
+        lens = rng.integers(len_min, len_max + 1, size=B).astype(np.int64)
+    else:
+        lens = np.asarray(lengths, dtype=np.int64)
+    pages = (lens + page_size - 1) // page_size
+    pool = int(pages.sum())
+    perm = rng.permutation(pool) if pool > 0 else np.zeros(0, dtype=np.int64)
+    max_blocks = max(1, -(-len_max // page_size))
+    bt = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += int(pages[b])
+    kc = _draw(rng, (max(pool, 1), page_size, Hkv, d), dtype)
+    vc = _draw(rng, (max(pool, 1), page_size, Hkv, d), dtype)
+    return DecodeInputs(q, kc, vc, torch.from_numpy(bt), torch.from_numpy(lens.astype(np.int32)),
+                        page_size, max_blocks, 1.0 / math.sqrt(d), dtype)
+
+
+# --------------------------------------------------------------------------
+# Named workloads: the pages' shapes (Qwen2.5-7B attention layout for prefill
+# and single-sequence decode, Llama-3-8B layout for batched paged decode).
+# --------------------------------------------------------------------------
+PREFILL_SMALL_F32 = dict(name="prefill-causal-f32-b1-h1-n256-d64", seed=0, B=1, Hq=1, Hkv=1,
+                         N=256, d=64, dtype=F32)
+PREFILL_2K = dict(name="prefill-causal-bf16-b1-h28x4-n2048-d128", seed=2, B=1, Hq=28, Hkv=4,
+                  N=2048, d=128, dtype=BF16)
+
+
+def prefill_long(N: int) -> dict:
+    assert N in (8192, 16384, 30720)
+    return dict(name="prefill-causal-bf16-b1-h28x4-n%d-d128" % N, seed=3, B=1, Hq=28, Hkv=4,
+                N=N, d=128, dtype=BF16)
+
+
+DECODE_32K = dict(name="decode-splitkv-bf16-b1-h28x4-s32768-d128-chunk512", seed=4, B=1, Hq=28,
+                  Hkv=4, S=32768, d=128, chunk=512)
+DECODE_PAGED = dict(name="decode-paged-bf16-b32-h32x8-len1024to32768-d128-page16", seed=5, B=32,
+                    Hq=32, Hkv=8, d=128, page_size=16, len_min=1024, len_max=32768, chunk=0)
+
+
+def make_prefill(cfg: dict) -> PrefillInputs:
+    return prefill_inputs(cfg["seed"], cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["N"], cfg["d"],
+                          cfg["dtype"])
+
+
+def make_decode_32k(cfg: dict = DECODE_32K) -> DecodeInputs:
+    return decode_contiguous_inputs(cfg["seed"], cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["S"], cfg["d"])
+
+
+def make_decode_paged(cfg: dict = DECODE_PAGED) -> DecodeInputs:
+    return decode_paged_inputs(cfg["seed"], cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"],
+                               cfg["page_size"], cfg["len_min"], cfg["len_max"])

@@ -1,0 +1,197 @@
+"""Exact-attention oracle (fp64, CPU) -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check in ``__graft_entry__`` and the CPU-baseline
+leg of ``bench.py`` may import this package.  The GPU library and its Python
+binding never import, load or call it, and it shares no code with them.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision), which follows
+the pofe.ai page "FlashAttention for inference: tiled prefill and split-KV
+decoding": the plain definition of attention (section "The bottleneck it
+attacks"), the online-softmax update and the combine rule (section "The online
+softmax, with every symbol defined"), the tiled prefill loop (section "Prefill:
+tiles, loop order and the tensor cores") and split-KV decoding over a paged cache
+(section "Decode: a different bottleneck").  This module only builds the C file,
+converts arrays to contiguous float64 and calls it.
+
+Parity status: every function here is pinned by CPU tests against values the
+page prints (its worked example), closed forms, a library routine (PyTorch's
+float64 ``scaled_dot_product_attention`` and ``logsumexp``) and invariances; see
+``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        dbl = ctypes.c_double
+        lib.oracle_prefill.argtypes = [P, P, P, P, P, i, i, i, i, i, i, dbl, i]
+        lib.oracle_prefill_tiled.argtypes = [P, P, P, P, P, i, i, i, i, i, i, dbl, i, i]
+        lib.oracle_decode.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i, dbl]
+        lib.oracle_split_decode.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i, dbl, i, i, P, P]
+        lib.oracle_lse_combine.argtypes = [P, P, P, i, i, i, P, P]
+        lib.oracle_online_trace.argtypes = [P, P, i, i, P, P, P, P, P, P]
+        lib.oracle_num_threads.argtypes = []
+        for f in (lib.oracle_prefill, lib.oracle_prefill_tiled, lib.oracle_decode,
+                  lib.oracle_split_decode, lib.oracle_lse_combine, lib.oracle_online_trace,
+                  lib.oracle_num_threads):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    """Contiguous float64 copy/view of an array-like (torch tensors included)."""
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i32(a) -> np.ndarray:
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def prefill(q, k, v, causal: bool, scale: float, row_step: int = 1):
+    """Plain-definition prefill.  q: [B,Hq,N,d]; k, v: [B,Hkv,N,d].
+
+    Returns (o [B,Hq,N,d], lse [B,Hq,N]) in float64.  With row_step > 1 only rows
+    i with i % row_step == 0 are computed; the rest are NaN.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, d) and v.shape == k.shape
+    o = np.full_like(q, np.nan)
+    lse = np.full((B, Hq, N), np.nan)
+    rc = _load().oracle_prefill(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, N, d,
+                                int(bool(causal)), float(scale), int(row_step))
+    if rc != 0:
+        raise ValueError("oracle_prefill rejected its arguments")
+    return o, lse
+
+
+def prefill_tiled(q, k, v, causal: bool, scale: float, br: int, bc: int):
+    """The pages' tiled online-softmax prefill with Br x Bc tiles (same layouts)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    o = np.full_like(q, np.nan)
+    lse = np.full((B, Hq, N), np.nan)
+    rc = _load().oracle_prefill_tiled(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, N, d,
+                                      int(bool(causal)), float(scale), int(br), int(bc))
+    if rc != 0:
+        raise ValueError("oracle_prefill_tiled rejected its arguments")
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, page_size: int,
+           max_blocks: int):
+    """Plain-definition decode.  q: [B,Hq,d].  Cache [nblk,P,Hkv,d] with a block table
+    [B,max_blocks], or contiguous [B,S,Hkv,d] when block_table is None (S = max_blocks*P).
+    Returns (o [B,Hq,d], lse [B,Hq]) in float64."""
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, Hq, d = q.shape
+    Hkv = kc.shape[-2]
+    bt = None if block_table is None else _i32(block_table)
+    sl = _i32(seq_lens)
+    o = np.full_like(q, np.nan)
+    lse = np.full((B, Hq), np.nan)
+    rc = _load().oracle_decode(_p(q), _p(kc), _p(vc), _p(bt), _p(sl), _p(o), _p(lse), B, Hq,
+                               Hkv, d, int(page_size), int(max_blocks), float(scale))
+    if rc != 0:
+        raise ValueError("oracle_decode rejected its arguments")
+    return o, lse
+
+
+def split_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, page_size: int,
+                 max_blocks: int, chunk: int, block: int = 64, return_parts: bool = False):
+    """The pages' split-KV decode: per-chunk online softmax, then the combine rule."""
+    q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, Hq, d = q.shape
+    Hkv = kc.shape[-2]
+    bt = None if block_table is None else _i32(block_table)
+    sl = _i32(seq_lens)
+    o = np.full_like(q, np.nan)
+    lse = np.full((B, Hq), np.nan)
+    max_chunks = -(-(max_blocks * page_size) // chunk)
+    op = lp = None
+    if return_parts:
+        op = np.full((B * Hq, max_chunks, d), np.nan)
+        lp = np.full((B * Hq, max_chunks), np.nan)
+    rc = _load().oracle_split_decode(_p(q), _p(kc), _p(vc), _p(bt), _p(sl), _p(o), _p(lse),
+                                     B, Hq, Hkv, d, int(page_size), int(max_blocks),
+                                     float(scale), int(chunk), int(block), _p(op), _p(lp))
+    if rc != 0:
+        raise ValueError("oracle_split_decode rejected its arguments")
+    if return_parts:
+        return o, lse, op, lp
+    return o, lse
+
+
+def lse_combine(o_parts, lse_parts, n_splits=None):
+    """Combine rule.  o_parts [rows, S, d], lse_parts [rows, S] -> (o [rows,d], lse [rows])."""
+    op, lp = _f64(o_parts), _f64(lse_parts)
+    rows, S, d = op.shape
+    ns = None if n_splits is None else _i32(n_splits)
+    o = np.full((rows, d), np.nan)
+    lse = np.full((rows,), np.nan)
+    rc = _load().oracle_lse_combine(_p(op), _p(lp), _p(ns), rows, S, d, _p(o), _p(lse))
+    if rc != 0:
+        raise ValueError("oracle_lse_combine rejected its arguments")
+    return o, lse
+
+
+def online_trace(scores, values, block: int):
+    """Online update on one row with given scores and scalar values.
+
+    Returns dict with per-block m, l, o_tilde, c and the final o, lse."""
+    s, v = _f64(scores), _f64(values)
+    n = s.shape[0]
+    nb = max(1, -(-n // block))
+    m, l, ot, c = (np.zeros(nb) for _ in range(4))
+    o = np.zeros(1)
+    lse = np.zeros(1)
+    cnt = _load().oracle_online_trace(_p(s), _p(v), n, int(block), _p(m), _p(l), _p(ot), _p(c),
+                                      _p(o), _p(lse))
+    if cnt < 0:
+        raise ValueError("oracle_online_trace rejected its arguments")
+    return {"m": m[:cnt], "l": l[:cnt], "o_tilde": ot[:cnt], "c": c[:cnt],
+            "o": float(o[0]), "lse": float(lse[0])}

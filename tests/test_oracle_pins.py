@@ -1,0 +1,430 @@
+"""Pins for the fp64 oracle, against things other than itself.
+
+* values the pofe.ai page prints for its worked example (tests/golden/worked_example.json);
+* closed forms of that example (each causal row is a small softmax written out by hand);
+* a library routine: PyTorch's float64 scaled_dot_product_attention and logsumexp on CPU;
+* a second, hand-written numpy softmax;
+* invariances the method guarantees in exact arithmetic: tile size, split count,
+  page placement, GQA = MHA on expanded K/V, score shifts, and special cases.
+
+Each test is chosen so that a plausible slip in the oracle (dropped term, wrong sign
+or index, transposed operand, wrong head group, wrong log base, off-by-one causal
+limit, wrong page index) fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
+E = math.e
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- worked example
+def test_worked_example_trace_matches_page(golden):
+    tr = oracle.online_trace(golden["scores"], golden["values"], golden["block"])
+    tol = 0.5 * 10 ** (-golden["printed_decimals"]) + 1e-12
+    b1, b2 = golden["block1"], golden["block2"]
+    assert len(tr["m"]) == 2
+    assert tr["m"][0] == b1["m"] and tr["m"][1] == b2["m"]
+    assert abs(tr["l"][0] - b1["l"]) <= tol
+    assert abs(tr["o_tilde"][0] - b1["o_tilde"]) <= tol
+    assert abs(tr["o_tilde"][0] / tr["l"][0] - b1["interim_output"]) <= tol
+    assert abs(tr["c"][1] - b2["c"]) <= tol
+    assert abs(tr["l"][1] - b2["l"]) <= tol
+    assert abs(tr["o_tilde"][1] - b2["o_tilde"]) <= tol
+    assert abs(tr["o"] - golden["result"]) <= tol
+    # the page's direct computation: e^s and their sum
+    es = np.exp(np.asarray(golden["scores"], dtype=np.float64))
+    assert np.allclose(es, golden["direct_exp_scores"], atol=5e-4)
+    assert abs(math.exp(tr["lse"]) - golden["direct_exp_sum"]) <= 5e-4
+
+
+def test_worked_example_closed_form():
+    tr = oracle.online_trace([2, 1, 4, 3], [1, 0, 2, -1], 2)
+    num = E**2 * 1 + E**1 * 0 + E**4 * 2 + E**3 * (-1)
+    den = E**2 + E**1 + E**4 + E**3
+    assert abs(tr["o"] - num / den) < 1e-14
+    assert abs(tr["o"] - 1.1380900204) < 1e-10
+    assert abs(tr["lse"] - math.log(den)) < 1e-14
+    assert abs(tr["lse"] - 4.4401896986) < 1e-10
+    # first block correction is exp(-inf) = 0, second is e^(2-4)
+    assert tr["c"][0] == 0.0
+    assert abs(tr["c"][1] - math.exp(-2.0)) < 1e-16
+
+
+@pytest.mark.parametrize("block", [1, 2, 3, 4, 7])
+def test_worked_example_block_size_invariant(block):
+    tr = oracle.online_trace([2, 1, 4, 3], [1, 0, 2, -1], block)
+    assert abs(tr["o"] - 1.1380900204) < 1e-10
+    assert abs(tr["lse"] - 4.4401896986) < 1e-10
+
+
+def _embedded_example(d=8):
+    s = [2.0, 1.0, 4.0, 3.0]
+    vals = [1.0, 0.0, 2.0, -1.0]
+    q = np.zeros((1, 1, 4, d)); k = np.zeros((1, 1, 4, d)); v = np.zeros((1, 1, 4, d))
+    q[0, 0, :, 0] = 1.0
+    k[0, 0, :, 0] = s
+    v[0, 0, :, 0] = vals
+    return q, k, v
+
+
+# closed forms of the causal prefixes of the example: row i sees keys 0..i
+ROWS_O = [1.0,
+          E**2 / (E**2 + E),
+          (E**2 + 2 * E**4) / (E**2 + E + E**4),
+          (E**2 + 2 * E**4 - E**3) / (E**2 + E + E**4 + E**3)]
+ROWS_LSE = [2.0, math.log(E**2 + E), math.log(E**2 + E + E**4), math.log(E**2 + E + E**4 + E**3)]
+
+
+@pytest.mark.parametrize("tiles", [None, (4, 2), (2, 2), (1, 2), (4, 1), (3, 3), (2, 4)])
+def test_worked_example_as_causal_prefill(golden, tiles):
+    q, k, v = _embedded_example()
+    if tiles is None:
+        o, lse = oracle.prefill(q, k, v, causal=True, scale=1.0)
+    else:
+        o, lse = oracle.prefill_tiled(q, k, v, True, 1.0, *tiles)
+    assert np.allclose(o[0, 0, :, 0], ROWS_O, atol=1e-14, rtol=0)
+    assert np.allclose(lse[0, 0], ROWS_LSE, atol=1e-14, rtol=0)
+    assert np.all(o[0, 0, :, 1:] == 0.0)
+    # row 1 is the page's interim output after block 1; row 3 is its result
+    assert abs(o[0, 0, 1, 0] - golden["block1"]["interim_output"]) < 5e-5
+    assert abs(o[0, 0, 3, 0] - golden["result"]) < 5e-5
+    assert abs(ROWS_O[3] - 1.1380900204) < 1e-10
+    assert abs(ROWS_LSE[1] - 2.3132616875) < 1e-10
+    assert abs(ROWS_O[2] - 1.8017846683) < 1e-10
+
+
+def test_combine_of_the_two_example_blocks(golden):
+    o1, l1 = E**2 / (E**2 + E), math.log(E**2 + E)          # block (2, 1)
+    o2, l2 = (2 * E**4 - E**3) / (E**4 + E**3), math.log(E**4 + E**3)  # block (4, 3)
+    o, lse = oracle.lse_combine(np.array([[[o1], [o2]]]), np.array([[l1, l2]]))
+    assert abs(o[0, 0] - 1.1380900204) < 1e-10
+    assert abs(o[0, 0] - golden["result"]) < 5e-5
+    assert abs(lse[0] - 4.4401896986) < 1e-10
+    # the merge weights are softmax(lambda): 0.1192..., 0.8807...
+    w1 = 1.0 / (1.0 + math.exp(l2 - l1))
+    assert abs(w1 - 0.1192029220) < 1e-9
+
+
+# --------------------------------------------------- library cross-check (SDPA)
+def _torch_ref(q, k, v, causal, scale):
+    """PyTorch float64 CPU reference; K/V expanded to Hq heads in contiguous groups."""
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    g = qt.shape[1] // kt.shape[1]
+    kt = kt.repeat_interleave(g, dim=1)
+    vt = vt.repeat_interleave(g, dim=1)
+    o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=causal, scale=scale)
+    s = torch.matmul(qt, kt.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        n = s.shape[-1]
+        mask = torch.ones(n, n, dtype=torch.bool).triu(1)
+        s = s.masked_fill(mask, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    return o.numpy(), lse.numpy()
+
+
+CASES = [
+    # B, Hq, Hkv, N, d, causal
+    (1, 1, 1, 1, 4, True),
+    (1, 1, 1, 5, 4, False),
+    (2, 4, 2, 17, 8, True),
+    (1, 6, 3, 33, 16, True),
+    (2, 6, 3, 33, 16, False),
+    (1, 6, 2, 64, 12, True),
+    (1, 3, 1, 9, 24, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_plain_prefill_matches_torch_sdpa(case):
+    B, Hq, Hkv, N, d, causal = case
+    rng = np.random.default_rng(1000 + N + d)
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    scale = 0.3 + rng.random()
+    o, lse = oracle.prefill(q, k, v, causal, scale)
+    ro, rl = _torch_ref(q, k, v, causal, scale)
+    assert np.max(np.abs(o - ro)) < 1e-12
+    assert np.max(np.abs(lse - rl)) < 1e-12
+
+
+def test_plain_prefill_matches_handwritten_numpy_softmax():
+    rng = np.random.default_rng(7)
+    N, d = 23, 5
+    q = rng.standard_normal((1, 1, N, d)); k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    o, lse = oracle.prefill(q, k, v, True, 0.7)
+    for i in range(N):
+        s = 0.7 * (k[0, 0, : i + 1] @ q[0, 0, i])
+        p = np.exp(s - s.max()); p /= p.sum()
+        assert np.max(np.abs(o[0, 0, i] - p @ v[0, 0, : i + 1])) < 1e-13
+        assert abs(lse[0, 0, i] - (s.max() + np.log(np.exp(s - s.max()).sum()))) < 1e-13
+
+
+def test_gqa_equals_mha_on_expanded_kv_bitwise():
+    rng = np.random.default_rng(3)
+    B, Hq, Hkv, N, d = 2, 8, 2, 19, 8
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d)); v = rng.standard_normal((B, Hkv, N, d))
+    o1, l1 = oracle.prefill(q, k, v, True, 0.5)
+    o2, l2 = oracle.prefill(q, np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1),
+                            True, 0.5)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_row_sampling_computes_only_sampled_rows():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 2, 40, 8)); k = rng.standard_normal((1, 1, 40, 8))
+    v = rng.standard_normal((1, 1, 40, 8))
+    o_all, l_all = oracle.prefill(q, k, v, True, 0.35)
+    o_s, l_s = oracle.prefill(q, k, v, True, 0.35, row_step=7)
+    rows = np.arange(40) % 7 == 0
+    assert np.array_equal(o_s[:, :, rows], o_all[:, :, rows])
+    assert np.array_equal(l_s[:, :, rows], l_all[:, :, rows])
+    assert np.all(np.isnan(l_s[:, :, ~rows]))
+
+
+# ----------------------------------------------------- the pages' tiled algorithm
+@pytest.mark.parametrize("causal", [True, False])
+def test_tiled_prefill_is_independent_of_tile_size(causal):
+    rng = np.random.default_rng(11)
+    B, Hq, Hkv, N, d = 1, 4, 2, 300, 16
+    q = rng.standard_normal((B, Hq, N, d)); k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    o0, l0 = oracle.prefill(q, k, v, causal, 0.25)
+    for br, bc in [(1, 1), (2, 2), (3, 7), (7, 3), (64, 64), (64, 16), (16, 64), (N, N), (300, 1)]:
+        o, l = oracle.prefill_tiled(q, k, v, causal, 0.25, br, bc)
+        assert np.max(np.abs(o - o0)) < 1e-12, (br, bc)
+        assert np.max(np.abs(l - l0)) < 1e-12, (br, bc)
+
+
+def test_tiled_prefill_toy_run_magnitude():
+    """The page's toy run: 2,048-token causal prefill, d=128, 64x64 tiles, fp64:
+    tiled and standard differ only by rounding (it reports 1.1e-15)."""
+    rng = np.random.default_rng(0)
+    N, d = 2048, 128
+    q = rng.standard_normal((1, 1, N, d)); k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    s = 1.0 / math.sqrt(d)
+    o0, l0 = oracle.prefill(q, k, v, True, s)
+    o1, l1 = oracle.prefill_tiled(q, k, v, True, s, 64, 64)
+    assert np.max(np.abs(o1 - o0)) < 1e-13
+    assert np.max(np.abs(l1 - l0)) < 1e-13
+
+
+# --------------------------------------------------------------------- decode
+def _to_cache(k):
+    """[B, Hkv, S, d] -> contiguous decode cache [B, S, Hkv, d]."""
+    return np.ascontiguousarray(np.transpose(k, (0, 2, 1, 3)))
+
+
+def _page(kc, lens, P, rng):
+    """Scatter a contiguous [B, S, Hkv, d] cache into a randomly permuted page pool.
+    Built directly here (not through the oracle) so the oracle's page gather is checked."""
+    B, S, Hkv, d = kc.shape
+    pages = [-(-int(L) // P) for L in lens]
+    pool = sum(pages)
+    perm = rng.permutation(pool)
+    maxb = -(-S // P)
+    bt = np.full((B, maxb), -1, dtype=np.int32)
+    kp = np.zeros((pool, P, Hkv, d))
+    off = 0
+    for b in range(B):
+        for p in range(pages[b]):
+            phys = perm[off + p]
+            bt[b, p] = phys
+            n = min(P, int(lens[b]) - p * P)
+            kp[phys, :n] = kc[b, p * P: p * P + n]
+        off += pages[b]
+    return kp, bt
+
+
+def test_decode_matches_torch_sdpa():
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, S, d, P = 3, 6, 2, 96, 16, 16
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, S, d)); v = rng.standard_normal((B, Hkv, S, d))
+    lens = np.array([96, 1, 37], dtype=np.int32)
+    o, lse = oracle.decode(q, _to_cache(k), _to_cache(v), None, lens, 0.4, P, S // P)
+    for b in range(B):
+        L = int(lens[b])
+        ro, rl = _torch_ref(q[b][None, :, None, :], k[b][None, :, :L], v[b][None, :, :L], False, 0.4)
+        assert np.max(np.abs(o[b] - ro[0, :, 0])) < 1e-12
+        assert np.max(np.abs(lse[b] - rl[0, :, 0])) < 1e-12
+
+
+def test_decode_paging_invariance_bitwise():
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, S, d, P = 4, 8, 4, 160, 8, 16
+    q = rng.standard_normal((B, Hq, d))
+    kc = rng.standard_normal((B, S, Hkv, d)); vc = rng.standard_normal((B, S, Hkv, d))
+    lens = np.array([160, 17, 1, 100], dtype=np.int32)
+    o0, l0 = oracle.decode(q, kc, vc, None, lens, 0.3, P, S // P)
+    kp, bt = _page(kc, lens, P, np.random.default_rng(5))
+    vp, bt2 = _page(vc, lens, P, np.random.default_rng(5))
+    assert np.array_equal(bt, bt2)
+    o1, l1 = oracle.decode(q, kp, vp, bt, lens, 0.3, P, S // P)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 16, 512, 1024])
+def test_split_decode_is_independent_of_chunk(chunk):
+    rng = np.random.default_rng(23)
+    B, Hq, Hkv, S, d, P = 2, 4, 2, 1024, 16, 16
+    q = rng.standard_normal((B, Hq, d))
+    kc = rng.standard_normal((B, S, Hkv, d)); vc = rng.standard_normal((B, S, Hkv, d))
+    lens = np.array([1024, 333], dtype=np.int32)
+    o0, l0 = oracle.decode(q, kc, vc, None, lens, 0.25, P, S // P)
+    for block in (1, 7, 64):
+        o, l = oracle.split_decode(q, kc, vc, None, lens, 0.25, P, S // P, chunk, block)
+        assert np.max(np.abs(o - o0)) < 1e-12
+        assert np.max(np.abs(l - l0)) < 1e-12
+
+
+def test_split_decode_toy_run_magnitude():
+    """The page's toy run: four query heads against a 32,768-token cache with
+    1,024-token chunks; split and standard differ only by rounding (it reports 3.0e-16)."""
+    rng = np.random.default_rng(0)
+    S, d, P = 32768, 128, 16
+    q = rng.standard_normal((1, 4, d))
+    kc = rng.standard_normal((1, S, 4, d)); vc = rng.standard_normal((1, S, 4, d))
+    lens = np.array([S], dtype=np.int32)
+    s = 1.0 / math.sqrt(d)
+    o0, l0 = oracle.decode(q, kc, vc, None, lens, s, P, S // P)
+    o1, l1 = oracle.split_decode(q, kc, vc, None, lens, s, P, S // P, 1024, 1024)
+    assert np.max(np.abs(o1 - o0)) < 1e-14
+    assert np.max(np.abs(l1 - l0)) < 1e-13
+
+
+def test_split_parts_recombine():
+    rng = np.random.default_rng(24)
+    q = rng.standard_normal((1, 2, 8))
+    kc = rng.standard_normal((1, 64, 1, 8)); vc = rng.standard_normal((1, 64, 1, 8))
+    lens = np.array([50], dtype=np.int32)
+    o, l, op, lp = oracle.split_decode(q, kc, vc, None, lens, 0.5, 16, 4, 16, 4, return_parts=True)
+    assert lp.shape == (2, 4) and np.isfinite(lp[:, :4]).all()
+    o2, l2 = oracle.lse_combine(op, lp)
+    assert np.array_equal(o2, o.reshape(2, 8)) and np.array_equal(l2, l.reshape(2))
+    # each partial is the plain softmax over its own chunk
+    for c in range(4):
+        t1 = min(50, 16 * c + 16)
+        ro, rl = oracle.decode(q, kc[:, 16 * c:16 * c + 16], vc[:, 16 * c:16 * c + 16], None,
+                               np.array([t1 - 16 * c], dtype=np.int32), 0.5, 16, 1)
+        assert np.max(np.abs(op[:, c] - ro[0])) < 1e-13
+        assert np.max(np.abs(lp[:, c] - rl[0])) < 1e-13
+
+
+def test_prefill_row_equals_decode_of_that_row_bitwise():
+    rng = np.random.default_rng(25)
+    B, Hq, Hkv, N, d = 1, 4, 2, 48, 8
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d)); v = rng.standard_normal((B, Hkv, N, d))
+    o, lse = oracle.prefill(q, k, v, True, 0.3)
+    for i in (0, 1, 15, 16, 47):
+        od, ld = oracle.decode(q[:, :, i], _to_cache(k), _to_cache(v), None,
+                               np.array([i + 1], dtype=np.int32), 0.3, 16, N // 16)
+        assert np.array_equal(od, o[:, :, i]) and np.array_equal(ld, lse[:, :, i])
+
+
+# -------------------------------------------------------------- special cases
+def test_single_key_gives_its_value():
+    rng = np.random.default_rng(26)
+    q = rng.standard_normal((1, 1, 1, 8)); k = rng.standard_normal((1, 1, 1, 8))
+    v = rng.standard_normal((1, 1, 1, 8))
+    o, lse = oracle.prefill(q, k, v, True, 0.6)
+    assert np.array_equal(o[0, 0, 0], v[0, 0, 0])
+    assert abs(lse[0, 0, 0] - 0.6 * float(q[0, 0, 0] @ k[0, 0, 0])) < 1e-15
+
+
+def test_equal_scores_give_prefix_means():
+    rng = np.random.default_rng(27)
+    N, d = 30, 6
+    q = np.zeros((1, 1, N, d)); k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    o, lse = oracle.prefill(q, k, v, True, 1.0)
+    means = np.cumsum(v[0, 0], axis=0) / np.arange(1, N + 1)[:, None]
+    assert np.max(np.abs(o[0, 0] - means)) < 1e-14
+    assert np.max(np.abs(lse[0, 0] - np.log(np.arange(1, N + 1)))) < 1e-14
+    o, lse = oracle.prefill(q, k, v, False, 1.0)
+    assert np.max(np.abs(o[0, 0] - v[0, 0].mean(axis=0))) < 1e-14
+    assert np.max(np.abs(lse[0, 0] - math.log(N))) < 1e-14
+
+
+def test_shifting_a_rows_scores_shifts_only_its_lse():
+    rng = np.random.default_rng(28)
+    N, d = 20, 6
+    q = rng.standard_normal((1, 1, N, d)); k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    shift = rng.standard_normal(N) * 5.0
+    # extra coordinate: q'_i = [q_i, shift_i], k'_j = [k_j, 1]  ->  s'_ij = s_ij + shift_i
+    q2 = np.concatenate([q, shift[None, None, :, None]], axis=-1)
+    k2 = np.concatenate([k, np.ones((1, 1, N, 1))], axis=-1)
+    v2 = np.concatenate([v, np.zeros((1, 1, N, 1))], axis=-1)
+    o1, l1 = oracle.prefill(q, k, v, True, 1.0)
+    o2, l2 = oracle.prefill(q2, k2, v2, True, 1.0)
+    assert np.max(np.abs(o2[..., :d] - o1)) < 1e-12
+    assert np.max(np.abs(l2 - (l1 + shift))) < 1e-12
+
+
+def test_dominant_key_selects_its_value():
+    rng = np.random.default_rng(29)
+    N, d = 16, 4
+    q = np.zeros((1, 1, N, d)); q[..., 0] = 1.0
+    k = np.zeros((1, 1, N, d)); k[0, 0, 5, 0] = 80.0
+    v = rng.standard_normal((1, 1, N, d))
+    o, lse = oracle.prefill(q, k, v, False, 1.0)
+    assert np.max(np.abs(o[0, 0] - v[0, 0, 5])) < 1e-30 + 1e-12
+    assert np.max(np.abs(lse[0, 0] - (80.0 + math.log1p((N - 1) * math.exp(-80.0))))) < 1e-12
+
+
+def test_empty_sequence_and_empty_combine():
+    q = np.ones((2, 2, 4))
+    kc = np.ones((2, 16, 1, 4)); vc = np.ones((2, 16, 1, 4))
+    o, lse = oracle.decode(q, kc, vc, None, np.array([0, 3], dtype=np.int32), 1.0, 16, 1)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    assert np.allclose(o[1], 1.0) and np.allclose(lse[1], 4.0 + math.log(3.0))
+    o, lse = oracle.split_decode(q, kc, vc, None, np.array([0, 3], dtype=np.int32), 1.0, 16, 1, 2, 1)
+    assert np.all(o[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    oc, lc = oracle.lse_combine(np.ones((1, 3, 4)), np.zeros((1, 3)), np.array([0], dtype=np.int32))
+    assert np.all(oc == 0.0) and np.isneginf(lc[0])
+
+
+def test_one_split_combine_is_identity():
+    rng = np.random.default_rng(30)
+    op = rng.standard_normal((5, 1, 7)); lp = rng.standard_normal((5, 1)) * 10
+    o, l = oracle.lse_combine(op, lp)
+    assert np.array_equal(o, op[:, 0]) and np.array_equal(l, lp[:, 0])
+
+
+def test_combine_ignores_splits_past_n_splits():
+    rng = np.random.default_rng(31)
+    op = rng.standard_normal((3, 4, 5)); lp = rng.standard_normal((3, 4))
+    ns = np.array([4, 2, 1], dtype=np.int32)
+    o, l = oracle.lse_combine(op, lp, ns)
+    for r in range(3):
+        o2, l2 = oracle.lse_combine(op[r:r + 1, :ns[r]], lp[r:r + 1, :ns[r]])
+        assert np.array_equal(o[r], o2[0]) and l[r] == l2[0]
+
+
+def test_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.prefill(np.zeros((1, 3, 4, 8)), np.zeros((1, 2, 4, 8)), np.zeros((1, 2, 4, 8)),
+                       True, 1.0)
+    with pytest.raises(ValueError):
+        oracle.decode(np.zeros((1, 2, 4)), np.zeros((1, 16, 1, 4)), np.zeros((1, 16, 1, 4)), None,
+                      np.array([17], dtype=np.int32), 1.0, 16, 1)
