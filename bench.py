@@ -1,0 +1,210 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+One step = one causal prefill of 28 query heads / 4 KV heads, N = 16,384, d = 128
+(bf16 in, fp32 accumulation, O bf16 + LSE fp32) followed by one split-KV decode of a
+single query token against a contiguous 32,768-token bf16 cache (28/4 heads, 64
+chunks of 512 tokens, then the LSE combine).  Inputs are seeded synthetic N(0,1)
+values already resident in HBM.  The decode reads one of 8 distinct cache copies
+per step (512 MiB in total, twice the Infinity Cache) so its bytes come from HBM.
+
+Prints one JSON line.  `value` is the prefill throughput in TFLOP/s (algorithmic
+FLOPs 2*B*Hq*d*N^2 per launch, i.e. the causal half of the dense 4*B*Hq*d*N^2);
+the decode figure (HBM GB/s over K+V read once plus q and o) is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak (published)
+METRIC = "causal prefill TFLOP/s (N=16k, d=128) + split-KV decode HBM GB/s at 32k"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_n16384_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_prefill_amd", "csrc", "prefill_bf16.hip")
+N_KV_COPIES = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle leg")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one half of the step (profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference dispatch for HBM counters)")
+    return ap.parse_args()
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(per_launch_units: float):
+    """HBM bytes per prefill launch from committed counter runs, if they still describe
+    the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, target_s: float):
+    """The fp64 oracle, as it stands, on a bounded row sample of the prefill workload."""
+    import numpy as np
+    import oracle
+    q = oracle._f64(x.q)
+    k = oracle._f64(x.k)
+    v = oracle._f64(x.v)
+    B, Hq, N, d = q.shape
+
+    def sample_flop(step):
+        rows = np.arange(0, N, step, dtype=np.float64)
+        return 4.0 * d * float((rows + 1).sum()) * B * Hq
+
+    # short calibration run, then one run sized to about target_s
+    step = 256
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, True, x.scale, row_step=step)
+    rate = sample_flop(step) / max(time.perf_counter() - t0, 1e-6)
+    step = int(min(256, max(2, round(sample_flop(1) / (rate * target_s)))))
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, True, x.scale, row_step=step)
+    dt = time.perf_counter() - t0
+    return {"value": sample_flop(step) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "fp64 plain-definition oracle on every %d-th query row of all 28 heads of the "
+                      "N=16384 causal prefill (%.1f GFLOP, %.1f s wall)" % (step, sample_flop(step) / 1e9, dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention path here runs on a single MI355X "
+              "and has no multi-GPU mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_io_aware_prefill_amd import attn
+    from exact_io_aware_prefill_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    pcfg = W.prefill_long(16384)
+    px = W.make_prefill(pcfg)
+    q, k, v = (t.to(dev) for t in (px.q, px.k, px.v))
+    B, Hq, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    prefill_flop = 2.0 * B * Hq * d * N * N
+
+    dcfg = W.DECODE_32K
+    dx = W.make_decode_32k(dcfg)
+    dq = dx.q.to(dev)
+    kc0, vc0 = dx.k_cache.to(dev), dx.v_cache.to(dev)
+    kcs = [kc0] + [kc0.clone() for _ in range(N_KV_COPIES - 1)]  # distinct allocations
+    vcs = [vc0] + [vc0.clone() for _ in range(N_KV_COPIES - 1)]
+    sl = dx.seq_lens.to(dev)
+    do = torch.empty_like(dq)
+    dl = torch.empty((dq.shape[0], dq.shape[1]), dtype=torch.float32, device=dev)
+    chunk = dcfg["chunk"]
+    wsb = attn.attn_decode_workspace_bytes(dq.shape[0], dq.shape[1], kcs[0].shape[2], d, dx.page_size,
+                                           dx.max_blocks, chunk)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    decode_bytes = (kcs[0].numel() + vcs[0].numel()) * 2 + dq.numel() * 2 + do.numel() * 2 + dl.numel() * 4
+
+    def run_prefill():
+        attn.attn_prefill(q, k, v, o, lse, True, px.scale)
+
+    def run_decode(i):
+        attn.attn_decode(dq, kcs[i % N_KV_COPIES], vcs[i % N_KV_COPIES], None, sl, do, dl, dx.page_size,
+                         dx.max_blocks, dx.scale, chunk, ws)
+
+    do_p = args.only in (None, "prefill")
+    do_d = args.only in (None, "decode")
+    for i in range(args.warmup):
+        if do_p:
+            run_prefill()
+        if do_d:
+            run_decode(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record()
+        if do_p:
+            run_prefill()
+        evs[i][1].record()
+        if do_d:
+            run_decode(i)
+        evs[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+
+    if args.copy_calibration:  # reference dispatch for the HBM byte counters: copy 1 GiB
+        src = torch.empty(1 << 29, dtype=torch.float16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": METRIC,
+        "value": (prefill_flop / (pre_ms * 1e-3) / 1e12) if do_p else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": pcfg["name"] + " + " + dcfg["name"],
+                   "prefill": {"batch": B, "q_heads": Hq, "kv_heads": k.shape[1], "seq_len": N,
+                               "head_dim": d, "causal": True},
+                   "decode": {"batch": 1, "q_heads": dq.shape[1], "kv_heads": kcs[0].shape[2],
+                              "cache_tokens": kcs[0].shape[1], "head_dim": d, "chunk_tokens": chunk,
+                              "splits": -(-kcs[0].shape[1] // chunk), "kv_copies_rotated": N_KV_COPIES}},
+    }
+    if do_p:
+        achieved = prefill_flop / (pre_ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                           "traffic": measured_traffic(1.0),
+                           "kernel": "prefill_bf16_kernel<128>", "avg_launch_ms": pre_ms,
+                           "algorithmic_flop_per_launch": prefill_flop}
+    if do_d:
+        gbs = decode_bytes / (dec_ms * 1e-3) / 1e9
+        out["decode"] = {"value": gbs, "unit": "GB/s", "avg_ms": dec_ms,
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                                      "kernels": "decode_split_kernel<128> + lse_combine_kernel<128>",
+                                      "algorithmic_bytes_per_launch": decode_bytes}}
+    if do_p and not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(px, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+"""ctypes binding to libattn.so (declared in include/attn.h), same entry-point names.
+
+Argument marshalling only: tensors are passed as device pointers with their sizes
+read from the tensor shapes, and the current PyTorch HIP stream is passed as the
+stream.  Every step of the computation runs in the library's HIP kernels; there is
+no other implementation behind these functions.  Importing this module raises if
+the library has not been built (python -m exact_io_aware_prefill_amd.build).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError("libattn.so is not built: run `python -m exact_io_aware_prefill_amd.build` "
+                      "(hipcc for gfx950); there is no fallback implementation")
+lib = ctypes.CDLL(_LIB_PATH)
+
+ATTN_OK = 0
+ATTN_ERR_NULL = -1
+ATTN_ERR_SHAPE = -2
+ATTN_ERR_GQA = -3
+ATTN_ERR_UNSUPPORTED = -4
+ATTN_ERR_WORKSPACE = -5
+ATTN_ERR_ALIGN = -6
+ATTN_ERR_HIP = -7
+ATTN_F32 = 0
+ATTN_BF16 = 1
+
+EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_chunk_tokens", "attn_decode_workspace_bytes",
+           "attn_lse_combine", "attn_status_string")
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+lib.attn_prefill.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+lib.attn_prefill.restype = _I
+lib.attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                            _I, _P, ctypes.c_size_t, _P]
+lib.attn_decode.restype = _I
+lib.attn_decode_chunk_tokens.argtypes = [_I, _I, _I, _I, _I]
+lib.attn_decode_chunk_tokens.restype = _I
+lib.attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I]
+lib.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+lib.attn_lse_combine.argtypes = [_P, _P, _P, _I, _I, _I, _P, _I, _P, _P]
+lib.attn_lse_combine.restype = _I
+lib.attn_status_string.argtypes = [_I]
+lib.attn_status_string.restype = ctypes.c_char_p
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s failed: %s (status %d)" % (where, attn_status_string(status), status))
+        self.status = status
+
+
+def attn_status_string(status: int) -> str:
+    return lib.attn_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    return -1
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(rc: int, where: str):
+    if rc != ATTN_OK:
+        raise AttnError(rc, where)
+
+
+def attn_prefill(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """q, o: [B, Hq, N, d]; k, v: [B, Hkv, N, d] (bf16 or f32, contiguous, on the GPU);
+    lse: [B, Hq, N] float32.  Writes o and lse."""
+    B, Hq, N, d = q.shape
+    rc = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, N, Hq, k.shape[1], d,
+                          _dtype_code(q), int(bool(causal)), float(scale), _stream(stream))
+    _check(rc, "attn_prefill")
+
+
+def attn_decode_chunk_tokens(batch: int, n_kv_heads: int, page_size: int, max_blocks_per_seq: int,
+                             chunk_tokens: int = 0) -> int:
+    r = lib.attn_decode_chunk_tokens(batch, n_kv_heads, page_size, max_blocks_per_seq, chunk_tokens)
+    _check(min(r, 0), "attn_decode_chunk_tokens")
+    return r
+
+
+def attn_decode_workspace_bytes(batch: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                                page_size: int, max_blocks_per_seq: int, chunk_tokens: int = 0) -> int:
+    return int(lib.attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, page_size,
+                                               max_blocks_per_seq, chunk_tokens))
+
+
+def attn_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, page_size: int,
+                max_blocks_per_seq: int, scale: float, chunk_tokens: int, workspace,
+                stream=None) -> None:
+    """q, o: [B, Hq, d]; caches [num_pages, P, Hkv, d] with block_table [B, max_blocks] int32,
+    or [B, S, Hkv, d] with block_table None; seq_lens [B] int32; lse [B, Hq] float32 or None;
+    workspace: a uint8 device tensor of at least attn_decode_workspace_bytes(...) bytes."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[-2]
+    rc = lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                         _ptr(o), _ptr(lse), B, Hq, Hkv, d, int(page_size), int(max_blocks_per_seq),
+                         _dtype_code(q), float(scale), int(chunk_tokens), _ptr(workspace),
+                         0 if workspace is None else workspace.numel() * workspace.element_size(),
+                         _stream(stream))
+    _check(rc, "attn_decode")
+
+
+def attn_lse_combine(o_parts, lse_parts, n_splits, o, lse, stream=None) -> None:
+    """o_parts [rows, S, d] f32; lse_parts [rows, S] f32; n_splits [rows] int32 or None;
+    o [rows, d] (bf16 or f32); lse [rows] f32 or None."""
+    rows, S, d = o_parts.shape
+    rc = lib.attn_lse_combine(_ptr(o_parts), _ptr(lse_parts), _ptr(n_splits), rows, S, d, _ptr(o),
+                              _dtype_code(o), _ptr(lse), _stream(stream))
+    _check(rc, "attn_lse_combine")
+
+
+# ---- conveniences that allocate outputs with PyTorch (allocation only) ----------
+def prefill(q, k, v, causal: bool = True, scale: float | None = None, stream=None):
+    B, Hq, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    attn_prefill(q, k, v, o, lse, causal, d ** -0.5 if scale is None else scale, stream)
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, page_size: int, max_blocks_per_seq: int,
+           scale: float | None = None, chunk_tokens: int = 0, stream=None, workspace=None):
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[-2]
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    attn_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, page_size, max_blocks_per_seq,
+                d ** -0.5 if scale is None else scale, chunk_tokens, workspace, stream)
+    return o, lse

@@ -1,0 +1,182 @@
+// C-ABI front end of libattn.so: argument checks (host only, before any HIP
+// call), chunk-size choice and workspace sizing for split-KV decode, and the
+// launches on the caller's stream.  The contract of every entry point is in
+// include/attn.h.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "attn_kernels.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// Clear a stale error left by an unrelated earlier call, launch, and map the result.
+template <typename F>
+int run(F &&launch)
+{
+    (void)hipGetLastError();
+    const hipError_t e = launch();
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+// Workgroups the split kernel should have at full capacity when the caller
+// leaves the chunk size to the library: enough to keep all 256 compute units
+// busy several times over, so uneven sequence lengths still balance.
+constexpr long long kDecodeTargetWorkgroups = 1024;
+constexpr int kDecodeMinChunk = 256;   // one pass of a split workgroup (8 waves x 32 tokens)
+constexpr int kDecodeMaxChunk = 2048;  // longer chunks unbalance mixed-length batches
+
+// Resolved chunk size, or a negative status.
+int resolve_chunk(int batch, int n_kv_heads, int page_size, int max_blocks, int chunk_tokens)
+{
+    if (batch < 0 || n_kv_heads <= 0 || page_size <= 0 || max_blocks <= 0 || chunk_tokens < 0)
+        return ATTN_ERR_SHAPE;
+    const long long cap = (long long)max_blocks * page_size;
+    if (cap > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+    if (chunk_tokens > 0) {
+        if (chunk_tokens % attn::kDecodeTokenQuantum != 0) return ATTN_ERR_UNSUPPORTED;
+        return chunk_tokens;
+    }
+    const long long units = (long long)(batch > 0 ? batch : 1) * n_kv_heads;
+    const long long splits = (kDecodeTargetWorkgroups + units - 1) / units;
+    long long chunk = (cap + splits - 1) / splits;
+    chunk = (chunk + kDecodeMinChunk - 1) / kDecodeMinChunk * kDecodeMinChunk;
+    if (chunk < kDecodeMinChunk) chunk = kDecodeMinChunk;
+    if (chunk > kDecodeMaxChunk) chunk = kDecodeMaxChunk;
+    return (int)chunk;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *attn_status_string(int status)
+{
+    switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_NULL: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid size argument";
+    case ATTN_ERR_GQA: return "n_q_heads is not a multiple of n_kv_heads";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, group size, page size or chunk size";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}
+
+int attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse, int batch,
+                 int seqlen, int n_q_heads, int n_kv_heads, int head_dim, int dtype, int causal,
+                 float scale, void *stream)
+{
+    if (batch < 0 || seqlen < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
+        return ATTN_ERR_SHAPE;
+    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
+    if (!head_dim_ok(head_dim) || (dtype != ATTN_F32 && dtype != ATTN_BF16))
+        return ATTN_ERR_UNSUPPORTED;
+    if (batch == 0 || seqlen == 0) return ATTN_OK;
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+        return ATTN_ERR_ALIGN;
+    // element offsets are formed in 64-bit; the grid is one dimension of query tiles
+    if ((long long)batch * n_q_heads * ((seqlen + 63) / 64) > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+
+    attn::PrefillParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    p.B = batch; p.N = seqlen; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
+    p.causal = causal ? 1 : 0;
+    p.scale = scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == ATTN_BF16) return run([&] { return attn::launch_prefill_bf16(p, s); });
+    return run([&] { return attn::launch_prefill_f32(p, s); });
+}
+
+int attn_decode_chunk_tokens(int batch, int n_kv_heads, int page_size, int max_blocks_per_seq,
+                             int chunk_tokens)
+{
+    return resolve_chunk(batch, n_kv_heads, page_size, max_blocks_per_seq, chunk_tokens);
+}
+
+size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                   int page_size, int max_blocks_per_seq, int chunk_tokens)
+{
+    if (n_q_heads <= 0 || head_dim <= 0) return 0;
+    const int chunk = resolve_chunk(batch, n_kv_heads, page_size, max_blocks_per_seq, chunk_tokens);
+    if (chunk <= 0) return 0;
+    const long long cap = (long long)max_blocks_per_seq * page_size;
+    const long long max_chunks = (cap + chunk - 1) / chunk;
+    return (size_t)batch * (size_t)n_q_heads * (size_t)max_chunks * (size_t)(head_dim + 1) * 4u;
+}
+
+int attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *block_table, const int32_t *seq_lens, void *o, float *lse_or_null,
+                int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,
+                int max_blocks_per_seq, int dtype, float scale, int chunk_tokens, void *workspace,
+                size_t workspace_bytes, void *stream)
+{
+    if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 ||
+        max_blocks_per_seq <= 0 || chunk_tokens < 0)
+        return ATTN_ERR_SHAPE;
+    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
+    if (!head_dim_ok(head_dim) || dtype != ATTN_BF16 ||
+        n_q_heads / n_kv_heads > attn::kDecodeMaxGroup)
+        return ATTN_ERR_UNSUPPORTED;
+    // paged blocks of 16 tokens must not straddle pages
+    if (block_table && page_size % attn::kDecodeTokenQuantum != 0) return ATTN_ERR_UNSUPPORTED;
+    const int chunk = resolve_chunk(batch, n_kv_heads, page_size, max_blocks_per_seq, chunk_tokens);
+    if (chunk < 0) return chunk;
+    if (batch == 0) return ATTN_OK;
+    if (!q || !k_cache || !v_cache || !seq_lens || !o) return ATTN_ERR_NULL;
+    const size_t need = attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+                                                    page_size, max_blocks_per_seq, chunk_tokens);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        !aligned16(workspace) || (lse_or_null && !aligned16(lse_or_null)))
+        return ATTN_ERR_ALIGN;
+    const long long cap = (long long)max_blocks_per_seq * page_size;
+    const long long max_chunks = (cap + chunk - 1) / chunk;
+    if (max_chunks > INT_MAX || n_kv_heads > 65535 || batch > 65535) return ATTN_ERR_UNSUPPORTED;
+
+    attn::DecodeParams p;
+    p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
+    p.block_table = block_table; p.seq_lens = seq_lens;
+    p.o = o; p.lse = lse_or_null;
+    p.B = batch; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
+    p.page_size = page_size; p.max_blocks = max_blocks_per_seq; p.dtype = dtype;
+    p.scale = scale;
+    p.chunk = chunk;
+    p.max_chunks = (int)max_chunks;
+    const size_t rows = (size_t)batch * n_q_heads;
+    p.o_parts = static_cast<float *>(workspace);
+    p.lse_parts = p.o_parts + rows * (size_t)max_chunks * head_dim;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return run([&] { return attn::launch_decode(p, s); });
+}
+
+int attn_lse_combine(const float *o_parts, const float *lse_parts, const int32_t *n_splits_or_null,
+                     int rows, int max_splits, int head_dim, void *o, int o_dtype,
+                     float *lse_or_null, void *stream)
+{
+    if (rows < 0 || max_splits <= 0 || head_dim <= 0) return ATTN_ERR_SHAPE;
+    if (!head_dim_ok(head_dim) || (o_dtype != ATTN_F32 && o_dtype != ATTN_BF16))
+        return ATTN_ERR_UNSUPPORTED;
+    if (rows == 0) return ATTN_OK;
+    if (!o_parts || !lse_parts || !o) return ATTN_ERR_NULL;
+    if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) ||
+        (lse_or_null && !aligned16(lse_or_null)) ||
+        (n_splits_or_null && !aligned16(n_splits_or_null)))
+        return ATTN_ERR_ALIGN;
+    attn::CombineParams p;
+    p.o_parts = o_parts; p.lse_parts = lse_parts; p.n_splits = n_splits_or_null;
+    p.rows = rows; p.max_splits = max_splits; p.head_dim = head_dim;
+    p.o = o; p.o_bf16 = (o_dtype == ATTN_BF16); p.lse = lse_or_null;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return run([&] { return attn::launch_lse_combine(p, s); });
+}
+
+}  // extern "C"

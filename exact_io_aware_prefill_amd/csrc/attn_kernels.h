@@ -1,0 +1,55 @@
+// Internal launch interface between the C-ABI front end (attn_api.cpp) and the
+// gfx950 kernels.  Not installed; callers use include/attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Tiled prefill, bf16 inputs on matrix cores (prefill_bf16.hip).
+struct PrefillParams {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;
+    int B, N, Hq, Hkv, head_dim, causal;
+    float scale;
+};
+hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream);
+
+// Tiled prefill, float32 arithmetic (prefill_f32.hip).
+hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream);
+
+// Split-KV decode: per-chunk partials, then the combine (decode.hip).
+struct DecodeParams {
+    const void *q, *k_cache, *v_cache;
+    const int32_t *block_table;  // NULL: contiguous cache
+    const int32_t *seq_lens;
+    void *o;
+    float *lse;  // may be NULL
+    int B, Hq, Hkv, head_dim, page_size, max_blocks, dtype;
+    float scale;
+    int chunk;        // resolved chunk size (tokens)
+    int max_chunks;   // ceil(max_blocks * page_size / chunk)
+    float *o_parts;   // [B*Hq, max_chunks, head_dim]
+    float *lse_parts; // [B*Hq, max_chunks]
+};
+hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+
+// Stand-alone combine of partials (decode.hip).
+struct CombineParams {
+    const float *o_parts, *lse_parts;
+    const int32_t *n_splits;  // may be NULL
+    int rows, max_splits, head_dim;
+    void *o;
+    bool o_bf16;  // true: o is bfloat16, false: float32
+    float *lse;   // may be NULL
+};
+hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream);
+
+// Decode tiling constants the host front end needs for validation/sizing.
+constexpr int kDecodeMaxGroup = 16;  // largest supported n_q_heads / n_kv_heads
+constexpr int kDecodeTokenQuantum = 16;  // chunk sizes are multiples of this
+
+}  // namespace attn

@@ -1,0 +1,135 @@
+// Tiled exact prefill attention in float32 arithmetic (gfx950 vector ALUs).
+//
+// Same method as the bf16 kernel (pofe.ai, "FlashAttention for inference: tiled
+// prefill and split-KV decoding", sections "Prefill: tiles, loop order and the
+// tensor cores" and "The online softmax, with every symbol defined"), for
+// float32 inputs whose results must stay within float32 rounding: no bf16
+// rounding anywhere, natural-base exponentials from the accurate device math
+// library.  One wave per (sequence, head, 64-row query tile), one query row per
+// lane; 32-key tiles of K and V are staged in LDS and read as broadcasts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int kRows = 64;  // query rows per workgroup (one wave)
+constexpr int kKeys = 32;  // keys per tile
+
+struct Args {
+    const float *q, *k, *v;
+    float *o, *lse;
+    int B, N, Hq, Hkv, group, causal, n_qtiles;
+    float scale;
+};
+
+template <int D>
+__global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
+{
+    __shared__ __attribute__((aligned(16))) float Ks[kKeys * D];
+    __shared__ __attribute__((aligned(16))) float Vs[kKeys * D];
+
+    const int tid = threadIdx.x;
+    const int nbh = a.B * a.Hq;
+    const int qtile = a.n_qtiles - 1 - (int)(blockIdx.x / nbh);
+    const int bh = (int)(blockIdx.x % nbh);
+    const int b = bh / a.Hq, h = bh % a.Hq, hk = h / a.group;
+    const int q0 = qtile * kRows;
+    const int qrow = q0 + tid;
+    const float *kp = a.k + (size_t)(b * a.Hkv + hk) * a.N * D;
+    const float *vp = a.v + (size_t)(b * a.Hkv + hk) * a.N * D;
+
+    float q[D], acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        q[d] = (qrow < a.N) ? a.q[((size_t)bh * a.N + qrow) * D + d] : 0.f;
+        acc[d] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+
+    const int kend = a.causal ? min(a.N, q0 + kRows) : a.N;
+    for (int k0 = 0; k0 < kend; k0 += kKeys) {
+        __syncthreads();
+        for (int idx = tid; idx < kKeys * D / 4; idx += kRows) {
+            const int r = idx / (D / 4), c = idx % (D / 4);
+            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+            if (k0 + r < a.N) {
+                kv = *reinterpret_cast<const float4 *>(kp + (size_t)(k0 + r) * D + 4 * c);
+                vv = *reinterpret_cast<const float4 *>(vp + (size_t)(k0 + r) * D + 4 * c);
+            }
+            *reinterpret_cast<float4 *>(&Ks[r * D + 4 * c]) = kv;
+            *reinterpret_cast<float4 *>(&Vs[r * D + 4 * c]) = vv;
+        }
+        __syncthreads();
+
+        float s[kKeys];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < kKeys; ++t) {
+            float dot = 0.f;
+#pragma unroll
+            for (int d = 0; d < D; ++d) dot = fmaf(q[d], Ks[t * D + d], dot);
+            float x = dot * a.scale;
+            const int key = k0 + t;
+            if (key >= a.N || (a.causal && key > qrow)) x = -INFINITY;
+            s[t] = x;
+            mx = fmaxf(mx, x);
+        }
+        const float m_new = fmaxf(m, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // nothing visible yet
+        const float c = expf(m - m_use);
+        l *= c;
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] *= c;
+#pragma unroll
+        for (int t = 0; t < kKeys; ++t) {
+            const float p = expf(s[t] - m_use);
+            l += p;
+#pragma unroll
+            for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vs[t * D + d], acc[d]);
+        }
+        m = m_new;
+    }
+
+    if (qrow < a.N) {
+        float *orow = a.o + ((size_t)bh * a.N + qrow) * D;
+        if (l > 0.f) {
+            const float inv = 1.f / l;
+#pragma unroll
+            for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
+            a.lse[(size_t)bh * a.N + qrow] = m + logf(l);
+        } else {  // no visible key (not reachable for square causal or full attention)
+#pragma unroll
+            for (int d = 0; d < D; ++d) orow[d] = 0.f;
+            a.lse[(size_t)bh * a.N + qrow] = -INFINITY;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream)
+{
+    Args a;
+    a.q = static_cast<const float *>(p.q);
+    a.k = static_cast<const float *>(p.k);
+    a.v = static_cast<const float *>(p.v);
+    a.o = static_cast<float *>(p.o);
+    a.lse = p.lse;
+    a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.group = p.Hq / p.Hkv;
+    a.causal = p.causal;
+    a.n_qtiles = (p.N + kRows - 1) / kRows;
+    a.scale = p.scale;
+    const long long nblk = (long long)a.n_qtiles * p.B * p.Hq;
+    if (nblk == 0) return hipSuccess;
+    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (p.head_dim == 128)
+        hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((unsigned)nblk), dim3(kRows), 0, stream, a);
+    else
+        hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((unsigned)nblk), dim3(kRows), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace attn

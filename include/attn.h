@@ -1,0 +1,161 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact attention with an online softmax on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the ones described on the pofe.ai page "FlashAttention
+ * for inference: tiled prefill and split-KV decoding":
+ *   - attn_prefill: tiled causal (or full) prefill; query tiles walk key/value
+ *     tiles, scores stay on chip, each row keeps a running max and sum, and
+ *     the row log-sum-exp is written out (sections "The online softmax, with
+ *     every symbol defined" and "Prefill: tiles, loop order and the tensor
+ *     cores");
+ *   - attn_decode: one query token per sequence against a paged (or
+ *     contiguous) KV cache, the keys split into chunks processed by separate
+ *     workgroups, each chunk's (output, log-sum-exp) merged by a separate
+ *     reduction (section "Decode: a different bottleneck"; layouts from
+ *     section "Minimal implementation");
+ *   - attn_lse_combine: that reduction on its own -- the combine rule for
+ *     independent partials, a softmax over the partials' log-sum-exps
+ *     (section "The online softmax, with every symbol defined" and the
+ *     `merge` helper of section "Minimal implementation").
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is a DEVICE pointer owned by the caller; the
+ *     library allocates nothing, keeps no state between calls and is safe to
+ *     call from several host threads.  Tensors are dense, row-major, with the
+ *     layouts stated per call, and must be 16-byte aligned.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     null stream).  Nothing synchronises with the host.
+ *   - Return value: ATTN_OK (0) or a negative status.  Argument errors are
+ *     detected on the host before any HIP call, so they are reported even on a
+ *     machine without a GPU.  A failed launch is reported as ATTN_ERR_HIP.
+ *     There is no silent fallback to another algorithm or precision: a shape,
+ *     dtype or head size the kernels do not implement is ATTN_ERR_UNSUPPORTED.
+ *   - Values the host cannot see (seq_lens and block_table contents) are the
+ *     caller's responsibility: each seq_lens[b] must lie in
+ *     [0, max_blocks_per_seq * page_size] (the kernels clamp a value outside
+ *     that range into it rather than read past the cache) and each
+ *     block-table entry a sequence reaches must name a page of the cache.
+ *   - Scores are s = scale * <q, k>; LSE outputs are natural logarithms over
+ *     scaled scores, lse = m + ln(l).  A row with no visible key gets O = 0 and
+ *     LSE = -inf.
+ *   - Grouped-query attention: query head h reads KV head h / (n_q_heads /
+ *     n_kv_heads) (consecutive query heads share a KV head).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define ATTN_OK               0
+#define ATTN_ERR_NULL        -1  /* a required pointer is NULL                          */
+#define ATTN_ERR_SHAPE       -2  /* a size is <= 0 (or negative where 0 is allowed)     */
+#define ATTN_ERR_GQA         -3  /* n_q_heads is not a multiple of n_kv_heads            */
+#define ATTN_ERR_UNSUPPORTED -4  /* head_dim, dtype, group size or chunk not implemented */
+#define ATTN_ERR_WORKSPACE   -5  /* workspace NULL or smaller than required             */
+#define ATTN_ERR_ALIGN       -6  /* a tensor pointer is not 16-byte aligned             */
+#define ATTN_ERR_HIP         -7  /* the HIP runtime reported an error at launch          */
+
+/* ---- element types ----------------------------------------------------- */
+#define ATTN_F32  0  /* IEEE binary32                                   */
+#define ATTN_BF16 1  /* bfloat16 (upper half of binary32), stored 2 B   */
+
+/*
+ * attn_prefill -- exact attention for a whole prompt, O = softmax(scale*QK^T) V.
+ *
+ *   q    [batch, n_q_heads,  seqlen, head_dim]  element type `dtype`
+ *   k, v [batch, n_kv_heads, seqlen, head_dim]  element type `dtype`
+ *   o    [batch, n_q_heads,  seqlen, head_dim]  element type `dtype` (written)
+ *   lse  [batch, n_q_heads,  seqlen] float32, row log-sum-exp (written; required)
+ *   causal != 0: row i attends keys 0..i; causal == 0: all keys.
+ *   head_dim in {64, 128}; dtype ATTN_BF16 (matrix cores, bf16 products with
+ *   float32 accumulation; P is rounded to bf16 before the P*V product; O is
+ *   rounded to nearest even) or ATTN_F32 (float32 arithmetic throughout).
+ *   batch, seqlen >= 0 (an empty call does nothing); heads >= 1.
+ */
+int attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
+                 int batch, int seqlen, int n_q_heads, int n_kv_heads, int head_dim,
+                 int dtype, int causal, float scale, void *stream);
+
+/*
+ * attn_decode -- one new query token per sequence against a KV cache, by
+ * split-KV: the first seq_lens[b] tokens of sequence b are cut into chunks of
+ * `chunk_tokens`; one workgroup per (sequence, KV head, chunk) computes the
+ * chunk's normalised output and log-sum-exp for all query heads of that KV
+ * head; a second kernel merges the chunks with the combine rule.
+ *
+ *   q        [batch, n_q_heads, head_dim]                      element `dtype`
+ *   k_cache, v_cache:
+ *     paged      (block_table != NULL): [num_pages, page_size, n_kv_heads, head_dim]
+ *     contiguous (block_table == NULL): [batch, max_blocks_per_seq*page_size,
+ *                                        n_kv_heads, head_dim]
+ *   block_table [batch, max_blocks_per_seq] int32: token t of sequence b is
+ *               slot t % page_size of page block_table[b][t / page_size]
+ *   seq_lens    [batch] int32: number of cached tokens the query attends
+ *               (already including the new token's own key/value)
+ *   o           [batch, n_q_heads, head_dim]  element `dtype` (written)
+ *   lse_or_null [batch, n_q_heads] float32 (written when not NULL)
+ *   chunk_tokens: 0 = choose from batch, heads and capacity (see
+ *               attn_decode_chunk_tokens); otherwise a positive multiple of 16.
+ *   workspace / workspace_bytes: device scratch of at least
+ *               attn_decode_workspace_bytes(...) bytes for the per-chunk
+ *               partials; contents on entry are ignored.
+ *   head_dim in {64, 128}; n_q_heads / n_kv_heads <= 16; dtype ATTN_BF16 only
+ *   (bf16 products on matrix cores with float32 accumulation, P rounded to bf16
+ *   before the P*V product, partials and the combine in float32, O rounded to
+ *   nearest even).  A paged cache needs page_size a multiple of 16 (no 16-token
+ *   block straddles two pages); for a contiguous cache page_size only sets the
+ *   capacity max_blocks_per_seq * page_size.
+ */
+int attn_decode(const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *block_table, const int32_t *seq_lens, void *o,
+                float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                int page_size, int max_blocks_per_seq, int dtype, float scale,
+                int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_chunk_tokens -- the chunk size attn_decode uses for these
+ * arguments (resolves chunk_tokens == 0), or a negative status.
+ */
+int attn_decode_chunk_tokens(int batch, int n_kv_heads, int page_size, int max_blocks_per_seq,
+                             int chunk_tokens);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of workspace attn_decode needs:
+ * batch * n_q_heads * ceil(max_blocks_per_seq*page_size / chunk) * (head_dim + 1) * 4
+ * (partials are float32), or 0 if the arguments are invalid.
+ */
+size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                                   int page_size, int max_blocks_per_seq, int chunk_tokens);
+
+/*
+ * attn_lse_combine -- merge independent partial results of the same rows:
+ * Lambda = ln sum_k exp(lambda_k), o = sum_k exp(lambda_k - Lambda) o_k.
+ *
+ *   o_parts   [rows, max_splits, head_dim] float32 (normalised partial outputs)
+ *   lse_parts [rows, max_splits] float32 (their log-sum-exps; -inf = empty)
+ *   n_splits_or_null [rows] int32: use the first n_splits[r] partials of row r
+ *               (0 <= n <= max_splits); NULL = all max_splits
+ *   o         [rows, head_dim] element type `o_dtype` (ATTN_F32 or ATTN_BF16)
+ *   lse_or_null [rows] float32 (written when not NULL)
+ *   A row whose partials are all empty gets o = 0, Lambda = -inf.
+ *   head_dim in {64, 128}; rows >= 0; max_splits >= 1.
+ */
+int attn_lse_combine(const float *o_parts, const float *lse_parts,
+                     const int32_t *n_splits_or_null, int rows, int max_splits, int head_dim,
+                     void *o, int o_dtype, float *lse_or_null, void *stream);
+
+/* attn_status_string -- static, human-readable text for a status code. */
+const char *attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,149 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every entry
+point include/attn.h declares, and rejects bad arguments on the host (before any
+HIP call) with the documented status codes."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+attn = pytest.importorskip("exact_io_aware_prefill_amd.attn",
+                           reason="libattn.so not built (python -m exact_io_aware_prefill_amd.build)")
+
+FAKE = 0x10000  # a 16-byte aligned, never dereferenced address
+MIS = FAKE + 4  # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(attn_[a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(attn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    for name in declared_functions():
+        assert hasattr(attn.lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", attn._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(attn_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name in ("ATTN_OK", "ATTN_ERR_NULL", "ATTN_ERR_SHAPE", "ATTN_ERR_GQA", "ATTN_ERR_UNSUPPORTED",
+                 "ATTN_ERR_WORKSPACE", "ATTN_ERR_ALIGN", "ATTN_ERR_HIP", "ATTN_F32", "ATTN_BF16"):
+        m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(attn, name), name
+    for code in range(-7, 1):
+        s = attn.attn_status_string(code)
+        assert s and s != "unknown status"
+    assert attn.attn_status_string(-99) == "unknown status"
+
+
+def P(x):
+    return ctypes.c_void_p(x)
+
+
+def prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, N=16, Hq=4, Hkv=2, d=128, dtype=1, causal=1):
+    return attn.lib.attn_prefill(P(q), P(k), P(v), P(o), P(lse), B, N, Hq, Hkv, d, dtype, causal,
+                                 0.1, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), attn.ATTN_ERR_NULL),
+    (dict(lse=0), attn.ATTN_ERR_NULL),
+    (dict(B=-1), attn.ATTN_ERR_SHAPE),
+    (dict(N=-5), attn.ATTN_ERR_SHAPE),
+    (dict(Hq=0), attn.ATTN_ERR_SHAPE),
+    (dict(d=0), attn.ATTN_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=7), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(k=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(o=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(B=0, q=0, k=0, v=0, o=0, lse=0), attn.ATTN_OK),   # empty call: nothing to do
+    (dict(N=0, q=0, k=0, v=0, o=0, lse=0), attn.ATTN_OK),
+])
+def test_prefill_argument_errors(kw, code):
+    assert prefill(**kw) == code
+
+
+def decode(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, d=128, P_=16,
+           maxb=8, dtype=1, chunk=0, ws=FAKE, wsb=1 << 30):
+    return attn.lib.attn_decode(P(q), P(kc), P(vc), P(bt), P(sl), P(o), P(lse), B, Hq, Hkv, d, P_,
+                                maxb, dtype, 0.1, chunk, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), attn.ATTN_ERR_NULL),
+    (dict(sl=0), attn.ATTN_ERR_NULL),
+    (dict(o=0), attn.ATTN_ERR_NULL),
+    (dict(B=-1), attn.ATTN_ERR_SHAPE),
+    (dict(P_=0), attn.ATTN_ERR_SHAPE),
+    (dict(maxb=0), attn.ATTN_ERR_SHAPE),
+    (dict(chunk=-16), attn.ATTN_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
+    (dict(d=80), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=0), attn.ATTN_ERR_UNSUPPORTED),          # decode is bf16 only
+    (dict(Hq=34, Hkv=2), attn.ATTN_ERR_UNSUPPORTED),     # group of 17 > 16
+    (dict(chunk=24), attn.ATTN_ERR_UNSUPPORTED),         # not a multiple of 16
+    (dict(P_=8), attn.ATTN_ERR_UNSUPPORTED),             # paged blocks would straddle pages
+    (dict(ws=0), attn.ATTN_ERR_WORKSPACE),
+    (dict(wsb=16), attn.ATTN_ERR_WORKSPACE),
+    (dict(vc=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(ws=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(lse=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(B=0, q=0, kc=0, vc=0, bt=0, sl=0, o=0, ws=0), attn.ATTN_OK),
+])
+def test_decode_argument_errors(kw, code):
+    assert decode(**kw) == code
+
+
+def test_decode_contiguous_accepts_any_page_size_for_capacity():
+    # page_size only fixes capacity when block_table is NULL; with a NULL workspace the
+    # host check stops at ERR_WORKSPACE, i.e. after the page-size checks passed
+    assert decode(bt=0, P_=8, ws=0) == attn.ATTN_ERR_WORKSPACE
+
+
+def test_workspace_formula_and_chunk_choice():
+    # explicit chunk: B * Hq * ceil(cap / chunk) * (d + 1) * 4
+    assert attn.attn_decode_workspace_bytes(1, 28, 4, 128, 16, 2048, 512) == 1 * 28 * 64 * 129 * 4
+    assert attn.attn_decode_workspace_bytes(3, 8, 2, 64, 16, 10, 48) == 3 * 8 * 4 * 65 * 4
+    assert attn.attn_decode_chunk_tokens(1, 4, 16, 2048, 512) == 512
+    # automatic choice: a multiple of 256 tokens between 256 and 2048
+    for B, Hkv, maxb in [(1, 4, 2048), (32, 8, 2048), (1, 1, 1), (128, 8, 64), (4, 2, 100000)]:
+        c = attn.attn_decode_chunk_tokens(B, Hkv, 16, maxb, 0)
+        assert 256 <= c <= 2048 and c % 256 == 0
+        assert attn.attn_decode_workspace_bytes(B, 4 * Hkv, Hkv, 128, 16, maxb, 0) == \
+            B * 4 * Hkv * (-(-(maxb * 16) // c)) * 129 * 4
+    assert attn.attn_decode_workspace_bytes(1, 28, 4, 128, 16, 2048, 24) == 0
+    with pytest.raises(attn.AttnError):
+        attn.attn_decode_chunk_tokens(1, 4, 16, 2048, 20)
+
+
+def combine(op=FAKE, lp=FAKE, ns=0, rows=4, S=3, d=128, o=FAKE, odt=1, lse=0):
+    return attn.lib.attn_lse_combine(P(op), P(lp), P(ns), rows, S, d, P(o), odt, P(lse), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=0), attn.ATTN_ERR_NULL),
+    (dict(o=0), attn.ATTN_ERR_NULL),
+    (dict(rows=-1), attn.ATTN_ERR_SHAPE),
+    (dict(S=0), attn.ATTN_ERR_SHAPE),
+    (dict(d=32), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(odt=5), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(lp=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(rows=0, op=0, lp=0, o=0), attn.ATTN_OK),
+])
+def test_combine_argument_errors(kw, code):
+    assert combine(**kw) == code

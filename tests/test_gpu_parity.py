@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path through the C-ABI against the fp64 oracle, element by
+element on the same seeded inputs.  Bars: float32 inputs max |err| <= 1e-5 on O and
+LSE; bf16 inputs (float32 accumulation) max |err| <= 2e-2 on O and <= 1e-3 on LSE.
+Full-size long-prefill workloads are compared on sampled rows (every row whose index
+is a multiple of a prime stride, so every position inside a tile is hit)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_prefill_amd import workloads as W
+from gpu_common import BF16_TOL, F32_TOL, check, dev, say, stats
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def attn():
+    from exact_io_aware_prefill_amd import attn as a  # raises if libattn.so is missing
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return a
+
+
+def run_prefill(attn, x):
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    o, lse = attn.prefill(q, k, v, x.causal, x.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ------------------------------------------------------------------ prefill fp32
+def test_worked_example_through_f32_prefill(attn):
+    say("case: worked example, f32 prefill N=4 d=64")
+    x = W.worked_example_inputs(64)
+    o, lse = run_prefill(attn, x)
+    e = math.e
+    rows_o = [1.0, e**2 / (e**2 + e), (e**2 + 2 * e**4) / (e**2 + e + e**4),
+              (e**2 + 2 * e**4 - e**3) / (e**2 + e + e**4 + e**3)]
+    rows_l = [2.0, math.log(e**2 + e), math.log(e**2 + e + e**4), math.log(e**2 + e + e**4 + e**3)]
+    oc = o.cpu().numpy()[0, 0]
+    assert np.max(np.abs(oc[:, 0] - rows_o)) <= 1e-5
+    assert np.max(np.abs(lse.cpu().numpy()[0, 0] - rows_l)) <= 1e-5
+    assert abs(oc[3, 0] - 1.1381) < 5e-5  # the page's printed result
+    assert np.all(oc[:, 1:] == 0.0)
+    ro, rl = oracle.prefill(x.q, x.k, x.v, True, 1.0)
+    check("worked-example", o, lse, ro, rl, F32_TOL)
+
+
+def test_small_f32_prefill_workload(attn):
+    cfg = W.PREFILL_SMALL_F32
+    say("case:", cfg["name"])
+    x = W.make_prefill(cfg)
+    assert x.scale == 1.0 / 8.0
+    o, lse = run_prefill(attn, x)
+    ro, rl = oracle.prefill(x.q, x.k, x.v, True, x.scale)
+    check(cfg["name"], o, lse, ro, rl, F32_TOL)
+
+
+@pytest.mark.parametrize("N", [1, 7, 64, 65, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_f32_prefill_ragged(attn, N, d, causal):
+    say("case: f32 prefill B=2 Hq=4 Hkv=2 N=%d d=%d causal=%s" % (N, d, causal))
+    x = W.prefill_inputs(100 + N + d, 2, 4, 2, N, d, W.F32, causal=causal)
+    o, lse = run_prefill(attn, x)
+    ro, rl = oracle.prefill(x.q, x.k, x.v, causal, x.scale)
+    check("f32 N=%d d=%d" % (N, d), o, lse, ro, rl, F32_TOL)
+
+
+# ------------------------------------------------------------------ prefill bf16
+def test_prefill_2k_workload(attn):
+    cfg = W.PREFILL_2K
+    say("case:", cfg["name"])
+    x = W.make_prefill(cfg)
+    o, lse = run_prefill(attn, x)
+    ro, rl = oracle.prefill(x.q, x.k, x.v, True, x.scale)
+    check(cfg["name"], o, lse, ro, rl, BF16_TOL)
+
+
+@pytest.mark.parametrize("N", [1, 5, 64, 127, 129, 300, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_prefill_ragged(attn, N, d, causal):
+    say("case: bf16 prefill B=2 Hq=6 Hkv=2 N=%d d=%d causal=%s" % (N, d, causal))
+    x = W.prefill_inputs(200 + N + d, 2, 6, 2, N, d, W.BF16, causal=causal)
+    o, lse = run_prefill(attn, x)
+    ro, rl = oracle.prefill(x.q, x.k, x.v, causal, x.scale)
+    check("bf16 N=%d d=%d causal=%d" % (N, d, causal), o, lse, ro, rl, BF16_TOL)
+
+
+def test_bf16_prefill_peaky_softmax(attn):
+    """Queries scaled by 10: near one-hot rows, frequent rescaling (c << 1)."""
+    say("case: bf16 prefill peaky (q x10) N=777 d=128")
+    x = W.prefill_inputs(7, 1, 4, 1, 777, 128, W.BF16)
+    x.q = (x.q.float() * 10.0).to(torch.bfloat16)
+    o, lse = run_prefill(attn, x)
+    ro, rl = oracle.prefill(x.q, x.k, x.v, True, x.scale)
+    check("peaky", o, lse, ro, rl, BF16_TOL)
+
+
+@pytest.mark.parametrize("N,row_step", [(8192, 31), (16384, 61), (30720, 97)])
+def test_long_prefill_workloads_sampled_rows(attn, N, row_step):
+    cfg = W.prefill_long(N)
+    say("case:", cfg["name"], "rows sampled every", row_step)
+    x = W.make_prefill(cfg)
+    o, lse = run_prefill(attn, x)
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    ro, rl = oracle.prefill(x.q, x.k, x.v, True, x.scale, row_step=row_step)
+    rows = np.arange(N) % row_step == 0
+    check(cfg["name"], o[:, :, rows].float().cpu().numpy(), lse[:, :, rows].cpu().numpy(),
+          ro[:, :, rows], rl[:, :, rows], BF16_TOL)
+    # a property at every row: LSE >= the row's own (diagonal) scaled score
+    diag = (x.q.float() * x.k.float().repeat_interleave(7, dim=1)).sum(-1) * x.scale
+    assert (lse.cpu() >= diag - 1e-3).all()
+
+
+# ------------------------------------------------------------------ combine
+def test_worked_example_through_lse_combine(attn):
+    say("case: worked example through attn_lse_combine")
+    e = math.e
+    o1, l1 = e**2 / (e**2 + e), math.log(e**2 + e)
+    o2, l2 = (2 * e**4 - e**3) / (e**4 + e**3), math.log(e**4 + e**3)
+    op = torch.zeros(1, 2, 64, dtype=torch.float32)
+    op[0, 0, 0], op[0, 1, 0] = o1, o2
+    lp = torch.tensor([[l1, l2]], dtype=torch.float32)
+    o = torch.empty(1, 64, dtype=torch.float32, device="cuda")
+    lse = torch.empty(1, dtype=torch.float32, device="cuda")
+    attn.attn_lse_combine(dev(op), dev(lp), None, o, lse)
+    torch.cuda.synchronize()
+    assert abs(o[0, 0].item() - 1.1380900204) <= 1e-5
+    assert abs(lse[0].item() - 4.4401896986) <= 1e-5
+    assert (o[0, 1:] == 0).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_lse_combine_random_partials(attn, d, odt):
+    say("case: lse_combine random partials d=%d out=%s" % (d, odt))
+    g = torch.Generator().manual_seed(d)
+    rows, S = 37, 300
+    op = torch.randn(rows, S, d, generator=g)
+    lp = torch.randn(rows, S, generator=g) * 4
+    lp[3, 7] = float("-inf")   # an empty partial
+    lp[5, :] = float("-inf")   # a row with only empty partials
+    ns = torch.randint(0, S + 1, (rows,), generator=g, dtype=torch.int32)
+    ns[0], ns[1], ns[5] = 0, 1, S
+    o = torch.empty(rows, d, dtype=odt, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    attn.attn_lse_combine(dev(op), dev(lp), dev(ns), o, lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.lse_combine(op, lp, ns)
+    tol = F32_TOL if odt == torch.float32 else dict(o=1e-2, lse=1e-5)
+    check("combine d=%d" % d, o, lse, ro, rl, tol)
+
+
+# ------------------------------------------------------------------ decode
+def run_decode(attn, x, chunk):
+    out = attn.decode(dev(x.q), dev(x.k_cache), dev(x.v_cache), dev(x.block_table), dev(x.seq_lens),
+                      x.page_size, x.max_blocks, x.scale, chunk)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode(x):
+    return oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale,
+                         x.page_size, x.max_blocks)
+
+
+def test_decode_32k_workload(attn):
+    cfg = W.DECODE_32K
+    say("case:", cfg["name"])
+    x = W.make_decode_32k(cfg)
+    assert attn.attn_decode_chunk_tokens(1, 4, x.page_size, x.max_blocks, 512) == 512
+    assert -(-cfg["S"] // 512) == 64
+    o, lse = run_decode(attn, x, cfg["chunk"])
+    ro, rl = oracle_decode(x)
+    check(cfg["name"], o, lse, ro, rl, BF16_TOL)
+
+
+def test_decode_paged_workload(attn):
+    cfg = W.DECODE_PAGED
+    say("case:", cfg["name"])
+    x = W.make_decode_paged(cfg)
+    o, lse = run_decode(attn, x, 0)
+    ro, rl = oracle_decode(x)
+    check(cfg["name"], o, lse, ro, rl, BF16_TOL)
+
+
+LENS = [1, 15, 16, 17, 100, 511, 513, 1000]
+
+
+@pytest.mark.parametrize("g", [1, 4, 7, 16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("chunk", [16, 256, 512])
+def test_decode_ragged(attn, g, d, paged, chunk):
+    say("case: decode g=%d d=%d paged=%s chunk=%d" % (g, d, paged, chunk))
+    Hkv = 2
+    if paged:
+        x = W.decode_paged_inputs(300 + g + d, len(LENS), g * Hkv, Hkv, d, 16, 1, 1024, lengths=LENS)
+    else:
+        x = W.decode_contiguous_inputs(300 + g + d, len(LENS), g * Hkv, Hkv, 1024, d, seq_lens=LENS)
+    o, lse = run_decode(attn, x, chunk)
+    ro, rl = oracle_decode(x)
+    check("decode g=%d d=%d paged=%d chunk=%d" % (g, d, paged, chunk), o, lse, ro, rl, BF16_TOL)
+
+
+def test_decode_empty_sequence(attn):
+    say("case: decode with seq_len 0")
+    x = W.decode_contiguous_inputs(9, 3, 8, 2, 64, 128, seq_lens=[0, 5, 0])
+    o, lse = run_decode(attn, x, 32)
+    assert (o[0] == 0).all() and torch.isneginf(lse[0]).all()
+    assert (o[2] == 0).all() and torch.isneginf(lse[2]).all()
+    ro, rl = oracle_decode(x)
+    check("decode empty", o, lse, ro, rl, BF16_TOL)
