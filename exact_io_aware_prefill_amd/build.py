@@ -20,6 +20,9 @@ LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+# per-source extra flags: the bf16 prefill assumes finite inputs so its row max
+# compiles to v_max3_f32 without NaN-quieting copies (infinities stay IEEE)
+EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -45,7 +48,7 @@ def common_flags() -> list:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(os.path.basename(src))[0] + ".o")
-    cmd = [hipcc()] + common_flags() + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

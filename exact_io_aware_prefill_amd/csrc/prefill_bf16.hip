@@ -11,7 +11,7 @@
 // the diagonal tile is masked.
 //
 // gfx950 mapping
-//   * workgroup = 4 waves x 32 query rows = 128 rows; key/value tile = 64 keys.
+//   * workgroup = WAVES waves x 32 query rows; key/value tile = 64 keys.
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //     A = K rows read from LDS, B = the wave's Q rows kept in registers for the
 //     whole kernel.  In the 32x32 accumulator a lane holds one query (lane % 32)
@@ -23,9 +23,30 @@
 //     accumulator holds them) and every lane again owns one query, so the
 //     rescale by c is per lane.  V is written to LDS transposed, in that key
 //     order, so each A fragment is one 16-byte LDS read.
-//   * Exponentials run in base 2 with scale*log2(e) folded into the scores.
-//   * Query tiles are issued longest-first (causal rows near the end see the
-//     most keys).
+//   * Software pipeline: iteration t issues the P*V product of tile t-1 and the
+//     scores of tile t+1 on the matrix cores while the vector ALUs compute the
+//     softmax of tile t, all in one basic block, so the two units overlap
+//     inside a wave.  K/V tiles are double-buffered in LDS and fetched one
+//     iteration ahead with buffer loads (scalar tile offsets, out-of-range rows
+//     read as zero); one barrier per tile.
+//   * The exponentials of tile t use the running max from before the tile,
+//     so they do not wait for the tile's own row max.  Only if some row's new
+//     scores exceed that max by more than 2^8 (in base-2 units) does a rare
+//     fix-up path raise the max, rescale l and O by c, and recompute the tile's
+//     probabilities.  Any reference value gives the same O = acc/l and
+//     LSE = m + ln l; the bound keeps every probability <= 256 in float32.
+//     Exponentials run in base 2 with scale*log2(e) folded into one FMA.
+//   * Work order: consecutive workgroup ids are dispatched round-robin over the
+//     8 XCDs, each with its own L2.  Ids are remapped so each XCD receives a
+//     contiguous slice of a list ordered (sequence, KV head, query tile, query
+//     head): the workgroups resident on one XCD share one KV head's keys and
+//     values in L2.  Query tiles are listed in zig-zag order (last, first,
+//     second last, second, ...) so every slice carries the same causal work
+//     and the longest tiles start first.
+//
+// This file is compiled with -fno-honor-nans (inputs must be finite): the row
+// max then maps to v_max3_f32 without NaN-quieting copies.  Infinities, which
+// the masking relies on, keep their IEEE meaning.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,58 +58,217 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBlockM = kWaves * 32;  // query rows per workgroup
-constexpr int kBlockN = 64;           // keys per tile
+constexpr int kBlockN = 64;  // keys per tile
+constexpr int kXcds = 8;     // MI355X: workgroups are dispatched round-robin over 8 XCDs
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kRescaleLog2 = 8.f;             // raise the reference max only past 2^8
+constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
 struct Args {
     const uint16_t *q, *k, *v;
     uint16_t *o;
     float *lse;
-    int B, N, Hq, Hkv, group, causal, n_qtiles;
-    float scale_log2;  // scale * log2(e)
+    int B, N, Hq, Hkv, group, causal, n_qtiles, n_items;
+    int negate_q;      // 1 when the caller's scale is negative
+    float scale_log2;  // |scale| * log2(e)
+    float scale;       // |scale|
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 
 // Position of key group `sub` (keys 4*sub..4*sub+3 of a 16-key step) inside
 // the transposed V row: lanes of the lower half-wave read keys {0-3, 8-11},
 // the upper half {4-7, 12-15}, matching the 32x32 accumulator rows.
 __device__ __forceinline__ int vt_slot(int sub) { return ((sub & 1) << 3) | ((sub & 2) << 1); }
 
+// Global -> register -> LDS staging of one K tile (row-major) and one V tile
+// (transposed into the accumulator key order).  Each thread owns fixed chunks;
+// the tile offset is a scalar, so a load is one buffer instruction.
+template <int D, int NT>
+struct Stage {
+    static constexpr int KS = D + 8;        // K row stride in LDS (bf16): 16-byte aligned, bank-rotating
+    static constexpr int VS = kBlockN + 8;  // transposed-V row stride in LDS (bf16)
+    static constexpr int KBUF = kBlockN * KS;
+    static constexpr int VBUF = D * VS;
+    static constexpr int KCHUNKS = kBlockN * D / 8;         // 16-byte chunks of a K tile
+    static constexpr int KPT = (KCHUNKS + NT - 1) / NT;     // per thread
+    static constexpr int VUNITS = (kBlockN / 2) * (D / 8);  // units of 2 keys x 8 dims
+    static constexpr int VPT = (VUNITS + NT - 1) / NT;
+    uint4 kr[KPT];
+    uint4 vr[VPT][2];
+    uint32_t koff[KPT], kls[KPT];  // global byte offset within a tile / LDS element offset
+    uint32_t voff[VPT], vls[VPT];
+
+    __device__ __forceinline__ void init(int tid)
+    {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int ch = tid + i * NT;
+            const int r = ch / (D / 8), c = ch % (D / 8);
+            koff[i] = (uint32_t)(r * D + 8 * c) * 2u;
+            kls[i] = (uint32_t)(r * KS + 8 * c);
+        }
+#pragma unroll
+        for (int i = 0; i < VPT; ++i) {
+            const int un = tid + i * NT;
+            const int kp = un % (kBlockN / 2), dc = un / (kBlockN / 2);  // key pair, 8-dim chunk
+            const int kg = kp >> 1;
+            voff[i] = (uint32_t)(2 * kp * D + 8 * dc) * 2u;
+            vls[i] = (uint32_t)((8 * dc) * VS + 16 * (kg >> 2) + vt_slot(kg & 3) + 2 * (kp & 1));
+        }
+    }
+
+    __device__ __forceinline__ bool kvalid(int i, int tid) const { return KCHUNKS % NT == 0 || tid + i * NT < KCHUNKS; }
+    __device__ __forceinline__ bool vvalid(int i, int tid) const { return VUNITS % NT == 0 || tid + i * NT < VUNITS; }
+
+    __device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rk, int k0, int tid)
+    {
+        const uint32_t so = (uint32_t)k0 * D * 2u;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+            if (kvalid(i, tid)) kr[i] = bload16(rk, koff[i], so);
+    }
+    __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, int k0, int tid)
+    {
+        const uint32_t so = (uint32_t)k0 * D * 2u;
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+            if (vvalid(i, tid)) {
+                vr[i][0] = bload16(rv, voff[i], so);
+                vr[i][1] = bload16(rv, voff[i] + D * 2u, so);
+            }
+    }
+    __device__ __forceinline__ void store_k(uint16_t *Ks, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+            if (kvalid(i, tid)) *reinterpret_cast<uint4 *>(&Ks[kls[i]]) = kr[i];
+    }
+    __device__ __forceinline__ void store_v(uint16_t *Vt, int tid) const
+    {
+#pragma unroll
+        for (int i = 0; i < VPT; ++i)
+            if (vvalid(i, tid)) {
+                const uint32_t a[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
+                const uint32_t b[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    // dim 8*dc+2p: (key0, key1) low halves; dim 8*dc+2p+1: high halves
+                    *reinterpret_cast<uint32_t *>(&Vt[vls[i] + (2 * p) * VS]) = (a[p] & 0xffffu) | (b[p] << 16);
+                    *reinterpret_cast<uint32_t *>(&Vt[vls[i] + (2 * p + 1) * VS]) = (a[p] >> 16) | (b[p] & 0xffff0000u);
+                }
+            }
+    }
+};
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Args a)
+__device__ __forceinline__ void qk_tile(f32x16_t (&S)[2], const uint16_t *Ks, const bf16x8_t (&qf)[D / 16],
+                                        int l32, int hh)
 {
-    constexpr int KS = D + 8;         // K row stride in LDS (bf16): 16-byte aligned, bank-rotating
-    constexpr int VS = kBlockN + 8;   // transposed-V row stride in LDS (bf16)
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlockN * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VS];
+    constexpr int KS = D + 8;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kb][i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Ks[(kb * 32 + l32) * KS + 16 * s + 8 * hh]);
+            S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], S[kb], 0, 0, 0);
+        }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16_t (&acc)[D / 32], const uint16_t *Vt, const bf16x8_t (&pf)[4],
+                                        int l32, int hh)
+{
+    constexpr int VS = kBlockN + 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vt[(db * 32 + l32) * VS + 16 * ks + 8 * hh]);
+            acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], acc[db], 0, 0, 0);
+        }
+}
+
+// probabilities of one tile against reference mb (= m * scale * log2 e), their
+// partial row sum, and the bf16 B operands of the P*V product
+__device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[2], float sl2, float mb, bf16x8_t (&pf)[4])
+{
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(S[kb][i], sl2, -mb));
+            if (i & 1) rs1 += p; else rs0 += p;
+            pf[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
+        }
+    return rs0 + rs1;
+}
+
+template <int D, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
+{
+    constexpr int NT = WAVES * 64;
+    constexpr int BM = WAVES * 32;
+    using St = Stage<D, NT>;
+    constexpr int KBUF = St::KBUF, VBUF = St::VBUF;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * KBUF + 2 * VBUF];
+    uint16_t *const KB0 = smem;
+    uint16_t *const KB1 = smem + KBUF;
+    uint16_t *const VB0 = smem + 2 * KBUF;
+    uint16_t *const VB1 = smem + 2 * KBUF + VBUF;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
 
-    const int nbh = a.B * a.Hq;
-    const int qtile = a.n_qtiles - 1 - (int)(blockIdx.x / nbh);  // longest tiles first
-    const int bh = (int)(blockIdx.x % nbh);
-    const int b = bh / a.Hq, h = bh % a.Hq, hk = h / a.group;
-    const int q0 = qtile * kBlockM;
-    const uint16_t *qp = a.q + (size_t)bh * a.N * D;
-    const uint16_t *kp = a.k + (size_t)(b * a.Hkv + hk) * a.N * D;
-    const uint16_t *vp = a.v + (size_t)(b * a.Hkv + hk) * a.N * D;
+    // ---- work item: XCD-contiguous slices of (b, kv head, zig-zag q tile, q head) ----
+    int item;
+    {
+        const int x = blockIdx.x, xcd = x % kXcds, i = x / kXcds;
+        const int base = a.n_items / kXcds, rem = a.n_items % kXcds;
+        item = xcd * base + min(xcd, rem) + i;
+    }
+    const int j = item % a.group;
+    const int r = (item / a.group) % a.n_qtiles;
+    const int bg = item / (a.group * a.n_qtiles);
+    const int b = bg / a.Hkv, hk = bg % a.Hkv;
+    const int h = hk * a.group + j;
+    const int qtile = (r & 1) ? (r >> 1) : a.n_qtiles - 1 - (r >> 1);
+    const int bh = b * a.Hq + h;
+    const int q0 = qtile * BM;
+    const uint32_t head_bytes = (uint32_t)a.N * D * 2u;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (size_t)bh * a.N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (size_t)(b * a.Hkv + hk) * a.N * D, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (size_t)(b * a.Hkv + hk) * a.N * D, head_bytes);
 
     const int wrow0 = q0 + wave * 32;  // first query row of this wave
     const int qrow = wrow0 + l32;      // the query row this lane owns
 
-    // Q fragments (B operand of S^T = K Q^T), resident for the whole kernel.
+    // Q fragments (B operand of S^T = K Q^T), resident for the whole kernel;
+    // rows past N read as zero.
     bf16x8_t qf[D / 16];
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (qrow < a.N) u = *reinterpret_cast<const uint4 *>(qp + (size_t)qrow * D + 16 * s + 8 * hh);
+        uint4 u = bload16(rq, (uint32_t)(qrow * D + 16 * s + 8 * hh) * 2u, 0);
+        if (a.negate_q) {  // scale < 0: s*scale = (-s)*|scale|, so the max stays on raw scores
+            u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
+        }
         qf[s] = as_bf16x8(u);
     }
 
@@ -97,131 +277,94 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Args a)
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
-    float m = -INFINITY;  // running max of scaled scores, base-2 units
-    float l = 0.f;        // this lane's share of the running sum (its 16-of-32 keys)
+    float m = -INFINITY;  // reference max of raw scores for this lane's row
+    float l = 0.f;        // this lane's share of the running sum (its 16 of every 32 keys)
+    const float sl2 = a.scale_log2;
+    const float slack = kRescaleLog2 / sl2;  // raw-score margin before the max must move
+    const int xlane = (lane ^ 32) << 2;      // ds_bpermute address of the other half-wave
 
-    const int kend = a.causal ? min(a.N, q0 + kBlockM) : a.N;  // keys this tile may see
+    const int kend = a.causal ? min(a.N, q0 + BM) : a.N;  // keys this tile may see
     const int ntiles = (kend + kBlockN - 1) / kBlockN;
 
-    for (int jt = 0; jt < ntiles; ++jt) {
-        const int k0 = jt * kBlockN;
-        __syncthreads();  // the previous tile's LDS reads are done
-        // ---- stage K (row-major) -------------------------------------------
-        {
-            constexpr int CPR = D / 8;            // 16-byte chunks per row
-            constexpr int RPP = kThreads / CPR;   // rows per pass
-            const int c = tid % CPR;
+    // ---- prologue: K(0) and K(1) staged, VB1 zeroed, S(0) formed, V(0) in flight ------
+    St st;
+    st.init(tid);
+    st.load_k(rk, 0, tid);
+    st.store_k(KB0, tid);
+    st.load_k(rk, kBlockN, tid);  // tile 1 (zeros past N); never multiplied in if ntiles == 1
+    st.store_k(KB1, tid);
+    for (int i = tid; i < VBUF / 8; i += NT) reinterpret_cast<uint4 *>(VB1)[i] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+    f32x16_t S0[2], S1[2];
+    qk_tile<D>(S0, KB0, qf, l32, hh);
+    bf16x8_t P0[4], P1[4];
 #pragma unroll
-            for (int r = tid / CPR; r < kBlockN; r += RPP) {
-                uint4 u = make_uint4(0, 0, 0, 0);
-                if (k0 + r < a.N) u = *reinterpret_cast<const uint4 *>(kp + (size_t)(k0 + r) * D + 8 * c);
-                *reinterpret_cast<uint4 *>(&Ks[r * KS + 8 * c]) = u;
-            }
-        }
-        // ---- stage V transposed: Vt[d][key slot] ----------------------------
-        {
-            constexpr int UNITS = (kBlockN / 4) * (D / 8);  // 4 keys x 8 dims each
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int u0 = 0; u0 < UNITS; u0 += kThreads) {
-                const int un = u0 + tid;
-                if (UNITS % kThreads == 0 || un < UNITS) {
-                    const int kg = un % (kBlockN / 4);  // key group (4 keys)
-                    const int dc = un / (kBlockN / 4);  // 8-dim chunk
-                    uint32_t w[4][4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        uint4 x = make_uint4(0, 0, 0, 0);
-                        const int key = k0 + 4 * kg + j;
-                        if (key < a.N) x = *reinterpret_cast<const uint4 *>(vp + (size_t)key * D + 8 * dc);
-                        w[j][0] = x.x; w[j][1] = x.y; w[j][2] = x.z; w[j][3] = x.w;
-                    }
-                    const int pos = 16 * (kg >> 2) + vt_slot(kg & 3);
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        // dims 8*dc+2p (low halves) and 8*dc+2p+1 (high halves)
-                        uint2 lo, hi;
-                        lo.x = (w[0][p] & 0xffffu) | (w[1][p] << 16);
-                        lo.y = (w[2][p] & 0xffffu) | (w[3][p] << 16);
-                        hi.x = (w[0][p] >> 16) | (w[1][p] & 0xffff0000u);
-                        hi.y = (w[2][p] >> 16) | (w[3][p] & 0xffff0000u);
-                        *reinterpret_cast<uint2 *>(&Vt[(8 * dc + 2 * p) * VS + pos]) = lo;
-                        *reinterpret_cast<uint2 *>(&Vt[(8 * dc + 2 * p + 1) * VS + pos]) = hi;
-                    }
-                }
-            }
-        }
-        __syncthreads();
+        for (int e = 0; e < 8; ++e) P1[ks][e] = (__bf16)0.f;  // "tile -1": P = 0 against the zeroed VB1
+    st.load_v(rv, 0, tid);
+    __syncthreads();  // every wave has read KB0 before iteration 0 refills it
 
-        // A wave whose rows all precede this tile's first key (or lie past N) has nothing to add.
-        if ((a.causal && k0 > wrow0 + 31) || wrow0 >= a.N) continue;
-
-        // ---- S^T = K Q^T for two 32-key blocks -----------------------------
-        f32x16_t st[2];
+    // One pipeline step.  Sc = scores of tile t (formed last step), Sn receives
+    // tile t+1; Pp = probabilities of tile t-1, Pc receives tile t's.
+    auto step = [&](f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], bf16x8_t (&Pp)[4], bf16x8_t (&Pc)[4], int t,
+                    const uint16_t *Kn, const uint16_t *Vp, uint16_t *Kw, uint16_t *Vw) {
+        const int k0 = t * kBlockN;
+        if (t + 2 < ntiles) st.load_k(rk, k0 + 2 * kBlockN, tid);  // fetched during this step
+        // diagonal / ragged tile: mask keys past the row (causal) or past N
+        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > a.N) {
+            const int lim = (a.causal ? min(qrow, a.N - 1) : a.N - 1) - (k0 + 4 * hh);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) st[kb][i] = 0.f;
+                for (int i = 0; i < 16; ++i)
+                    if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) Sc[kb][i] = -INFINITY;
         }
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(&Ks[(kb * 32 + l32) * KS + 16 * s + 8 * hh]);
-                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], st[kb], 0, 0, 0);
-            }
-        }
-
-        // ---- scale, mask, online softmax -----------------------------------
-        const bool need_mask = (a.causal && k0 + kBlockN - 1 > wrow0) || (k0 + kBlockN > a.N);
+        // ---- hot block: matrix cores run PV(t-1) and S(t+1) while the ALUs do softmax(t)
+        const float mb = (m == -INFINITY) ? 0.f : m * sl2;
+        pv_tile<D>(acc, Vp, Pp, l32, hh);
+        qk_tile<D>(Sn, Kn, qf, l32, hh);
         float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float x = st[kb][i] * a.scale_log2;
-                if (need_mask) {
-                    const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-                    if (key >= a.N || (a.causal && key > qrow)) x = -INFINITY;
-                }
-                st[kb][i] = x;
-                mx = fmaxf(mx, x);
-            }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, Sc[kb][i]);
+        float rs = softmax_tile(Sc, sl2, mb, Pc);
+        mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
+        // ---- rare: a row's scores passed its reference max by more than 2^8 ------------
+        if (__ballot(mx > m + slack)) {
+            const float m_new = fmaxf(m, mx);
+            const float c = __builtin_amdgcn_exp2f((m - m_new) * sl2);  // 0 while m = -inf
+            l *= c;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[db][i] *= c;
+            m = m_new;
+            rs = softmax_tile(Sc, sl2, (m == -INFINITY) ? 0.f : m * sl2, Pc);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // no visible key yet: state unchanged
-        const float c = __builtin_amdgcn_exp2f(m - m_use);
-        float rs = 0.f;
-        bf16x8_t pf[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(st[kb][i] - m_use);
-                rs += p;
-                pf[2 * kb + (i >> 3)][i & 7] = (__bf16)p;
-            }
-        }
-        l = l * c + rs;
-        m = m_new;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[db][i] *= c;
+        l += rs;
+        // ---- stage K(t+2) and V(t) for the next step ------------------------------------
+        if (t + 2 < ntiles) st.store_k(Kw, tid);
+        st.store_v(Vw, tid);
+        if (t + 1 < ntiles) st.load_v(rv, k0 + kBlockN, tid);
+        __syncthreads();
+    };
 
-        // ---- O^T += V^T P^T -------------------------------------------------
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-                const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vt[(db * 32 + l32) * VS + 16 * ks + 8 * hh]);
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], acc[db], 0, 0, 0);
-            }
-        }
+    // iteration t reads K(t+1) from KB[(t+1)&1] and V(t-1) from VB[(t-1)&1];
+    // it writes K(t+2) into KB[t&1] and V(t) into VB[t&1]
+    for (int t = 0; t < ntiles; t += 2) {
+        step(S0, S1, P1, P0, t, KB1, VB1, KB0, VB0);
+        if (t + 1 < ntiles) step(S1, S0, P0, P1, t + 1, KB0, VB0, KB1, VB1);
     }
+    // last product: P of tile ntiles-1 is in P0 (ntiles odd) or P1 (even), V in VB[(ntiles-1)&1]
+    if (ntiles & 1)
+        pv_tile<D>(acc, VB0, P0, l32, hh);
+    else
+        pv_tile<D>(acc, VB1, P1, l32, hh);
 
-    // ---- epilogue: O = acc / l, LSE = (m + log2 l) * ln 2 ----------------------
-    const float lt = l + __shfl_xor(l, 32);
+    // ---- epilogue: O = acc / l, LSE = m * scale + ln l ---------------------------------
+    const float lt = l + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, l)));
     if (qrow < a.N) {
         const float inv = 1.f / lt;
         uint16_t *orow = a.o + ((size_t)bh * a.N + qrow) * D;
@@ -240,14 +383,27 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(Args a)
                 *reinterpret_cast<uint2 *>(orow + d0) = pk;
             }
         }
-        if (hh == 0) a.lse[(size_t)bh * a.N + qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+        if (hh == 0) a.lse[(size_t)bh * a.N + qrow] = m * a.scale + log2f(lt) * kLn2;
     }
 }
+
+template <int D, int WAVES>
+hipError_t launch(const Args &a, hipStream_t stream)
+{
+    hipLaunchKernelGGL((prefill_bf16_kernel<D, WAVES>), dim3((unsigned)a.n_items), dim3(WAVES * 64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+#ifndef ATTN_PREFILL_WAVES
+#define ATTN_PREFILL_WAVES 8
+#endif
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
 {
+    constexpr int W = ATTN_PREFILL_WAVES;
     Args a;
     a.q = static_cast<const uint16_t *>(p.q);
     a.k = static_cast<const uint16_t *>(p.k);
@@ -256,17 +412,19 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     a.lse = p.lse;
     a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.group = p.Hq / p.Hkv;
     a.causal = p.causal;
-    a.n_qtiles = (p.N + kBlockM - 1) / kBlockM;
-    a.scale_log2 = p.scale * kLog2e;
-    const long long nblk = (long long)a.n_qtiles * p.B * p.Hq;
-    if (nblk == 0) return hipSuccess;
-    if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)nblk), block(kThreads);
-    if (p.head_dim == 128)
-        hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, stream, a);
-    else
-        hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, stream, a);
-    return hipGetLastError();
+    a.n_qtiles = (p.N + W * 32 - 1) / (W * 32);
+    a.negate_q = p.scale < 0.f ? 1 : 0;
+    // |scale| below 1e-30 is raised to 1e-30: every probability still rounds to
+    // exactly 1 (the scale-0 result), and the reference max stays finite.
+    a.scale = fmaxf(fabsf(p.scale), 1e-30f);
+    a.scale_log2 = a.scale * kLog2e;
+    const long long items = (long long)a.n_qtiles * p.B * p.Hq;
+    if (items == 0) return hipSuccess;
+    if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+    // per-head byte offsets, including the padded last query tile, must fit 32 bits
+    if ((long long)(a.n_qtiles * W * 32) * p.head_dim * 2 > 0xffffffffLL) return hipErrorInvalidValue;
+    a.n_items = (int)items;
+    return p.head_dim == 128 ? launch<128, W>(a, stream) : launch<64, W>(a, stream);
 }
 
 }  // namespace attn

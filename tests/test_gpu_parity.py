@@ -215,3 +215,15 @@ def test_decode_empty_sequence(attn):
     assert (o[2] == 0).all() and torch.isneginf(lse[2]).all()
     ro, rl = oracle_decode(x)
     check("decode empty", o, lse, ro, rl, BF16_TOL)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 2.0])
+@pytest.mark.parametrize("dtype", [W.BF16, W.F32])
+def test_prefill_unusual_scales(attn, scale, dtype):
+    """Negative scale (the kernel negates Q instead), zero scale (uniform weights) and a
+    large scale (peaky rows)."""
+    say("case: prefill scale=%g dtype=%s" % (scale, dtype))
+    x = W.prefill_inputs(8, 1, 4, 2, 333, 128, dtype, scale=scale)
+    o, lse = run_prefill(attn, x)
+    ro, rl = oracle.prefill(x.q, x.k, x.v, True, scale)
+    check("scale=%g" % scale, o, lse, ro, rl, BF16_TOL if dtype == W.BF16 else F32_TOL)
