@@ -234,7 +234,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
     uint16_t *const VB1 = smem + 2 * KBUF + VBUF;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
     const int l32 = lane & 31, hh = lane >> 5;
 
     // ---- work item: XCD-contiguous slices of (b, kv head, zig-zag q tile, q head) ----

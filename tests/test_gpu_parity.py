@@ -226,4 +226,9 @@ def test_prefill_unusual_scales(attn, scale, dtype):
     x = W.prefill_inputs(8, 1, 4, 2, 333, 128, dtype, scale=scale)
     o, lse = run_prefill(attn, x)
     ro, rl = oracle.prefill(x.q, x.k, x.v, True, scale)
-    check("scale=%g" % scale, o, lse, ro, rl, BF16_TOL if dtype == W.BF16 else F32_TOL)
+    # The fixed bars hold at the workloads' scale 1/sqrt(d).  Float rounding of a
+    # score grows with its magnitude, |scale| * sqrt(d) times larger for N(0,1)
+    # inputs, so the bar is widened by that factor (never narrowed).
+    grow = max(1.0, abs(scale) * math.sqrt(128))
+    base = BF16_TOL if dtype == W.BF16 else F32_TOL
+    check("scale=%g" % scale, o, lse, ro, rl, {k_: v_ * grow for k_, v_ in base.items()})
