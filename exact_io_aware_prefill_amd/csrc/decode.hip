@@ -12,20 +12,31 @@
 // Lambda) o_k.
 //
 // gfx950 mapping of the split kernel
-//   * 8 waves per workgroup; each wave walks 32-token steps of the chunk with its
-//     own online-softmax state, and the eight states are merged through LDS at
-//     the end (the same combine rule, inside the workgroup).
-//   * Scores use v_mfma_f32_16x16x32_bf16 on S^T = K Q^T: the A operand is read
-//     straight from the cache (lane = token, 16 bytes of its row), the B operand
-//     holds the group's query rows (padded to 16 with zeros) for the whole
-//     kernel.  A lane of the accumulator then owns one query head and four
-//     tokens, so the softmax is in-register plus two half-wave exchanges.
+//   * 8 waves per workgroup; wave w takes 32-token steps w, w+8, ... of the
+//     chunk with its own online-softmax state; the eight states are merged
+//     through LDS at the end (the same combine rule, inside the workgroup).
+//   * A step is two 16-token blocks.  A block never crosses a page (pages hold
+//     a multiple of 16 tokens), so each block is addressed through one scalar
+//     buffer descriptor: one block-table lookup per 16 tokens, and tokens past
+//     the sequence get an out-of-range offset and read as zero.
+//   * Scores use v_mfma_f32_16x16x32_bf16 on S^T = K Q^T: the A operand is
+//     loaded straight into registers (lane = token, 16 bytes of its row), the
+//     B operand holds the group's query rows (padded to 16 with zeros) for the
+//     whole kernel.  A lane of the accumulator owns one query head and four
+//     tokens, so the softmax is in-register plus two cross-lane exchanges.
 //   * The output is accumulated as O^T += V^T P^T on the same instruction; the
-//     score accumulator (rounded to bf16) is the B operand as it stands, and V
-//     is transposed through a wave-private LDS slab in the matching token order.
-//   * The next step's key/value loads are issued before the current step is
-//     computed (two register buffers), so a workgroup keeps its whole chunk in
-//     flight for the chunk sizes used at batch 1.
+//     score accumulator (rounded to bf16) is the B operand as it stands.  V
+//     rows are loaded coalesced (16 lanes per 256-byte row), stored unchanged
+//     into a wave-private LDS slab, and the V^T operand is read back with the
+//     LDS transpose read ds_read_b64_tr_b16 (in each 16-lane group, lane 4r+q
+//     reads 4 dims of token row r and lane j receives dim j of the 4 rows), so
+//     no VALU work is spent on the transpose.  16-byte chunk c of slab row r
+//     sits at slot c ^ 2(r & 7) (D = 128; c ^ 2((r >> 1) & 3) for D = 64),
+//     which makes both the row stores and the transpose reads bank-conflict
+//     free on the 64-bank LDS.
+//   * Each wave keeps two steps in flight (two register sets), so a workgroup
+//     has 512 tokens of keys and values in flight: a whole 512-token chunk is
+//     requested at once.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -35,107 +46,192 @@ namespace attn {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kStep = 32;          // tokens per wave step (two 16-token score blocks)
-constexpr int kVS = kStep + 8;     // transposed-V row stride in LDS (bf16 elements)
+constexpr int kStep = 32;  // tokens per wave step (two 16-token blocks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;  // per-lane offset that reads as zero
 
 struct SplitArgs {
     const uint16_t *q, *k, *v;
     const int32_t *bt, *seq_lens;
     float *o_parts, *lse_parts;
     int Hq, Hkv, group, page, max_blocks, chunk, max_chunks;
-    long long seq_tokens;  // contiguous layout: tokens per sequence
+    long long seq_tokens;  // tokens per sequence of the contiguous layout (= capacity)
     float scale_log2;
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// Element offset of token t's row for KV head 0 (add hk * D).  `t` is a
-// multiple-of-4 group or block start plus an in-page offset; pages hold a
-// multiple of 16 tokens, so any 16-aligned block stays inside one page.
-__device__ __forceinline__ size_t row_of(const SplitArgs &a, int b, int t)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, (int)bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Index of token t of sequence b in units of one token's rows (all KV heads):
+// paged: slot t % page of page block_table[b][t / page]; contiguous: b*capacity + t.
+__device__ __forceinline__ long long token_index(const SplitArgs &a, int b, int t)
 {
     if (a.bt) {
         const int page = a.bt[(size_t)b * a.max_blocks + t / a.page];
-        return ((size_t)page * a.page + (size_t)(t % a.page)) * a.Hkv;
+        return (long long)page * a.page + (t % a.page);
     }
-    return ((size_t)b * a.seq_tokens + (size_t)t) * a.Hkv;
+    return (long long)b * a.seq_tokens + t;
+}
+
+// slot permutation of the V slab rows (see the header comment)
+template <int D>
+__device__ __forceinline__ int slab_swz(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+
+template <int D>
+struct Geo {
+    static constexpr int RB = D * 2;          // bytes of one token row of one head
+    static constexpr int NC = D / 8;          // 16-byte chunks per row
+    static constexpr int RPI = 64 / NC;       // V rows covered by one load instruction
+    static constexpr int VI = kStep / RPI;    // V load instructions per step
+    static constexpr int VIB = VI / 2;        // ... per 16-token block
+    static constexpr int SLAB = kStep * RB;   // bytes of one wave's slab
+};
+
+// Registers of one step: K as score A operands [block][k-step], V rows as loaded.
+template <int D>
+struct StepRegs {
+    uint4 k[2][D / 32];
+    uint4 v[Geo<D>::VI];
+};
+
+// Per-lane constants of the loads.
+struct LaneOffsets {
+    uint32_t k;  // K: token l16 of a block, bytes 16G.. of each 64-byte piece
+    uint32_t v;  // V: token vtok of a load's rows, chunk vchunk
+    int l16, vtok;
+};
+
+template <int D>
+__device__ __forceinline__ void issue_step(const SplitArgs &a, StepRegs<D> &s, const char *kbase,
+                                           const char *vbase, int b, int tb, int t_end, uint32_t rstride,
+                                           const LaneOffsets &lo)
+{
+    using Gm = Geo<D>;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+        const int t0 = tb + 16 * blk;
+        const bool live = t0 < t_end;  // uniform; a dead block reads nothing and loads no table entry
+        const long long row0 = live ? token_index(a, b, t0) * a.Hkv : 0;
+        const uint32_t nrec = live ? 16u * rstride : 0u;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0 * Gm::RB, nrec);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0 * Gm::RB, nrec);
+        const uint32_t ko = (t0 + lo.l16 < t_end) ? lo.k : kOutOfRange;
+#pragma unroll
+        for (int st = 0; st < D / 32; ++st) s.k[blk][st] = bload16(rk, ko + 64u * st, 0);
+#pragma unroll
+        for (int i = 0; i < Gm::VIB; ++i) {
+            const int tok = Gm::RPI * i + lo.vtok;  // token within the block
+            const uint32_t vo = (t0 + tok < t_end) ? lo.v : kOutOfRange;
+            s.v[Gm::VIB * blk + i] = bload16(rv, vo, (uint32_t)(Gm::RPI * i) * rstride);
+        }
+    }
 }
 
 template <int D>
-struct StepRegs {
-    uint4 k[2][D / 32];                    // score A operands: [block][k-step]
-    uint4 v[(kStep / 4) * (D / 8) / 64][4]; // V units: [unit][token within group]
-};
-
-// Slot of 4-token group tg inside a transposed-V row: lane group G reads
-// positions 8G..8G+7 = tokens {4G..4G+3} of block 0 then {16+4G..} of block 1.
-__device__ __forceinline__ int vt_pos(int tg) { return (tg < 4) ? 8 * tg : 8 * (tg - 4) + 4; }
-
-template <int D>
-__device__ __forceinline__ void load_step(const SplitArgs &a, StepRegs<D> &r, int b, int hk, int tb,
-                                          int t_end, int lane)
+__device__ __forceinline__ void consume_step(const StepRegs<D> &s, char *slab, const bf16x8_t *qf, f32x4_t *acc,
+                                             float &m, float &l, int tb, int t_end, float scale_log2, int G,
+                                             const uint32_t *vstore, uint32_t vread)
 {
-    const int l16 = lane & 15, G = lane >> 4;
-    // one block-table lookup per 16-token block (a block never crosses a page);
-    // blocks starting at or past t_end are never dereferenced
-    size_t rb[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) rb[blk] = (tb + 16 * blk < t_end) ? row_of(a, b, tb + 16 * blk) + hk : 0;
+    using Gm = Geo<D>;
+    // scores of the two 16-token blocks
+    f32x4_t st[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-        const int t = tb + 16 * blk + l16;
-        if (t < t_end) {
-            const uint16_t *row = a.k + (rb[blk] + (size_t)l16 * a.Hkv) * D;
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) r.k[blk][s] = *reinterpret_cast<const uint4 *>(row + 32 * s + 8 * G);
-        } else {
+        for (int i = 0; i < 4; ++i) st[blk][i] = 0.f;
 #pragma unroll
-            for (int s = 0; s < D / 32; ++s) r.k[blk][s] = make_uint4(0, 0, 0, 0);
-        }
+        for (int ks = 0; ks < D / 32; ++ks)
+            st[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s.k[blk][ks]), qf[ks], st[blk], 0, 0, 0);
     }
-    constexpr int UPL = (kStep / 4) * (D / 8) / 64;  // V units per lane
+    // V rows into the wave's slab.  LDS executes one wave's accesses in order, so
+    // these stores land after the previous step's transpose reads of the slab.
 #pragma unroll
-    for (int u = 0; u < UPL; ++u) {
-        const int un = lane + 64 * u;
-        const int tg = un & 7, dc = un >> 3;
-        const int blk = tg >> 2;
+    for (int i = 0; i < Gm::VI; ++i)
+        *reinterpret_cast<uint4 *>(slab + vstore[i % 2] + (i & ~1) * Gm::RPI * Gm::RB) = s.v[i];
+
+    // online softmax over this step (lane: query l16, tokens 4G+i of each block)
+    const bool tail = tb + kStep > t_end;
+    float x[8];
+    float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int o = 4 * (tg & 3) + j;  // offset inside the 16-token block
-            if (tb + 16 * blk + o < t_end)
-                r.v[u][j] = *reinterpret_cast<const uint4 *>(a.v + (rb[blk] + (size_t)o * a.Hkv) * D + 8 * dc);
-            else
-                r.v[u][j] = make_uint4(0, 0, 0, 0);
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float xv = st[blk][i] * scale_log2;
+            if (tail && tb + 16 * blk + 4 * G + i >= t_end) xv = -INFINITY;
+            x[4 * blk + i] = xv;
+            mx = fmaxf(mx, xv);
         }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);  // finite: the step's first token is in the sequence
+    const float c = __builtin_amdgcn_exp2f(m - m_new);
+    float rs = 0.f;
+    bf16x8_t pf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(x[j] - m_new);
+        rs += p;
+        pf[j] = (__bf16)p;
+    }
+    l = l * c + rs;
+    m = m_new;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[nb][i] *= c;
+
+    // O^T += V^T P^T; P's k index 8G+j is token 4G+j (j < 4) or 16+4G+(j-4)
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+        const char *p = slab + (vread ^ (32u * nb));
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)p);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(p + 16 * Gm::RB));
+        const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[nb], 0, 0, 0);
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
 {
-    constexpr int VT_BYTES = kWaves * D * kVS * 2;
-    constexpr int CMB_BYTES = kWaves * 16 * (D + 2) * 4;
-    constexpr int LDS_BYTES = VT_BYTES > CMB_BYTES ? VT_BYTES : CMB_BYTES;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+    using Gm = Geo<D>;
+    // one slab per wave; reused at the end for the eight waves' [16][D] float outputs
+    static_assert(Gm::SLAB == 16 * D * 4, "slab must hold a wave's 16 x D float output");
+    __shared__ __attribute__((aligned(1024))) char slabs[kWaves * Gm::SLAB];
+    __shared__ float ml[2][kWaves][16];
 
     const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     // lengths outside [0, capacity] are clamped so no read leaves the sequence's cache
-    const int L = max(0, (int)min((long long)a.seq_lens[b], a.seq_tokens));
+    const int L = (int)max(0LL, min((long long)a.seq_lens[b], a.seq_tokens));
     const int t_begin = chunk * a.chunk;
     if (t_begin >= L) return;  // whole workgroup exits together: this chunk is empty
     const int t_end = min(t_begin + a.chunk, L);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, G = lane >> 4;
     const int g = a.group;
+    const uint32_t rstride = (uint32_t)a.Hkv * Gm::RB;  // bytes between consecutive tokens of one head
 
-    // Query fragments (B operand of S^T = K Q^T); rows >= g are zero padding.
+    // query fragments (B operand of S^T = K Q^T); rows >= g are zero padding
     bf16x8_t qf[D / 32];
     {
         const uint16_t *qrow = a.q + ((size_t)b * a.Hq + (size_t)hk * g + l16) * D;
@@ -147,6 +243,31 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
         }
     }
 
+    LaneOffsets lo;
+    lo.l16 = l16;
+    lo.vtok = lane / Gm::NC;
+    const int vchunk = lane % Gm::NC;
+    lo.k = (uint32_t)l16 * rstride + 16u * G;
+    lo.v = (uint32_t)lo.vtok * rstride + 16u * vchunk;
+    char *slab = slabs + wave * Gm::SLAB;
+    // slab byte offsets of this lane's V row stores for even and odd load
+    // instructions (instruction i covers rows i*RPI..; the slot permutation
+    // repeats every 8 rows, i.e. every two instructions for D = 128)
+    uint32_t vstore[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+        const int r = Gm::RPI * par + lo.vtok;
+        vstore[par] = (uint32_t)(r * Gm::RB + 16 * (vchunk ^ slab_swz<D>(r)));
+    }
+    // transpose reads: group G, lane 4r+q reads 8 bytes of slab row 4G+r, dims
+    // 16nb + 4q..4q+3; the slot permutation only touches bits 5+ of the offset,
+    // so d-block nb is a XOR by 32nb
+    const int vrow = 4 * G + (l16 >> 2), vq = l16 & 3;
+    const uint32_t vread = (uint32_t)(vrow * Gm::RB + 16 * ((vq >> 1) ^ slab_swz<D>(vrow)) + 8 * (vq & 1));
+
+    const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)hk * Gm::RB;
+    const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)hk * Gm::RB;
+
     f32x4_t acc[D / 16];
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb)
@@ -154,142 +275,68 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
         for (int i = 0; i < 4; ++i) acc[nb][i] = 0.f;
     float m = -INFINITY, l = 0.f;
 
-    uint16_t *vt = reinterpret_cast<uint16_t *>(lds) + wave * D * kVS;  // this wave's slab
-
-    auto compute_step = [&](const StepRegs<D> &r, int tb) {
-        // scores for two 16-token blocks
-        f32x4_t st[2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) st[blk][i] = 0.f;
-#pragma unroll
-            for (int s = 0; s < D / 32; ++s)
-                st[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(r.k[blk][s]), qf[s], st[blk], 0, 0, 0);
-        }
-        // transpose V into the slab while the scores are in flight
-        constexpr int UPL = (kStep / 4) * (D / 8) / 64;
-#pragma unroll
-        for (int u = 0; u < UPL; ++u) {
-            const int un = lane + 64 * u;
-            const int tg = un & 7, dc = un >> 3;
-            const int pos = vt_pos(tg);
-            const uint32_t w[4][4] = {{r.v[u][0].x, r.v[u][0].y, r.v[u][0].z, r.v[u][0].w},
-                                      {r.v[u][1].x, r.v[u][1].y, r.v[u][1].z, r.v[u][1].w},
-                                      {r.v[u][2].x, r.v[u][2].y, r.v[u][2].z, r.v[u][2].w},
-                                      {r.v[u][3].x, r.v[u][3].y, r.v[u][3].z, r.v[u][3].w}};
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                uint2 lo, hi;
-                lo.x = (w[0][p] & 0xffffu) | (w[1][p] << 16);
-                lo.y = (w[2][p] & 0xffffu) | (w[3][p] << 16);
-                hi.x = (w[0][p] >> 16) | (w[1][p] & 0xffff0000u);
-                hi.y = (w[2][p] >> 16) | (w[3][p] & 0xffff0000u);
-                *reinterpret_cast<uint2 *>(&vt[(8 * dc + 2 * p) * kVS + pos]) = lo;
-                *reinterpret_cast<uint2 *>(&vt[(8 * dc + 2 * p + 1) * kVS + pos]) = hi;
-            }
-        }
-        // online softmax over this step (lane: query l16, tokens 4G+i of each block)
-        const bool tail = tb + kStep > t_end;
-        float x[8];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float xv = st[blk][i] * a.scale_log2;
-                if (tail && tb + 16 * blk + 4 * G + i >= t_end) xv = -INFINITY;
-                x[4 * blk + i] = xv;
-                mx = fmaxf(mx, xv);
-            }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float c = __builtin_amdgcn_exp2f(m - m_use);
-        float rs = 0.f;
-        bf16x8_t pf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float p = __builtin_amdgcn_exp2f(x[j] - m_use);
-            rs += p;
-            pf[j] = (__bf16)p;
-        }
-        l = l * c + rs;
-        m = m_new;
-#pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[nb][i] *= c;
-        // the slab writes of all lanes must land before any lane reads them
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) {
-            const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&vt[(16 * nb + l16) * kVS + 8 * G]);
-            acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc[nb], 0, 0, 0);
-        }
-        // the next step may overwrite the slab only after every lane has read it
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-
-    // two register buffers: the next step's loads are in flight during this step's math
+    // This wave's steps start at t_begin + (wave + 8j) * 32, two in flight.  Loads
+    // are issued unconditionally (a step past the chunk has empty descriptors and
+    // reads nothing), so the number of loads in flight is the same on every path
+    // and each step waits only for its own loads.
     const int stride = kWaves * kStep;
     int tb = t_begin + wave * kStep;
     StepRegs<D> r0, r1;
-    if (tb < t_end) load_step<D>(a, r0, b, hk, tb, t_end, lane);
+    issue_step<D>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
     while (tb < t_end) {
-        int tn = tb + stride;
-        if (tn < t_end) load_step<D>(a, r1, b, hk, tn, t_end, lane);
-        compute_step(r0, tb);
-        tb = tn;
+        issue_step<D>(a, r1, kbase, vbase, b, tb + stride, t_end, rstride, lo);
+        consume_step<D>(r0, slab, qf, acc, m, l, tb, t_end, a.scale_log2, G, vstore, vread);
+        tb += stride;
         if (tb >= t_end) break;
-        tn = tb + stride;
-        if (tn < t_end) load_step<D>(a, r0, b, hk, tn, t_end, lane);
-        compute_step(r1, tb);
-        tb = tn;
+        issue_step<D>(a, r0, kbase, vbase, b, tb + stride, t_end, rstride, lo);
+        consume_step<D>(r1, slab, qf, acc, m, l, tb, t_end, a.scale_log2, G, vstore, vread);
+        tb += stride;
     }
 
     // ---- merge the eight wave states (combine rule) ------------------------------
+    // row sum of query l16 over the four token groups of the lane's column
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
-    __syncthreads();  // every wave is done with its slab
-    float *wm = reinterpret_cast<float *>(lds);  // [kWaves][16]
-    float *wl = wm + kWaves * 16;                // [kWaves][16]
-    float *wo = wl + kWaves * 16;                // [kWaves][16][D]
     if (G == 0) {
-        wm[wave * 16 + l16] = m;
-        wl[wave * 16 + l16] = lt;
+        ml[0][wave][l16] = m;  // -inf for a wave that saw no token
+        ml[1][wave][l16] = lt;
     }
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb)
-        *reinterpret_cast<f32x4_t *>(&wo[(wave * 16 + l16) * D + 16 * nb + 4 * G]) = acc[nb];
     __syncthreads();
-    for (int idx = tid; idx < g * D; idx += kThreads) {
-        const int n = idx / D, d = idx % D;
-        float ms = -INFINITY;
+    float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, wm[w * 16 + n]);
-        float lsum = 0.f, osum = 0.f;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[0][w][l16]);
+    float Lsum = 0.f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float e = __builtin_amdgcn_exp2f(wm[w * 16 + n] - ms);  // 0 for a wave that saw no token
-            lsum += e * wl[w * 16 + n];
-            osum += e * wo[(w * 16 + n) * D + d];
-        }
-        const size_t row = (size_t)b * a.Hq + (size_t)hk * g + n;
-        a.o_parts[(row * a.max_chunks + chunk) * D + d] = osum / lsum;
-        if (d == 0) a.lse_parts[row * a.max_chunks + chunk] = (ms + log2f(lsum)) * kLn2;
+    for (int w = 0; w < kWaves; ++w) Lsum += __builtin_amdgcn_exp2f(ml[0][w][l16] - M) * ml[1][w][l16];
+    const float sc = __builtin_amdgcn_exp2f(m - M);
+    // the wave's slab now holds its rescaled output as [query][D] floats
+    float *wo = reinterpret_cast<float *>(slab);
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) *reinterpret_cast<f32x4_t *>(&wo[l16 * D + 16 * nb + 4 * G]) = acc[nb] * sc;
+    __syncthreads();
+    // wave w sums d-block w over the eight waves and writes the chunk's partial
+    if (wave < D / 16 && l16 < g) {
+        f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            sum += *reinterpret_cast<const f32x4_t *>(
+                reinterpret_cast<const float *>(slabs + w * Gm::SLAB) + l16 * D + 16 * wave + 4 * G);
+        const size_t row = (size_t)b * a.Hq + (size_t)hk * g + l16;
+        const float inv = 1.f / Lsum;  // Lsum >= 1: the row's largest term is exp2(0)
+        *reinterpret_cast<f32x4_t *>(&a.o_parts[(row * a.max_chunks + chunk) * D + 16 * wave + 4 * G]) = sum * inv;
+        if (wave == 0 && G == 0) a.lse_parts[row * a.max_chunks + chunk] = (M + log2f(Lsum)) * kLn2;
     }
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one workgroup per row (sequence x query head).
+// Combine: one workgroup of 256 threads per row (sequence x query head).  Thread
+// (sg, c) accumulates float4 column c over splits sg, sg + SG, ...; the first
+// batch of partial loads is issued before the row's Lambda is reduced, so the
+// whole row is requested at once for up to 8*SG splits.  Each wave reduces the
+// row's log-sum-exps itself (no barrier); the SG partial sums meet in LDS.
 // ---------------------------------------------------------------------------
+constexpr int kCombineThreads = 256;
+
 struct CombineArgs {
     const float *o_parts, *lse_parts;
     const int32_t *n_splits;  // explicit per-row split counts, or NULL
@@ -299,8 +346,6 @@ struct CombineArgs {
     int o_bf16;
     float *lse;
 };
-
-constexpr int kCombineThreads = 256;
 
 __device__ __forceinline__ float wave_max(float x)
 {
@@ -318,14 +363,14 @@ __device__ __forceinline__ float wave_sum(float x)
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArgs a)
 {
-    constexpr int NWV = kCombineThreads / 64;
-    constexpr int DPL = D / 64;  // output dims per lane
-    __shared__ float red[NWV];
-    __shared__ float red2[NWV];
-    __shared__ float obuf[NWV][D];
+    constexpr int C4 = D / 4;                    // float4 columns of a row
+    constexpr int SG = kCombineThreads / C4;     // split groups
+    constexpr int U = 8;                         // splits per thread per batch
+    __shared__ f32x4_t red[SG][C4];
 
     const size_t row = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int col = tid % C4, sg = tid / C4;
     int ns;
     if (a.seq_lens) {
         const int L = max(0, min(a.seq_lens[row / a.Hq], a.capacity));
@@ -337,52 +382,75 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
     }
     ns = max(0, min(ns, a.max_splits));
     const float *lam = a.lse_parts + row * a.max_splits;
-    const float *op = a.o_parts + row * a.max_splits * D;
+    const f32x4_t *op = reinterpret_cast<const f32x4_t *>(a.o_parts + row * a.max_splits * D) + col;
 
-    float mx = -INFINITY;
-    for (int kx = tid; kx < ns; kx += kCombineThreads) mx = fmaxf(mx, lam[kx]);
-    mx = wave_max(mx);
-    if (lane == 0) red[wave] = mx;
-    __syncthreads();
-    mx = red[0];
+    // first batch of partials, in flight while Lambda is reduced
+    f32x4_t v[U];
+    float lk[U];
 #pragma unroll
-    for (int w = 1; w < NWV; ++w) mx = fmaxf(mx, red[w]);
-
-    float z = 0.f;
-    if (mx != -INFINITY)
-        for (int kx = tid; kx < ns; kx += kCombineThreads) z += expf(lam[kx] - mx);
-    z = wave_sum(z);
-    if (lane == 0) red2[wave] = z;
-    __syncthreads();
-    z = 0.f;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) z += red2[w];
-    const bool empty = (mx == -INFINITY);
-    const float Lam = empty ? -INFINITY : mx + logf(z);
-
-    float accv[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) accv[e] = 0.f;
-    if (!empty) {
-        for (int kx = wave; kx < ns; kx += NWV) {
-            const float wk = expf(lam[kx] - Lam);
-            const float *src = op + (size_t)kx * D + lane * DPL;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) accv[e] = fmaf(wk, src[e], accv[e]);
+    for (int u = 0; u < U; ++u) {
+        const int k = sg + SG * u;
+        if (k < ns) {
+            v[u] = op[(size_t)k * C4];
+            lk[u] = lam[k];
+        } else {
+            v[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            lk[u] = -INFINITY;
         }
     }
+    // Lambda = mx + ln sum_k exp(lambda_k - mx)
+    float mx = -INFINITY;
+    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, lam[k]);
+    mx = wave_max(mx);
+    const bool empty = (mx == -INFINITY);
+    float z = 0.f;
+    if (!empty)
+        for (int k = lane; k < ns; k += 64) z += expf(lam[k] - mx);
+    z = wave_sum(z);
+    const float Lam = empty ? -INFINITY : mx + logf(z);
+
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (!empty) {
+        // a split with lambda = -inf has weight 0 and contributes nothing
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) obuf[wave][lane * DPL + e] = accv[e];
+        for (int u = 0; u < U; ++u) {
+            const float w = expf(lk[u] - Lam);
+            if (w != 0.f) acc += w * v[u];
+        }
+        for (int k0 = sg + SG * U; k0 < ns; k0 += SG * U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + SG * u;
+                if (k < ns) {
+                    v[u] = op[(size_t)k * C4];
+                    lk[u] = lam[k];
+                } else {
+                    lk[u] = -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float w = expf(lk[u] - Lam);
+                if (w != 0.f) acc += w * v[u];
+            }
+        }
+    }
+    red[sg][col] = acc;
     __syncthreads();
-    if (tid < D) {
-        float s = 0.f;
+    if (sg == 0) {
+        f32x4_t sum = red[0][col];
 #pragma unroll
-        for (int w = 0; w < NWV; ++w) s += obuf[w][tid];
+        for (int s = 1; s < SG; ++s) sum += red[s][col];
         if (a.o_bf16) {
-            const __bf16 r = (__bf16)s;
-            static_cast<uint16_t *>(a.o)[row * D + tid] = __builtin_bit_cast(uint16_t, r);
+            uint16_t h[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = __builtin_bit_cast(uint16_t, (__bf16)sum[e]);
+            uint2 packed;
+            packed.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+            packed.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+            reinterpret_cast<uint2 *>(a.o)[row * C4 + col] = packed;
         } else {
-            static_cast<float *>(a.o)[row * D + tid] = s;
+            reinterpret_cast<f32x4_t *>(a.o)[row * C4 + col] = sum;
         }
     }
     if (tid == 0 && a.lse) a.lse[row] = Lam;
@@ -409,9 +477,13 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     a.seq_lens = p.seq_lens;
     a.o_parts = p.o_parts;
     a.lse_parts = p.lse_parts;
-    a.Hq = p.Hq; a.Hkv = p.Hkv; a.group = p.Hq / p.Hkv;
-    a.page = p.page_size; a.max_blocks = p.max_blocks;
-    a.chunk = p.chunk; a.max_chunks = p.max_chunks;
+    a.Hq = p.Hq;
+    a.Hkv = p.Hkv;
+    a.group = p.Hq / p.Hkv;
+    a.page = p.page_size;
+    a.max_blocks = p.max_blocks;
+    a.chunk = p.chunk;
+    a.max_chunks = p.max_chunks;
     a.seq_tokens = (long long)p.max_blocks * p.page_size;
     a.scale_log2 = p.scale * kLog2e;
     const dim3 grid((unsigned)p.max_chunks, (unsigned)p.Hkv, (unsigned)p.B);
@@ -423,11 +495,17 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     if (e != hipSuccess) return e;
 
     CombineArgs c;
-    c.o_parts = p.o_parts; c.lse_parts = p.lse_parts;
-    c.n_splits = nullptr; c.seq_lens = p.seq_lens;
-    c.Hq = p.Hq; c.chunk = p.chunk; c.max_splits = p.max_chunks;
+    c.o_parts = p.o_parts;
+    c.lse_parts = p.lse_parts;
+    c.n_splits = nullptr;
+    c.seq_lens = p.seq_lens;
+    c.Hq = p.Hq;
+    c.chunk = p.chunk;
+    c.max_splits = p.max_chunks;
     c.capacity = p.max_blocks * p.page_size;
-    c.o = p.o; c.o_bf16 = 1; c.lse = p.lse;
+    c.o = p.o;
+    c.o_bf16 = 1;
+    c.lse = p.lse;
     const int rows = p.B * p.Hq;
     return p.head_dim == 128 ? launch_combine<128>(c, rows, stream) : launch_combine<64>(c, rows, stream);
 }
@@ -435,10 +513,17 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
 hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream)
 {
     CombineArgs c;
-    c.o_parts = p.o_parts; c.lse_parts = p.lse_parts;
-    c.n_splits = p.n_splits; c.seq_lens = nullptr;
-    c.Hq = 1; c.chunk = 1; c.max_splits = p.max_splits; c.capacity = 0;
-    c.o = p.o; c.o_bf16 = p.o_bf16 ? 1 : 0; c.lse = p.lse;
+    c.o_parts = p.o_parts;
+    c.lse_parts = p.lse_parts;
+    c.n_splits = p.n_splits;
+    c.seq_lens = nullptr;
+    c.Hq = 1;
+    c.chunk = 1;
+    c.max_splits = p.max_splits;
+    c.capacity = 0;
+    c.o = p.o;
+    c.o_bf16 = p.o_bf16 ? 1 : 0;
+    c.lse = p.lse;
     return p.head_dim == 128 ? launch_combine<128>(c, p.rows, stream) : launch_combine<64>(c, p.rows, stream);
 }
 
