@@ -140,7 +140,9 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
         return ATTN_ERR_ALIGN;
     const long long cap = (long long)max_blocks_per_seq * page_size;
     const long long max_chunks = (cap + chunk - 1) / chunk;
-    if (max_chunks > INT_MAX || n_kv_heads > 65535 || batch > 65535) return ATTN_ERR_UNSUPPORTED;
+    if (max_chunks > attn::kMaxSplits || max_chunks * n_kv_heads > attn::kMaxSplitWorkgroups ||
+        batch > 65535 || (long long)batch * n_q_heads > attn::kMaxCombineRows)
+        return ATTN_ERR_UNSUPPORTED;
 
     attn::DecodeParams p;
     p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
@@ -165,6 +167,7 @@ int attn_lse_combine(const float *o_parts, const float *lse_parts, const int32_t
     if (rows < 0 || max_splits <= 0 || head_dim <= 0) return ATTN_ERR_SHAPE;
     if (!head_dim_ok(head_dim) || (o_dtype != ATTN_F32 && o_dtype != ATTN_BF16))
         return ATTN_ERR_UNSUPPORTED;
+    if (max_splits > attn::kMaxSplits || rows > attn::kMaxCombineRows) return ATTN_ERR_UNSUPPORTED;
     if (rows == 0) return ATTN_OK;
     if (!o_parts || !lse_parts || !o) return ATTN_ERR_NULL;
     if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) ||

@@ -51,5 +51,11 @@ hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream);
 // Decode tiling constants the host front end needs for validation/sizing.
 constexpr int kDecodeMaxGroup = 16;  // largest supported n_q_heads / n_kv_heads
 constexpr int kDecodeTokenQuantum = 16;  // chunk sizes are multiples of this
+// Largest number of partials per row: a row's partials (splits x head_dim x 4
+// bytes) are addressed through one buffer descriptor with a 31-bit range.
+constexpr long long kMaxSplits = (1LL << 22) - 1;
+// Largest one-dimensional grid of the decode kernels (workgroups x threads < 2^32).
+constexpr long long kMaxSplitWorkgroups = (1LL << 23) - 1;   // 512-thread split workgroups
+constexpr long long kMaxCombineRows = (1LL << 24) - 1;       // 256-thread combine workgroups
 
 }  // namespace attn

@@ -218,7 +218,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
     __shared__ __attribute__((aligned(1024))) char slabs[kWaves * Gm::SLAB];
     __shared__ float ml[2][kWaves][16];
 
-    const int chunk = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    // the KV heads of one chunk are adjacent workgroups, so the heads' rows of the
+    // same tokens (adjacent in memory) are requested at about the same time
+    const int hk = blockIdx.x % a.Hkv, chunk = blockIdx.x / a.Hkv, b = blockIdx.y;
     // lengths outside [0, capacity] are clamped so no read leaves the sequence's cache
     const int L = (int)max(0LL, min((long long)a.seq_lens[b], a.seq_tokens));
     const int t_begin = chunk * a.chunk;
@@ -347,19 +349,6 @@ struct CombineArgs {
     float *lse;
 };
 
-__device__ __forceinline__ float wave_max(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
-__device__ __forceinline__ float wave_sum(float x)
-{
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
-
 template <int D>
 __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArgs a)
 {
@@ -382,31 +371,45 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
     }
     ns = max(0, min(ns, a.max_splits));
     const float *lam = a.lse_parts + row * a.max_splits;
-    const f32x4_t *op = reinterpret_cast<const f32x4_t *>(a.o_parts + row * a.max_splits * D) + col;
+    // descriptors over the row's first ns partials: loads past them return zero,
+    // so every load is unconditional and all of them can be in flight together
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(reinterpret_cast<const char *>(a.o_parts + row * a.max_splits * D), (uint32_t)ns * D * 4u);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(reinterpret_cast<const char *>(lam), (uint32_t)ns * 4u);
+    auto load_part = [&](int k, f32x4_t &vk, float &lk) {
+        vk = __builtin_bit_cast(f32x4_t, bload16(ro, (uint32_t)k * (D * 4) + 16u * col, 0));
+        const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4u * k, 0, 0));
+        lk = (k < ns) ? x : -INFINITY;
+    };
 
     // first batch of partials, in flight while Lambda is reduced
     f32x4_t v[U];
     float lk[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int k = sg + SG * u;
-        if (k < ns) {
-            v[u] = op[(size_t)k * C4];
-            lk[u] = lam[k];
-        } else {
-            v[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            lk[u] = -INFINITY;
+    for (int u = 0; u < U; ++u) load_part(sg + SG * u, v[u], lk[u]);
+    // Lambda = mx + ln z, z = sum_k exp(lambda_k - mx): every wave reduces the
+    // row on its own, one pass with a running (max, sum) per lane, then a
+    // butterfly merge of the lanes' pairs by the same rule
+    const int npass = (ns + 63) / 64;
+    float mx = -INFINITY, z = 0.f;
+    for (int p = 0; p < npass; ++p) {
+        const int k = lane + 64 * p;
+        const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4u * k, 0, 0));
+        if (k < ns && x > mx) {
+            z = z * expf(mx - x) + 1.f;
+            mx = x;
+        } else if (k < ns && x != -INFINITY) {
+            z += expf(x - mx);
         }
     }
-    // Lambda = mx + ln sum_k exp(lambda_k - mx)
-    float mx = -INFINITY;
-    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, lam[k]);
-    mx = wave_max(mx);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float om = __shfl_xor(mx, off), oz = __shfl_xor(z, off);
+        const float nm = fmaxf(mx, om);
+        if (nm != -INFINITY) z = z * expf(mx - nm) + oz * expf(om - nm);
+        mx = nm;
+    }
     const bool empty = (mx == -INFINITY);
-    float z = 0.f;
-    if (!empty)
-        for (int k = lane; k < ns; k += 64) z += expf(lam[k] - mx);
-    z = wave_sum(z);
     const float Lam = empty ? -INFINITY : mx + logf(z);
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -419,15 +422,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
         }
         for (int k0 = sg + SG * U; k0 < ns; k0 += SG * U) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int k = k0 + SG * u;
-                if (k < ns) {
-                    v[u] = op[(size_t)k * C4];
-                    lk[u] = lam[k];
-                } else {
-                    lk[u] = -INFINITY;
-                }
-            }
+            for (int u = 0; u < U; ++u) load_part(k0 + SG * u, v[u], lk[u]);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const float w = expf(lk[u] - Lam);
@@ -486,7 +481,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     a.max_chunks = p.max_chunks;
     a.seq_tokens = (long long)p.max_blocks * p.page_size;
     a.scale_log2 = p.scale * kLog2e;
-    const dim3 grid((unsigned)p.max_chunks, (unsigned)p.Hkv, (unsigned)p.B);
+    const dim3 grid((unsigned)((long long)p.max_chunks * p.Hkv), (unsigned)p.B);
     if (p.head_dim == 128)
         hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(kThreads), 0, stream, a);
     else

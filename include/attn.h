@@ -106,6 +106,8 @@ int attn_prefill(const void *q, const void *k, const void *v, void *o, float *ls
  *   workspace / workspace_bytes: device scratch of at least
  *               attn_decode_workspace_bytes(...) bytes for the per-chunk
  *               partials; contents on entry are ignored.
+ *   Size limits (else ATTN_ERR_UNSUPPORTED): batch <= 65535, batch*n_q_heads < 2^24,
+ *   chunks per sequence < 2^22 and chunks per sequence * n_kv_heads < 2^23.
  *   head_dim in {64, 128}; n_q_heads / n_kv_heads <= 16; dtype ATTN_BF16 only
  *   (bf16 products on matrix cores with float32 accumulation, P rounded to bf16
  *   before the P*V product, partials and the combine in float32, O rounded to
@@ -145,7 +147,8 @@ size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
  *   o         [rows, head_dim] element type `o_dtype` (ATTN_F32 or ATTN_BF16)
  *   lse_or_null [rows] float32 (written when not NULL)
  *   A row whose partials are all empty gets o = 0, Lambda = -inf.
- *   head_dim in {64, 128}; rows >= 0; max_splits >= 1.
+ *   head_dim in {64, 128}; rows >= 0; 1 <= max_splits < 2^22 and rows < 2^24
+ *   (larger is ATTN_ERR_UNSUPPORTED).
  */
 int attn_lse_combine(const float *o_parts, const float *lse_parts,
                      const int32_t *n_splits_or_null, int rows, int max_splits, int head_dim,
