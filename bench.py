@@ -26,8 +26,16 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak (published)
 METRIC = "causal prefill TFLOP/s (N=16k, d=128) + split-KV decode HBM GB/s at 32k"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_n16384_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "exact_io_aware_prefill_amd", "csrc", "prefill_bf16.hip")
+CSRC = os.path.join(ROOT, "exact_io_aware_prefill_amd", "csrc")
+# HBM traffic per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script,
+# valid while the kernel source they were taken on is unchanged (sha256 recorded)
+TRAFFIC = {
+    "prefill": {"file": os.path.join(ROOT, "profiles", "prefill_bf16_n16384_traffic.json"),
+                "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel"},
+    "decode": {"file": os.path.join(ROOT, "profiles", "decode_split_s32768_traffic.json"),
+               "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel"},
+}
+COPY_BYTES = 1 << 30  # reference dispatch for the counters: a 1 GiB device-to-device copy
 N_KV_COPIES = 8
 
 
@@ -42,25 +50,70 @@ def parse():
                     help="time one half of the step (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference dispatch for HBM counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="write profiles/*_traffic.json from two rocprofv3 counter runs, then exit")
+    ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
     return ap.parse_args()
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(per_launch_units: float):
-    """HBM bytes per prefill launch from committed counter runs, if they still describe
-    the current kernel source; else None."""
+def measured_traffic(which: str):
+    """HBM bytes per launch of the named kernel from committed counter runs, if they
+    still describe the current kernel source; else None."""
+    t = TRAFFIC[which]
     try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
+        with open(t["file"]) as f:
+            rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_hash():
+    if rec.get("kernel_source_sha256") != source_hash(t["src"]):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(csv_path: str, counter: str):
+    import csv
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def write_traffic(fetch_csv: str, write_csv: str, command: str):
+    """Turn two counter runs of this script (FETCH_SIZE, then WRITE_SIZE; each with
+    --copy-calibration) into per-launch HBM byte records for the prefill and decode
+    split kernels.  Counter values are KiB per dispatch; each counter is scaled by
+    the factor that makes it read COPY_BYTES for the 1 GiB copy dispatch."""
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, name)
+        copy_kib = max(v for k, v in rows if "copyBuffer" in k)  # the 1 GiB copy is the largest
+        factor = COPY_BYTES / (copy_kib * 1024.0)
+        for which, t in TRAFFIC.items():
+            vals = [v for k, v in rows if t["kernel"] in k]
+            if not vals:
+                continue
+            rec = out.setdefault(which, {"calibration": {}})
+            rec[name.lower() + "_kib_avg"] = sum(vals) / len(vals)
+            rec[name.lower() + "_dispatches"] = len(vals)
+            rec[name.lower() + "_bytes"] = sum(vals) / len(vals) * 1024.0 * factor
+            rec["calibration"][name] = {"copy_bytes": COPY_BYTES, "copy_counter_kib": copy_kib,
+                                        "factor": factor}
+    for which, rec in out.items():
+        t = TRAFFIC[which]
+        rec["kernel"] = t["kernel"]
+        rec["kernel_source_sha256"] = source_hash(t["src"])
+        rec["hbm_bytes_per_launch"] = rec.get("fetch_size_bytes", 0.0) + rec.get("write_size_bytes", 0.0)
+        rec["command"] = command
+        with open(t["file"], "w") as f:
+            json.dump(rec, f, indent=1)
+        print("wrote", t["file"], json.dumps({k: rec[k] for k in ("hbm_bytes_per_launch",)}))
 
 
 def cpu_baseline(x, target_s: float):
@@ -93,6 +146,9 @@ def cpu_baseline(x, target_s: float):
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.traffic_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention path here runs on a single MI355X "
               "and has no multi-GPU mode (--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -162,7 +218,7 @@ def main():
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
 
     if args.copy_calibration:  # reference dispatch for the HBM byte counters: copy 1 GiB
-        src = torch.empty(1 << 29, dtype=torch.float16, device=dev).fill_(1)
+        src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device=dev).fill_(1)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
@@ -191,14 +247,14 @@ def main():
         achieved = prefill_flop / (pre_ms * 1e-3) / 1e12
         out["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                           "traffic": measured_traffic(1.0),
+                           "traffic": measured_traffic("prefill"),
                            "kernel": "prefill_bf16_kernel<128>", "avg_launch_ms": pre_ms,
                            "algorithmic_flop_per_launch": prefill_flop}
     if do_d:
         gbs = decode_bytes / (dec_ms * 1e-3) / 1e9
         out["decode"] = {"value": gbs, "unit": "GB/s", "avg_ms": dec_ms,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                      "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                                      "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode"),
                                       "kernels": "decode_split_kernel<128> + lse_combine_kernel<128>",
                                       "algorithmic_bytes_per_launch": decode_bytes}}
     if do_p and not args.no_cpu_baseline:
