@@ -27,7 +27,7 @@
 //     scores of tile t+1 on the matrix cores while the vector ALUs compute the
 //     softmax of tile t, all in one basic block, so the two units overlap
 //     inside a wave.  K/V tiles are double-buffered in LDS and fetched one
-//     iteration ahead with buffer loads (scalar tile offsets, out-of-range rows
+//     iteration ahead with buffer loads (one descriptor per tile, rows past N
 //     read as zero); one barrier per tile.
 //   * The exponentials of tile t use the running max from before the tile,
 //     so they do not wait for the tile's own row max.  Only if some row's new
@@ -94,7 +94,8 @@ __device__ __forceinline__ int vt_slot(int sub) { return ((sub & 1) << 3) | ((su
 
 // Global -> register -> LDS staging of one K tile (row-major) and one V tile
 // (transposed into the accumulator key order).  Each thread owns fixed chunks;
-// the tile offset is a scalar, so a load is one buffer instruction.
+// the tile's position is in the (scalar) descriptor, so a load is one buffer
+// instruction with a per-lane offset fixed for the whole kernel.
 template <int D, int NT>
 struct Stage {
     static constexpr int KS = D + 8;        // K row stride in LDS (bf16): 16-byte aligned, bank-rotating
@@ -132,21 +133,25 @@ struct Stage {
     __device__ __forceinline__ bool kvalid(int i, int tid) const { return KCHUNKS % NT == 0 || tid + i * NT < KCHUNKS; }
     __device__ __forceinline__ bool vvalid(int i, int tid) const { return VUNITS % NT == 0 || tid + i * NT < VUNITS; }
 
-    __device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rk, int k0, int tid)
+    // A tile's loads go through a descriptor based at the tile's first row whose
+    // range ends at row N: rows past N read as zero and nothing past the head's
+    // rows is touched.  (The range check applies to the per-lane offset, so the
+    // tile offset is folded into the base rather than passed as a scalar offset.)
+    __device__ __forceinline__ void load_k(const uint16_t *kh, int N, int k0, int tid)
     {
-        const uint32_t so = (uint32_t)k0 * D * 2u;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + (size_t)k0 * D, (uint32_t)max(N - k0, 0) * D * 2u);
 #pragma unroll
         for (int i = 0; i < KPT; ++i)
-            if (kvalid(i, tid)) kr[i] = bload16(rk, koff[i], so);
+            if (kvalid(i, tid)) kr[i] = bload16(r, koff[i], 0);
     }
-    __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, int k0, int tid)
+    __device__ __forceinline__ void load_v(const uint16_t *vh, int N, int k0, int tid)
     {
-        const uint32_t so = (uint32_t)k0 * D * 2u;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(vh + (size_t)k0 * D, (uint32_t)max(N - k0, 0) * D * 2u);
 #pragma unroll
         for (int i = 0; i < VPT; ++i)
             if (vvalid(i, tid)) {
-                vr[i][0] = bload16(rv, voff[i], so);
-                vr[i][1] = bload16(rv, voff[i] + D * 2u, so);
+                vr[i][0] = bload16(r, voff[i], 0);
+                vr[i][1] = bload16(r, voff[i] + D * 2u, 0);
             }
     }
     __device__ __forceinline__ void store_k(uint16_t *Ks, int tid) const
@@ -255,8 +260,8 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
     const int q0 = qtile * BM;
     const uint32_t head_bytes = (uint32_t)a.N * D * 2u;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (size_t)bh * a.N * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + (size_t)(b * a.Hkv + hk) * a.N * D, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + (size_t)(b * a.Hkv + hk) * a.N * D, head_bytes);
+    const uint16_t *const kh = a.k + (size_t)(b * a.Hkv + hk) * a.N * D;
+    const uint16_t *const vh = a.v + (size_t)(b * a.Hkv + hk) * a.N * D;
 
     const int wrow0 = q0 + wave * 32;  // first query row of this wave
     const int qrow = wrow0 + l32;      // the query row this lane owns
@@ -290,9 +295,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
     // ---- prologue: K(0) and K(1) staged, VB1 zeroed, S(0) formed, V(0) in flight ------
     St st;
     st.init(tid);
-    st.load_k(rk, 0, tid);
+    st.load_k(kh, a.N, 0, tid);
     st.store_k(KB0, tid);
-    st.load_k(rk, kBlockN, tid);  // tile 1 (zeros past N); never multiplied in if ntiles == 1
+    st.load_k(kh, a.N, kBlockN, tid);  // tile 1 (zeros past N); never multiplied in if ntiles == 1
     st.store_k(KB1, tid);
     for (int i = tid; i < VBUF / 8; i += NT) reinterpret_cast<uint4 *>(VB1)[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
@@ -303,7 +308,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) P1[ks][e] = (__bf16)0.f;  // "tile -1": P = 0 against the zeroed VB1
-    st.load_v(rv, 0, tid);
+    st.load_v(vh, a.N, 0, tid);
     __syncthreads();  // every wave has read KB0 before iteration 0 refills it
 
     // One pipeline step.  Sc = scores of tile t (formed last step), Sn receives
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
     auto step = [&](f32x16_t (&Sc)[2], f32x16_t (&Sn)[2], bf16x8_t (&Pp)[4], bf16x8_t (&Pc)[4], int t,
                     const uint16_t *Kn, const uint16_t *Vp, uint16_t *Kw, uint16_t *Vw) {
         const int k0 = t * kBlockN;
-        if (t + 2 < ntiles) st.load_k(rk, k0 + 2 * kBlockN, tid);  // fetched during this step
+        if (t + 2 < ntiles) st.load_k(kh, a.N, k0 + 2 * kBlockN, tid);  // fetched during this step
         // diagonal / ragged tile: mask keys past the row (causal) or past N
         if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > a.N) {
             const int lim = (a.causal ? min(qrow, a.N - 1) : a.N - 1) - (k0 + 4 * hh);
@@ -348,7 +353,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
         // ---- stage K(t+2) and V(t) for the next step ------------------------------------
         if (t + 2 < ntiles) st.store_k(Kw, tid);
         st.store_v(Vw, tid);
-        if (t + 1 < ntiles) st.load_v(rv, k0 + kBlockN, tid);
+        if (t + 1 < ntiles) st.load_v(vh, a.N, k0 + kBlockN, tid);
         __syncthreads();
     };
 
