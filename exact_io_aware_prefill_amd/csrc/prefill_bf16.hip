@@ -62,7 +62,7 @@ constexpr int kBlockN = 64;  // keys per tile
 constexpr int kXcds = 8;     // MI355X: workgroups are dispatched round-robin over 8 XCDs
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRescaleLog2 = 8.f;             // raise the reference max only past 2^8
+constexpr float kMaxLaneSum = 256.f;            // a lane's tile sum above this redoes the tile
 constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
 struct Args {
@@ -87,93 +87,64 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// Position of key group `sub` (keys 4*sub..4*sub+3 of a 16-key step) inside
-// the transposed V row: lanes of the lower half-wave read keys {0-3, 8-11},
-// the upper half {4-7, 12-15}, matching the 32x32 accumulator rows.
-__device__ __forceinline__ int vt_slot(int sub) { return ((sub & 1) << 3) | ((sub & 2) << 1); }
+// 64-byte unit permutation of the row-major V tile in LDS: unit u of key row r
+// sits at u ^ vswz(r), so the transpose reads of 4 consecutive rows (64 bytes
+// each) fall in distinct banks.
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? (r & 3) : ((r >> 1) & 1); }
 
-// Global -> register -> LDS staging of one K tile (row-major) and one V tile
-// (transposed into the accumulator key order).  Each thread owns fixed chunks;
-// the tile's position is in the (scalar) descriptor, so a load is one buffer
-// instruction with a per-lane offset fixed for the whole kernel.
+// Global -> register -> LDS staging of one K tile and one V tile, both row-major
+// (V is read back transposed by the LDS transpose read).  Each thread owns fixed
+// 16-byte chunks; the tile's position is in the (scalar) descriptor, so a load is
+// one buffer instruction with a per-lane offset fixed for the whole kernel.
 template <int D, int NT>
 struct Stage {
     static constexpr int KS = D + 8;        // K row stride in LDS (bf16): 16-byte aligned, bank-rotating
-    static constexpr int VS = kBlockN + 8;  // transposed-V row stride in LDS (bf16)
     static constexpr int KBUF = kBlockN * KS;
-    static constexpr int VBUF = D * VS;
-    static constexpr int KCHUNKS = kBlockN * D / 8;         // 16-byte chunks of a K tile
-    static constexpr int KPT = (KCHUNKS + NT - 1) / NT;     // per thread
-    static constexpr int VUNITS = (kBlockN / 2) * (D / 8);  // units of 2 keys x 8 dims
-    static constexpr int VPT = (VUNITS + NT - 1) / NT;
-    uint4 kr[KPT];
-    uint4 vr[VPT][2];
-    uint32_t koff[KPT], kls[KPT];  // global byte offset within a tile / LDS element offset
-    uint32_t voff[VPT], vls[VPT];
+    static constexpr int VBUF = kBlockN * D;
+    static constexpr int CHUNKS = kBlockN * D / 8;        // 16-byte chunks of a tile
+    static constexpr int CPT = (CHUNKS + NT - 1) / NT;    // per thread
+    uint4 kr[CPT], vr[CPT];
+    uint32_t goff[CPT], kls[CPT], vls[CPT];  // global byte offset in a tile / LDS element offsets
 
     __device__ __forceinline__ void init(int tid)
     {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
+        for (int i = 0; i < CPT; ++i) {
             const int ch = tid + i * NT;
             const int r = ch / (D / 8), c = ch % (D / 8);
-            koff[i] = (uint32_t)(r * D + 8 * c) * 2u;
+            goff[i] = (uint32_t)(r * D + 8 * c) * 2u;
             kls[i] = (uint32_t)(r * KS + 8 * c);
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int un = tid + i * NT;
-            const int kp = un % (kBlockN / 2), dc = un / (kBlockN / 2);  // key pair, 8-dim chunk
-            const int kg = kp >> 1;
-            voff[i] = (uint32_t)(2 * kp * D + 8 * dc) * 2u;
-            vls[i] = (uint32_t)((8 * dc) * VS + 16 * (kg >> 2) + vt_slot(kg & 3) + 2 * (kp & 1));
+            vls[i] = (uint32_t)(r * D + 32 * ((c >> 2) ^ vswz<D>(r)) + 8 * (c & 3));
         }
     }
 
-    __device__ __forceinline__ bool kvalid(int i, int tid) const { return KCHUNKS % NT == 0 || tid + i * NT < KCHUNKS; }
-    __device__ __forceinline__ bool vvalid(int i, int tid) const { return VUNITS % NT == 0 || tid + i * NT < VUNITS; }
+    __device__ __forceinline__ bool valid(int i, int tid) const { return CHUNKS % NT == 0 || tid + i * NT < CHUNKS; }
 
     // A tile's loads go through a descriptor based at the tile's first row whose
     // range ends at row N: rows past N read as zero and nothing past the head's
     // rows is touched.  (The range check applies to the per-lane offset, so the
     // tile offset is folded into the base rather than passed as a scalar offset.)
-    __device__ __forceinline__ void load_k(const uint16_t *kh, int N, int k0, int tid)
+    __device__ __forceinline__ void load(uint4 (&dst)[CPT], const uint16_t *base, int N, int k0, int tid)
     {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(kh + (size_t)k0 * D, (uint32_t)max(N - k0, 0) * D * 2u);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (size_t)k0 * D, (uint32_t)max(N - k0, 0) * D * 2u);
 #pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            if (kvalid(i, tid)) kr[i] = bload16(r, koff[i], 0);
+        for (int i = 0; i < CPT; ++i)
+            if (valid(i, tid)) dst[i] = bload16(r, goff[i], 0);
     }
-    __device__ __forceinline__ void load_v(const uint16_t *vh, int N, int k0, int tid)
-    {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(vh + (size_t)k0 * D, (uint32_t)max(N - k0, 0) * D * 2u);
-#pragma unroll
-        for (int i = 0; i < VPT; ++i)
-            if (vvalid(i, tid)) {
-                vr[i][0] = bload16(r, voff[i], 0);
-                vr[i][1] = bload16(r, voff[i] + D * 2u, 0);
-            }
-    }
+    __device__ __forceinline__ void load_k(const uint16_t *kh, int N, int k0, int tid) { load(kr, kh, N, k0, tid); }
+    __device__ __forceinline__ void load_v(const uint16_t *vh, int N, int k0, int tid) { load(vr, vh, N, k0, tid); }
     __device__ __forceinline__ void store_k(uint16_t *Ks, int tid) const
     {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i)
-            if (kvalid(i, tid)) *reinterpret_cast<uint4 *>(&Ks[kls[i]]) = kr[i];
+        for (int i = 0; i < CPT; ++i)
+            if (valid(i, tid)) *reinterpret_cast<uint4 *>(&Ks[kls[i]]) = kr[i];
     }
-    __device__ __forceinline__ void store_v(uint16_t *Vt, int tid) const
+    __device__ __forceinline__ void store_v(uint16_t *Vs, int tid) const
     {
 #pragma unroll
-        for (int i = 0; i < VPT; ++i)
-            if (vvalid(i, tid)) {
-                const uint32_t a[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
-                const uint32_t b[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    // dim 8*dc+2p: (key0, key1) low halves; dim 8*dc+2p+1: high halves
-                    *reinterpret_cast<uint32_t *>(&Vt[vls[i] + (2 * p) * VS]) = (a[p] & 0xffffu) | (b[p] << 16);
-                    *reinterpret_cast<uint32_t *>(&Vt[vls[i] + (2 * p + 1) * VS]) = (a[p] >> 16) | (b[p] & 0xffff0000u);
-                }
-            }
+        for (int i = 0; i < CPT; ++i)
+            if (valid(i, tid)) *reinterpret_cast<uint4 *>(&Vs[vls[i]]) = vr[i];
     }
 };
 
@@ -195,16 +166,28 @@ __device__ __forceinline__ void qk_tile(f32x16_t (&S)[2], const uint16_t *Ks, co
         }
 }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// O^T += V^T P^T for one 64-key tile.  The A operand (V^T: 32 dims x 8 keys per
+// lane) comes from the row-major V tile by two transpose reads: in 16-lane group
+// G of the wave, lane 4r+q reads dims 16(G&1)+4q..+3 of key row kb+r, and lane j
+// receives dim 16(G&1)+j of the 4 rows.  Keys follow the score accumulator's
+// order: for 16-key step ks the lane's 8 values are keys 16ks + 4hh + {0..3} and
+// 16ks + 8 + 4hh + {0..3}.  `vrd` is the lane's element offset for ks = 0, db = 0.
 template <int D>
-__device__ __forceinline__ void pv_tile(f32x16_t (&acc)[D / 32], const uint16_t *Vt, const bf16x8_t (&pf)[4],
-                                        int l32, int hh)
+__device__ __forceinline__ void pv_tile(f32x16_t (&acc)[D / 32], const uint16_t *Vs, const bf16x8_t (&pf)[4],
+                                        uint32_t vrd)
 {
-    constexpr int VS = kBlockN + 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-            const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(&Vt[(db * 32 + l32) * VS + 16 * ks + 8 * hh]);
+            // rows 16ks.. keep the row's swizzle (16ks is a multiple of 4); unit db is a XOR
+            const uint16_t *p = Vs + 16 * ks * D + (vrd ^ (32u * db));
+            const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)p);
+            const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)(p + 8 * D));
+            const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], acc[db], 0, 0, 0);
         }
 }
@@ -286,8 +269,12 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
     float m = -INFINITY;  // reference max of raw scores for this lane's row
     float l = 0.f;        // this lane's share of the running sum (its 16 of every 32 keys)
     const float sl2 = a.scale_log2;
-    const float slack = kRescaleLog2 / sl2;  // raw-score margin before the max must move
     const int xlane = (lane ^ 32) << 2;      // ds_bpermute address of the other half-wave
+    // transpose-read offset of this lane into a V tile (see pv_tile)
+    const uint32_t vrd = [&] {
+        const int w = lane & 15, r = w >> 2, q = w & 3, g1 = (lane >> 4) & 1;
+        return (uint32_t)((4 * hh + r) * D + 32 * vswz<D>(r) + 16 * g1 + 4 * q);
+    }();
 
     const int kend = a.causal ? min(a.N, q0 + BM) : a.N;  // keys this tile may see
     const int ntiles = (kend + kBlockN - 1) / kBlockN;
@@ -327,18 +314,20 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
                     if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) Sc[kb][i] = -INFINITY;
         }
         // ---- hot block: matrix cores run PV(t-1) and S(t+1) while the ALUs do softmax(t)
-        const float mb = (m == -INFINITY) ? 0.f : m * sl2;
-        pv_tile<D>(acc, Vp, Pp, l32, hh);
+        // against the reference max from before this tile (the first tile, with no
+        // reference yet, always takes the branch below)
+        pv_tile<D>(acc, Vp, Pp, vrd);
         qk_tile<D>(Sn, Kn, qf, l32, hh);
-        float mx = -INFINITY;
+        float rs = softmax_tile(Sc, sl2, m * sl2, Pc);
+        // ---- rare: some probability may exceed 2^8 (or the row has no reference
+        // yet): raise the reference to the true running max, rescale, redo the tile
+        if (__ballot(m == -INFINITY || rs > kMaxLaneSum)) {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, Sc[kb][i]);
-        float rs = softmax_tile(Sc, sl2, mb, Pc);
-        mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
-        // ---- rare: a row's scores passed its reference max by more than 2^8 ------------
-        if (__ballot(mx > m + slack)) {
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, Sc[kb][i]);
+            mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
             const float m_new = fmaxf(m, mx);
             const float c = __builtin_amdgcn_exp2f((m - m_new) * sl2);  // 0 while m = -inf
             l *= c;
@@ -347,7 +336,7 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[db][i] *= c;
             m = m_new;
-            rs = softmax_tile(Sc, sl2, (m == -INFINITY) ? 0.f : m * sl2, Pc);
+            rs = softmax_tile(Sc, sl2, m * sl2, Pc);
         }
         l += rs;
         // ---- stage K(t+2) and V(t) for the next step ------------------------------------
@@ -365,9 +354,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void prefill_bf16_kernel(Args a)
     }
     // last product: P of tile ntiles-1 is in P0 (ntiles odd) or P1 (even), V in VB[(ntiles-1)&1]
     if (ntiles & 1)
-        pv_tile<D>(acc, VB0, P0, l32, hh);
+        pv_tile<D>(acc, VB0, P0, vrd);
     else
-        pv_tile<D>(acc, VB1, P1, l32, hh);
+        pv_tile<D>(acc, VB1, P1, vrd);
 
     // ---- epilogue: O = acc / l, LSE = m * scale + ln l ---------------------------------
     const float lt = l + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, l)));
