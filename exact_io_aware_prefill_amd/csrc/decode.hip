@@ -303,29 +303,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
         ml[0][wave][l16] = m;  // -inf for a wave that saw no token
         ml[1][wave][l16] = lt;
     }
-    __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[0][w][l16]);
-    float Lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) Lsum += __builtin_amdgcn_exp2f(ml[0][w][l16] - M) * ml[1][w][l16];
-    const float sc = __builtin_amdgcn_exp2f(m - M);
-    // The wave's slab now holds its rescaled output as [query][D] floats, the
+    // The wave's slab now holds its unscaled output as [query][D] floats, the
     // 16-byte column chunk c of query row r at chunk c ^ r: the 16 rows a store
     // or load instruction touches per pass then fall on distinct banks.
     float *wo = reinterpret_cast<float *>(slab);
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb)
-        *reinterpret_cast<f32x4_t *>(&wo[l16 * D + 4 * ((4 * nb + G) ^ l16)]) = acc[nb] * sc;
+    for (int nb = 0; nb < D / 16; ++nb) *reinterpret_cast<f32x4_t *>(&wo[l16 * D + 4 * ((4 * nb + G) ^ l16)]) = acc[nb];
     __syncthreads();
-    // wave w sums d-block w over the eight waves and writes the chunk's partial
+    // wave w merges d-block w of the eight waves and writes the chunk's partial
     if (wave < D / 16 && l16 < g) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[0][w][l16]);
+        float Lsum = 0.f;
         f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            sum += *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(slabs + w * Gm::SLAB) + l16 * D +
-                                                      4 * ((4 * wave + G) ^ l16));
+        for (int w = 0; w < kWaves; ++w) {
+            const float e = __builtin_amdgcn_exp2f(ml[0][w][l16] - M);  // 0 for a wave that saw no token
+            Lsum += e * ml[1][w][l16];
+            sum += e * *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(slabs + w * Gm::SLAB) +
+                                                          l16 * D + 4 * ((4 * wave + G) ^ l16));
+        }
         const size_t row = (size_t)b * a.Hq + (size_t)hk * g + l16;
         const float inv = 1.f / Lsum;  // Lsum >= 1: the row's largest term is exp2(0)
         *reinterpret_cast<f32x4_t *>(&a.o_parts[(row * a.max_chunks + chunk) * D + 16 * wave + 4 * G]) = sum * inv;

@@ -46,13 +46,13 @@
 //     reference value gives the same O = acc/l and LSE = m + ln l; the bound
 //     keeps every probability <= 256 in float32.  Exponentials run in base 2
 //     with scale*log2(e) folded into one FMA.
-//   * Work order: consecutive workgroup ids are dispatched round-robin over the
-//     8 XCDs, each with its own L2.  Ids are remapped so each XCD receives a
-//     contiguous slice of a list ordered (sequence, KV head, query tile, query
-//     head): the workgroups resident on one XCD share one KV head's keys and
-//     values in L2.  Query tiles are listed in zig-zag order (last, first,
-//     second last, second, ...) so every slice carries the same causal work
-//     and the longest tiles start first.
+//   * Work order: workgroup ids walk (sequence, KV head, query tile, query head)
+//     with the query head fastest, so the query heads that share a KV head run
+//     at the same time and read the same key/value tiles.  Query tiles are
+//     taken in zig-zag order (last, first, second last, second, ...) so the
+//     longest tiles start first and the causal work stays balanced over time.
+//     (Remapping ids so that each XCD gets a contiguous slice of this list, to
+//     keep a KV head's tiles in one XCD's L2, measured 2% slower.)
 //
 // This file is compiled with -fno-honor-nans (inputs must be finite): the row
 // max then maps to v_max3_f32 without NaN-quieting copies.  Infinities, which
@@ -79,7 +79,6 @@ constexpr int kBM = kWaves * kBlocks * 32;  // query rows per workgroup
 constexpr int kBlockN = 32;    // keys per tile
 constexpr int kKB = kBlockN / 32;  // 32-key score blocks per tile
 constexpr int kKS = kBlockN / 16;  // 16-key steps of the P*V product per tile
-constexpr int kXcds = 8;       // MI355X: workgroups are dispatched round-robin over 8 XCDs
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaxLaneSum = 256.f;            // a lane's tile sum above this redoes the tile
@@ -126,6 +125,9 @@ struct TileLoader {
     static constexpr int INSTR = kBlockN * NC / 64;  // wave instructions per tile
     static constexpr int PER_WAVE = (INSTR + kWaves - 1) / kWaves;
     static_assert(INSTR % kWaves == 0 || INSTR < kWaves, "tile instructions split evenly over the waves");
+    // a lane's instructions fill rows 4*kWaves apart (D = 128) or 8*kWaves apart
+    // (D = 64); with kWaves a multiple of 4 those rows share their permutation
+    static_assert(kWaves % 4 == 0, "one per-lane offset needs kWaves to be a multiple of 4");
     uint32_t voff;  // per-lane byte offset inside the 1 KiB an instruction fills
 
     template <typename Swz>
@@ -246,13 +248,8 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // ---- work item: XCD-contiguous slices of (b, kv head, zig-zag q tile, q head) ----
-    int item;
-    {
-        const int x = blockIdx.x, xcd = x % kXcds, i = x / kXcds;
-        const int base = a.n_items / kXcds, rem = a.n_items % kXcds;
-        item = xcd * base + min(xcd, rem) + i;
-    }
+    // ---- work item: (b, kv head, zig-zag q tile, q head), query head fastest ----
+    const int item = blockIdx.x;
     const int j = item % a.group;
     const int r = (item / a.group) % a.n_qtiles;
     const int bg = item / (a.group * a.n_qtiles);
