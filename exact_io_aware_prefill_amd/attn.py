@@ -30,8 +30,8 @@ ATTN_ERR_HIP = -7
 ATTN_F32 = 0
 ATTN_BF16 = 1
 
-EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_chunk_tokens", "attn_decode_workspace_bytes",
-           "attn_lse_combine", "attn_status_string")
+EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_append", "attn_decode_chunk_tokens",
+           "attn_decode_workspace_bytes", "attn_lse_combine", "attn_status_string")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -40,6 +40,9 @@ lib.attn_prefill.restype = _I
 lib.attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                             _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode.restype = _I
+lib.attn_decode_append.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                                   _I, _P, ctypes.c_size_t, _P]
+lib.attn_decode_append.restype = _I
 lib.attn_decode_chunk_tokens.argtypes = [_I, _I, _I, _I, _I]
 lib.attn_decode_chunk_tokens.restype = _I
 lib.attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I]
@@ -121,6 +124,23 @@ def attn_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, page_size: i
     _check(rc, "attn_decode")
 
 
+def attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse,
+                       page_size: int, max_blocks_per_seq: int, scale: float, chunk_tokens: int, workspace,
+                       stream=None) -> None:
+    """attn_decode after writing k_new, v_new [B, Hkv, d] into the caches at token
+    cache_seqlens[b] (the tokens already cached); the query attends cache_seqlens[b] + 1
+    tokens.  cache_seqlens is not modified."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[-2]
+    rc = lib.attn_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(block_table), _ptr(cache_seqlens), _ptr(o), _ptr(lse), B, Hq, Hkv, d,
+                                int(page_size), int(max_blocks_per_seq), _dtype_code(q), float(scale),
+                                int(chunk_tokens), _ptr(workspace),
+                                0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _check(rc, "attn_decode_append")
+
+
 def attn_lse_combine(o_parts, lse_parts, n_splits, o, lse, stream=None) -> None:
     """o_parts [rows, S, d] f32; lse_parts [rows, S] f32; n_splits [rows] int32 or None;
     o [rows, d] (bf16 or f32); lse [rows] f32 or None."""
@@ -136,6 +156,24 @@ def prefill(q, k, v, causal: bool = True, scale: float | None = None, stream=Non
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     attn_prefill(q, k, v, o, lse, causal, d ** -0.5 if scale is None else scale, stream)
+    return o, lse
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, page_size: int,
+                  max_blocks_per_seq: int, scale: float | None = None, chunk_tokens: int = 0, stream=None,
+                  workspace=None):
+    """Decode step with the new token's k_new, v_new [B, Hkv, d] written into the caches
+    in place at token cache_seqlens[b]; returns (o, lse) over cache_seqlens[b] + 1 tokens."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[-2]
+    need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse, page_size,
+                       max_blocks_per_seq, d ** -0.5 if scale is None else scale, chunk_tokens, workspace,
+                       stream)
     return o, lse
 
 

@@ -51,6 +51,58 @@ int resolve_chunk(int batch, int n_kv_heads, int page_size, int max_blocks, int 
     return (int)chunk;
 }
 
+// Shared body of attn_decode and attn_decode_append; `append` selects the latter
+// (k_new and v_new are then required).
+int decode_impl(bool append, const void *q, const void *k_new, const void *v_new, const void *k_cache,
+                const void *v_cache, const int32_t *block_table, const int32_t *seq_lens, void *o, float *lse_or_null, int batch,
+                int n_q_heads, int n_kv_heads, int head_dim, int page_size, int max_blocks_per_seq, int dtype,
+                float scale, int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 ||
+        max_blocks_per_seq <= 0 || chunk_tokens < 0)
+        return ATTN_ERR_SHAPE;
+    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
+    if (!head_dim_ok(head_dim) || dtype != ATTN_BF16 ||
+        n_q_heads / n_kv_heads > attn::kDecodeMaxGroup)
+        return ATTN_ERR_UNSUPPORTED;
+    // paged blocks of 16 tokens must not straddle pages
+    if (block_table && page_size % attn::kDecodeTokenQuantum != 0) return ATTN_ERR_UNSUPPORTED;
+    const int chunk = resolve_chunk(batch, n_kv_heads, page_size, max_blocks_per_seq, chunk_tokens);
+    if (chunk < 0) return chunk;
+    if (batch == 0) return ATTN_OK;
+    if (!q || !k_cache || !v_cache || !seq_lens || !o) return ATTN_ERR_NULL;
+    if (append && (!k_new || !v_new)) return ATTN_ERR_NULL;
+    const size_t need = attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
+                                                    page_size, max_blocks_per_seq, chunk_tokens);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+        !aligned16(workspace) || (lse_or_null && !aligned16(lse_or_null)) ||
+        (append && (!aligned16(k_new) || !aligned16(v_new))))
+        return ATTN_ERR_ALIGN;
+    const long long cap = (long long)max_blocks_per_seq * page_size;
+    const long long max_chunks = (cap + chunk - 1) / chunk;
+    if (max_chunks > attn::kMaxSplits || max_chunks * n_kv_heads > attn::kMaxSplitWorkgroups ||
+        batch > 65535 || (long long)batch * n_q_heads > attn::kMaxCombineRows)
+        return ATTN_ERR_UNSUPPORTED;
+
+    attn::DecodeParams p;
+    p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
+    p.block_table = block_table; p.seq_lens = seq_lens;
+    p.o = o; p.lse = lse_or_null;
+    p.B = batch; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
+    p.page_size = page_size; p.max_blocks = max_blocks_per_seq; p.dtype = dtype;
+    p.scale = scale;
+    p.chunk = chunk;
+    p.max_chunks = (int)max_chunks;
+    const size_t rows = (size_t)batch * n_q_heads;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.o_parts = static_cast<float *>(workspace);
+    p.lse_parts = p.o_parts + rows * (size_t)max_chunks * head_dim;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return run([&] { return attn::launch_decode(p, s); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -119,45 +171,20 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 int max_blocks_per_seq, int dtype, float scale, int chunk_tokens, void *workspace,
                 size_t workspace_bytes, void *stream)
 {
-    if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 ||
-        max_blocks_per_seq <= 0 || chunk_tokens < 0)
-        return ATTN_ERR_SHAPE;
-    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
-    if (!head_dim_ok(head_dim) || dtype != ATTN_BF16 ||
-        n_q_heads / n_kv_heads > attn::kDecodeMaxGroup)
-        return ATTN_ERR_UNSUPPORTED;
-    // paged blocks of 16 tokens must not straddle pages
-    if (block_table && page_size % attn::kDecodeTokenQuantum != 0) return ATTN_ERR_UNSUPPORTED;
-    const int chunk = resolve_chunk(batch, n_kv_heads, page_size, max_blocks_per_seq, chunk_tokens);
-    if (chunk < 0) return chunk;
-    if (batch == 0) return ATTN_OK;
-    if (!q || !k_cache || !v_cache || !seq_lens || !o) return ATTN_ERR_NULL;
-    const size_t need = attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
-                                                    page_size, max_blocks_per_seq, chunk_tokens);
-    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
-        !aligned16(workspace) || (lse_or_null && !aligned16(lse_or_null)))
-        return ATTN_ERR_ALIGN;
-    const long long cap = (long long)max_blocks_per_seq * page_size;
-    const long long max_chunks = (cap + chunk - 1) / chunk;
-    if (max_chunks > attn::kMaxSplits || max_chunks * n_kv_heads > attn::kMaxSplitWorkgroups ||
-        batch > 65535 || (long long)batch * n_q_heads > attn::kMaxCombineRows)
-        return ATTN_ERR_UNSUPPORTED;
+    return decode_impl(false, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, o, lse_or_null, batch,
+                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale, chunk_tokens,
+                       workspace, workspace_bytes, stream);
+}
 
-    attn::DecodeParams p;
-    p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
-    p.block_table = block_table; p.seq_lens = seq_lens;
-    p.o = o; p.lse = lse_or_null;
-    p.B = batch; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
-    p.page_size = page_size; p.max_blocks = max_blocks_per_seq; p.dtype = dtype;
-    p.scale = scale;
-    p.chunk = chunk;
-    p.max_chunks = (int)max_chunks;
-    const size_t rows = (size_t)batch * n_q_heads;
-    p.o_parts = static_cast<float *>(workspace);
-    p.lse_parts = p.o_parts + rows * (size_t)max_chunks * head_dim;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return run([&] { return attn::launch_decode(p, s); });
+int attn_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                       const int32_t *block_table, const int32_t *cache_seqlens, void *o,
+                       float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                       int page_size, int max_blocks_per_seq, int dtype, float scale, int chunk_tokens,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    return decode_impl(true, q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse_or_null, batch,
+                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale, chunk_tokens,
+                       workspace, workspace_bytes, stream);
 }
 
 int attn_lse_combine(const float *o_parts, const float *lse_parts, const int32_t *n_splits_or_null,

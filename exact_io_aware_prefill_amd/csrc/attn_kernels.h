@@ -34,6 +34,9 @@ struct DecodeParams {
     int max_chunks;   // ceil(max_blocks * page_size / chunk)
     float *o_parts;   // [B*Hq, max_chunks, head_dim]
     float *lse_parts; // [B*Hq, max_chunks]
+    // in-place append (both NULL for plain decode): rows [B, Hkv, head_dim]
+    // written into the cache at token seq_lens[b], which the query then attends
+    const void *k_new = nullptr, *v_new = nullptr;
 };
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 

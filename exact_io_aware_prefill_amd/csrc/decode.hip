@@ -62,10 +62,28 @@ struct SplitArgs {
     const uint16_t *q, *k, *v;
     const int32_t *bt, *seq_lens;
     float *o_parts, *lse_parts;
+    // In-place append (both NULL otherwise): the new token's key/value rows
+    // [B, Hkv, D]; seq_lens then counts the tokens cached before it.
+    const uint16_t *k_new, *v_new;
     int Hq, Hkv, group, page, max_blocks, chunk, max_chunks;
     long long seq_tokens;  // tokens per sequence of the contiguous layout (= capacity)
     float scale_log2;
 };
+
+// Tokens the query attends for sequence b, and the index of the appended token
+// (-1 without append).  Lengths are clamped so nothing is read or written past
+// the sequence's capacity; with append, a full cache's new row goes to the last slot.
+__device__ __forceinline__ int attended_tokens(const SplitArgs &a, int b, int &t_new)
+{
+    const long long cap = a.seq_tokens;
+    const long long sl = a.seq_lens[b];
+    if (a.k_new) {
+        t_new = (int)max(0LL, min(sl, cap - 1));
+        return t_new + 1;
+    }
+    t_new = -1;
+    return (int)max(0LL, min(sl, cap));
+}
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
@@ -209,7 +227,9 @@ __device__ __forceinline__ void consume_step(const StepRegs<D> &s, char *slab, c
     }
 }
 
-template <int D>
+// APPEND selects the in-place append variant (a separate instantiation, so the
+// plain decode keeps its register budget).
+template <int D, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
 {
     using Gm = Geo<D>;
@@ -222,10 +242,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
     // same tokens (adjacent in memory) are requested at about the same time
     const int hk = blockIdx.x % a.Hkv, chunk = blockIdx.x / a.Hkv, b = blockIdx.y;
     // lengths outside [0, capacity] are clamped so no read leaves the sequence's cache
-    const int L = (int)max(0LL, min((long long)a.seq_lens[b], a.seq_tokens));
+    int t_new;
+    const int L = attended_tokens(a, b, t_new);
     const int t_begin = chunk * a.chunk;
     if (t_begin >= L) return;  // whole workgroup exits together: this chunk is empty
     const int t_end = min(t_begin + a.chunk, L);
+    // append: only the workgroup whose chunk holds the new token touches it
+    const bool has_new = APPEND && t_new >= t_begin && t_new < t_end;  // workgroup-uniform
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -283,6 +306,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
     // and each step waits only for its own loads.
     const int stride = kWaves * kStep;
     int tb = t_begin + wave * kStep;
+    if (APPEND && has_new) {
+        // Write the new rows into the cache slot first: this workgroup is the only
+        // reader of that slot, and its loads below are issued after the barrier,
+        // which orders them after these stores.
+        const long long row = token_index(a, b, t_new) * a.Hkv + hk;
+        const size_t src = ((size_t)b * a.Hkv + hk) * D;
+        if (tid < D / 8)
+            reinterpret_cast<uint4 *>(const_cast<uint16_t *>(a.k) + row * D)[tid] =
+                reinterpret_cast<const uint4 *>(a.k_new + src)[tid];
+        else if (tid < D / 4)
+            reinterpret_cast<uint4 *>(const_cast<uint16_t *>(a.v) + row * D)[tid - D / 8] =
+                reinterpret_cast<const uint4 *>(a.v_new + src)[tid - D / 8];
+        __syncthreads();
+    }
     StepRegs<D> r0, r1;
     issue_step<D>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
     while (tb < t_end) {
@@ -343,8 +380,9 @@ constexpr int kCombineThreads = 256;
 struct CombineArgs {
     const float *o_parts, *lse_parts;
     const int32_t *n_splits;  // explicit per-row split counts, or NULL
-    const int32_t *seq_lens;  // decode: splits = ceil(seq_lens[row / Hq] / chunk), or NULL
+    const int32_t *seq_lens;  // decode: splits = ceil(tokens / chunk), or NULL
     int Hq, chunk, max_splits, capacity;
+    int append;  // decode with append: tokens = min(seq_lens, capacity - 1) + 1
     void *o;
     int o_bf16;
     float *lse;
@@ -363,7 +401,8 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
     const int col = tid % C4, sg = tid / C4;
     int ns;
     if (a.seq_lens) {
-        const int L = max(0, min(a.seq_lens[row / a.Hq], a.capacity));
+        const int sl = a.seq_lens[row / a.Hq];
+        const int L = a.append ? max(0, min(sl, a.capacity - 1)) + 1 : max(0, min(sl, a.capacity));
         ns = (L + a.chunk - 1) / a.chunk;
     } else if (a.n_splits) {
         ns = a.n_splits[row];
@@ -473,6 +512,8 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     a.seq_lens = p.seq_lens;
     a.o_parts = p.o_parts;
     a.lse_parts = p.lse_parts;
+    a.k_new = static_cast<const uint16_t *>(p.k_new);
+    a.v_new = static_cast<const uint16_t *>(p.v_new);
     a.Hq = p.Hq;
     a.Hkv = p.Hkv;
     a.group = p.Hq / p.Hkv;
@@ -483,10 +524,18 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     a.seq_tokens = (long long)p.max_blocks * p.page_size;
     a.scale_log2 = p.scale * kLog2e;
     const dim3 grid((unsigned)((long long)p.max_chunks * p.Hkv), (unsigned)p.B);
-    if (p.head_dim == 128)
-        hipLaunchKernelGGL(decode_split_kernel<128>, grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL(decode_split_kernel<64>, grid, dim3(kThreads), 0, stream, a);
+    const bool append = a.k_new != nullptr;
+    if (p.head_dim == 128) {
+        if (append)
+            hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        if (append)
+            hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, dim3(kThreads), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -499,6 +548,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     c.chunk = p.chunk;
     c.max_splits = p.max_chunks;
     c.capacity = p.max_blocks * p.page_size;
+    c.append = p.k_new != nullptr;
     c.o = p.o;
     c.o_bf16 = 1;
     c.lse = p.lse;
@@ -517,6 +567,7 @@ hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream)
     c.chunk = 1;
     c.max_splits = p.max_splits;
     c.capacity = 0;
+    c.append = 0;
     c.o = p.o;
     c.o_bf16 = p.o_bf16 ? 1 : 0;
     c.lse = p.lse;

@@ -137,6 +137,12 @@ def decode_paged_inputs(seed: int, B: int, Hq: int, Hkv: int, d: int, page_size:
                         page_size, max_blocks, 1.0 / math.sqrt(d), dtype)
 
 
+def decode_new_rows(seed: int, B: int, Hkv: int, d: int, dtype: str = BF16):
+    """The appended token's key and value rows [B, Hkv, d] (draw order: K, then V)."""
+    rng = np.random.default_rng(seed)
+    return _draw(rng, (B, Hkv, d), dtype), _draw(rng, (B, Hkv, d), dtype)
+
+
 # --------------------------------------------------------------------------
 # Named workloads: the pages' shapes (Qwen2.5-7B attention layout for prefill
 # and single-sequence decode, Llama-3-8B layout for batched paged decode).

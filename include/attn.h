@@ -14,6 +14,9 @@
  *     workgroups, each chunk's (output, log-sum-exp) merged by a separate
  *     reduction (section "Decode: a different bottleneck"; layouts from
  *     section "Minimal implementation");
+ *   - attn_decode_append: the same decode step with the new token's key and
+ *     value written into the cache in place first (section "Minimal
+ *     implementation");
  *   - attn_lse_combine: that reduction on its own -- the combine rule for
  *     independent partials, a softmax over the partials' log-sum-exps
  *     (section "The online softmax, with every symbol defined" and the
@@ -120,6 +123,30 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim,
                 int page_size, int max_blocks_per_seq, int dtype, float scale,
                 int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_append -- attn_decode with the new token's key and value appended
+ * to the cache in place first, as the decode step of the pofe.ai page's section
+ * "Minimal implementation" does: cache_seqlens counts the tokens already cached
+ * (before the new one); the new rows are written at token cache_seqlens[b] of
+ * sequence b (slot cache_seqlens[b] % page_size of page
+ * block_table[b][cache_seqlens[b] / page_size], or row cache_seqlens[b] of a
+ * contiguous cache), and the query attends cache_seqlens[b] + 1 tokens.
+ *
+ *   k_new, v_new [batch, n_kv_heads, head_dim]  element `dtype` (read)
+ *   k_cache, v_cache: as attn_decode, written at the new token's slot only
+ *   cache_seqlens [batch] int32, read only: the caller advances it afterwards
+ *   All other arguments, the workspace and the limits are those of attn_decode.
+ *   Each cache_seqlens[b] must be below max_blocks_per_seq * page_size and the
+ *   block-table entry of the new token must name a page of the cache; a value
+ *   outside [0, capacity - 1] is clamped into it (a full cache's new row lands
+ *   in its last slot).  k_new and v_new are required (ATTN_ERR_NULL).
+ */
+int attn_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                       const int32_t *block_table, const int32_t *cache_seqlens, void *o,
+                       float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                       int page_size, int max_blocks_per_seq, int dtype, float scale, int chunk_tokens,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * attn_decode_chunk_tokens -- the chunk size attn_decode uses for these

@@ -141,6 +141,35 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, page_size: 
     return o, lse
 
 
+def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, scale: float,
+                  page_size: int, max_blocks: int):
+    """Decode step with the new token appended in place first (pofe.ai page, section
+    "Minimal implementation": the cache and block table take the new keys and values,
+    cache_seqlens counts the tokens already cached).  The new rows k_new, v_new
+    [B, Hkv, d] go to token t = cache_seqlens[b] of sequence b -- slot t % P of page
+    block_table[b][t // P], or row t of a contiguous cache -- and the query attends
+    t + 1 tokens.  t is clamped into [0, capacity - 1], the library's reading for a
+    value outside the cache.  Returns (o, lse, k_cache_after, v_cache_after) in
+    float64; the arguments are not modified."""
+    kc, vc = _f64(k_cache).copy(), _f64(v_cache).copy()
+    kn, vn = _f64(k_new), _f64(v_new)
+    sl = _i32(cache_seqlens)
+    bt = None if block_table is None else _i32(block_table)
+    cap = int(max_blocks) * int(page_size)
+    t_new = np.clip(sl.astype(np.int64), 0, cap - 1)
+    for b in range(sl.shape[0]):
+        t = int(t_new[b])
+        if bt is None:
+            kc[b, t] = kn[b]
+            vc[b, t] = vn[b]
+        else:
+            page = int(bt[b, t // page_size])
+            kc[page, t % page_size] = kn[b]
+            vc[page, t % page_size] = vn[b]
+    o, lse = decode(q, kc, vc, bt, (t_new + 1).astype(np.int32), scale, page_size, max_blocks)
+    return o, lse, kc, vc
+
+
 def split_decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, page_size: int,
                  max_blocks: int, chunk: int, block: int = 64, return_parts: bool = False):
     """The pages' split-KV decode: per-chunk online softmax, then the combine rule."""

@@ -109,6 +109,27 @@ def test_decode_argument_errors(kw, code):
     assert decode(**kw) == code
 
 
+def decode_append(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2,
+                  d=128, P_=16, maxb=8, dtype=1, chunk=0, ws=FAKE, wsb=1 << 30):
+    return attn.lib.attn_decode_append(P(q), P(kn), P(vn), P(kc), P(vc), P(bt), P(sl), P(o), P(lse), B, Hq, Hkv,
+                                       d, P_, maxb, dtype, 0.1, chunk, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=0), attn.ATTN_ERR_NULL),
+    (dict(vn=0), attn.ATTN_ERR_NULL),
+    (dict(q=0), attn.ATTN_ERR_NULL),
+    (dict(kn=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(vn=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(B=-1, kn=0), attn.ATTN_ERR_SHAPE),        # shape errors come before pointer checks
+    (dict(d=80, kn=0), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=0), attn.ATTN_ERR_WORKSPACE),
+    (dict(B=0, q=0, kn=0, vn=0, kc=0, vc=0, bt=0, sl=0, o=0, ws=0), attn.ATTN_OK),
+])
+def test_decode_append_argument_errors(kw, code):
+    assert decode_append(**kw) == code
+
+
 def test_decode_contiguous_accepts_any_page_size_for_capacity():
     # page_size only fixes capacity when block_table is NULL; with a NULL workspace the
     # host check stops at ERR_WORKSPACE, i.e. after the page-size checks passed

@@ -232,3 +232,52 @@ def test_prefill_unusual_scales(attn, scale, dtype):
     grow = max(1.0, abs(scale) * math.sqrt(128))
     base = BF16_TOL if dtype == W.BF16 else F32_TOL
     check("scale=%g" % scale, o, lse, ro, rl, {k_: v_ * grow for k_, v_ in base.items()})
+
+
+# ------------------------------------------------------------------ decode with append
+APPEND_LENS = [0, 1, 15, 16, 17, 255, 511, 512, 1023]  # tokens cached before the new one
+
+
+@pytest.mark.parametrize("g", [1, 7])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("chunk", [16, 512, 0])
+def test_decode_append(attn, g, d, paged, chunk):
+    """The new token's rows go into the cache in place (only its slot changes, bit for
+    bit) and the query attends the cached tokens plus the new one."""
+    say("case: decode append g=%d d=%d paged=%s chunk=%d" % (g, d, paged, chunk))
+    Hkv, cap, B = 2, 1024, len(APPEND_LENS)
+    seed = 700 + g + d + chunk
+    if paged:  # pages for the cached tokens and the new one
+        x = W.decode_paged_inputs(seed, B, g * Hkv, Hkv, d, 16, 1, cap, lengths=[L + 1 for L in APPEND_LENS])
+    else:
+        x = W.decode_contiguous_inputs(seed, B, g * Hkv, Hkv, cap, d, seq_lens=APPEND_LENS)
+    cached = torch.tensor(APPEND_LENS, dtype=torch.int32)
+    kn, vn = W.decode_new_rows(seed + 1, B, Hkv, d)
+    kc, vc, sl = dev(x.k_cache), dev(x.v_cache), dev(cached)
+    o, lse = attn.decode_append(dev(x.q), dev(kn), dev(vn), kc, vc, dev(x.block_table), sl, x.page_size,
+                                x.max_blocks, x.scale, chunk)
+    torch.cuda.synchronize()
+    ro, rl, rk, rv = oracle.decode_append(x.q, kn, vn, x.k_cache, x.v_cache, x.block_table, cached, x.scale,
+                                          x.page_size, x.max_blocks)
+    check("append g=%d d=%d paged=%d chunk=%d" % (g, d, paged, chunk), o, lse, ro, rl, BF16_TOL)
+    assert np.array_equal(kc.cpu().double().numpy(), rk), "K cache after the append differs"
+    assert np.array_equal(vc.cpu().double().numpy(), rv), "V cache after the append differs"
+    assert torch.equal(sl.cpu(), cached), "cache_seqlens must be left to the caller"
+
+
+def test_decode_append_full_cache_uses_last_slot(attn):
+    """A length at or past the capacity is clamped: the new rows replace the last slot."""
+    say("case: decode append into a full cache")
+    lens = [64, 500, 63]
+    x = W.decode_contiguous_inputs(41, 3, 8, 2, 64, 128, seq_lens=[64, 64, 63])
+    cached = torch.tensor(lens, dtype=torch.int32)
+    kn, vn = W.decode_new_rows(42, 3, 2, 128)
+    kc, vc = dev(x.k_cache), dev(x.v_cache)
+    o, lse = attn.decode_append(dev(x.q), dev(kn), dev(vn), kc, vc, None, dev(cached), x.page_size, x.max_blocks,
+                                x.scale, 16)
+    torch.cuda.synchronize()
+    ro, rl, rk, rv = oracle.decode_append(x.q, kn, vn, x.k_cache, x.v_cache, None, cached, x.scale, x.page_size,
+                                          x.max_blocks)
+    check("append full cache", o, lse, ro, rl, BF16_TOL)
+    assert np.array_equal(kc.cpu().double().numpy(), rk) and np.array_equal(vc.cpu().double().numpy(), rv)

@@ -428,3 +428,65 @@ def test_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.decode(np.zeros((1, 2, 4)), np.zeros((1, 16, 1, 4)), np.zeros((1, 16, 1, 4)), None,
                       np.array([17], dtype=np.int32), 1.0, 16, 1)
+
+
+# ---------------------------------------------------------------------------
+# Decode with in-place append (pofe.ai page, section "Minimal implementation")
+# ---------------------------------------------------------------------------
+def test_append_into_empty_cache_is_the_new_token_alone():
+    """With nothing cached, the query sees only the new key: the softmax has one
+    term, so O = v_new and LSE = scale * <q, k_new> (closed form)."""
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, d, P, nb = 2, 4, 2, 8, 16, 3
+    q = rng.standard_normal((B, Hq, d))
+    kn = rng.standard_normal((B, Hkv, d)); vn = rng.standard_normal((B, Hkv, d))
+    kc = rng.standard_normal((B, nb * P, Hkv, d)); vc = rng.standard_normal((B, nb * P, Hkv, d))
+    o, lse, kc2, vc2 = oracle.decode_append(q, kn, vn, kc, vc, None, np.zeros(B, np.int32), 0.3, P, nb)
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            assert np.array_equal(o[b, h], vn[b, h // g])
+            assert abs(lse[b, h] - 0.3 * float(q[b, h] @ kn[b, h // g])) < 1e-12
+    assert np.array_equal(kc2[:, 0], kn) and np.array_equal(vc2[:, 0], vn)
+
+
+def test_append_of_a_cached_row_equals_decode_of_one_more_token():
+    """Appending the row the cache already holds at position L changes no data, so
+    the result is plain decode over L + 1 tokens, bit for bit, and the cache is
+    unchanged; paged and contiguous layouts, including page boundaries."""
+    rng = np.random.default_rng(32)
+    B, Hq, Hkv, d, P = 4, 6, 3, 16, 16
+    S = 80
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, S, d)); v = rng.standard_normal((B, Hkv, S, d))
+    kc, vc = _to_cache(k), _to_cache(v)
+    lens = np.array([0, 15, 16, 63], dtype=np.int32)
+    kn = np.stack([kc[b, lens[b]] for b in range(B)]); vn = np.stack([vc[b, lens[b]] for b in range(B)])
+    o, lse, kc2, vc2 = oracle.decode_append(q, kn, vn, kc, vc, None, lens, 0.25, P, S // P)
+    ro, rl = oracle.decode(q, kc, vc, None, lens + 1, 0.25, P, S // P)
+    assert np.array_equal(o, ro) and np.array_equal(lse, rl)
+    assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc)
+    # the same through a permuted page pool
+    kp, bt = _page(kc, lens + 1, P, np.random.default_rng(5))
+    vp, _ = _page(vc, lens + 1, P, np.random.default_rng(5))
+    o3, lse3, kp2, vp2 = oracle.decode_append(q, kn, vn, kp, vp, bt, lens, 0.25, P, bt.shape[1])
+    assert np.array_equal(o3, ro) and np.array_equal(lse3, rl)
+    assert np.array_equal(kp2, kp) and np.array_equal(vp2, vp)
+
+
+def test_append_writes_only_the_new_slot():
+    """The new rows land at token L (page bt[b][L // P], slot L % P) and nowhere else;
+    a length at or past the capacity puts them in the last slot."""
+    rng = np.random.default_rng(33)
+    B, Hq, Hkv, d, P, nb = 3, 2, 2, 4, 16, 2
+    pool = 7
+    kp = rng.standard_normal((pool, P, Hkv, d)); vp = rng.standard_normal((pool, P, Hkv, d))
+    bt = np.array([[3, 5], [0, 6], [2, 1]], dtype=np.int32)
+    lens = np.array([17, 5, 99], dtype=np.int32)  # the last is past the capacity 32
+    kn = rng.standard_normal((B, Hkv, d)); vn = rng.standard_normal((B, Hkv, d))
+    q = rng.standard_normal((B, Hq, d))
+    _, _, kp2, vp2 = oracle.decode_append(q, kn, vn, kp, vp, bt, lens, 1.0, P, nb)
+    expect_k, expect_v = kp.copy(), vp.copy()
+    for b, (page, slot) in enumerate([(5, 1), (0, 5), (1, 15)]):
+        expect_k[page, slot] = kn[b]; expect_v[page, slot] = vn[b]
+    assert np.array_equal(kp2, expect_k) and np.array_equal(vp2, expect_v)
