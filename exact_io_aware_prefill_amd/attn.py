@@ -30,13 +30,15 @@ ATTN_ERR_HIP = -7
 ATTN_F32 = 0
 ATTN_BF16 = 1
 
-EXPORTS = ("attn_prefill", "attn_decode", "attn_decode_append", "attn_decode_chunk_tokens",
+EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_decode", "attn_decode_append", "attn_decode_chunk_tokens",
            "attn_decode_workspace_bytes", "attn_lse_combine", "attn_status_string")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 lib.attn_prefill.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 lib.attn_prefill.restype = _I
+lib.attn_prefill_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+lib.attn_prefill_varlen.restype = _I
 lib.attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                             _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode.restype = _I
@@ -93,6 +95,18 @@ def attn_prefill(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> No
     rc = lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, N, Hq, k.shape[1], d,
                           _dtype_code(q), int(bool(causal)), float(scale), _stream(stream))
     _check(rc, "attn_prefill")
+
+
+def attn_prefill_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, causal: bool, scale: float,
+                        stream=None) -> None:
+    """Packed batch: q, o [T, Hq, d]; k, v [T, Hkv, d]; lse [Hq, T] float32; cu_seqlens
+    [B+1] int32 on the GPU; max_seqlen >= every sequence length.  Writes o and lse."""
+    T, Hq, d = q.shape
+    B = cu_seqlens.numel() - 1
+    rc = lib.attn_prefill_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), B,
+                                 int(max_seqlen), T, Hq, k.shape[1], d, _dtype_code(q), int(bool(causal)),
+                                 float(scale), _stream(stream))
+    _check(rc, "attn_prefill_varlen")
 
 
 def attn_decode_chunk_tokens(batch: int, n_kv_heads: int, page_size: int, max_blocks_per_seq: int,
@@ -156,6 +170,16 @@ def prefill(q, k, v, causal: bool = True, scale: float | None = None, stream=Non
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     attn_prefill(q, k, v, o, lse, causal, d ** -0.5 if scale is None else scale, stream)
+    return o, lse
+
+
+def prefill_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, scale: float | None = None,
+                   stream=None):
+    T, Hq, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    attn_prefill_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, d ** -0.5 if scale is None else scale,
+                        stream)
     return o, lse
 
 

@@ -136,13 +136,49 @@ int attn_prefill(const void *q, const void *k, const void *v, void *o, float *ls
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
         return ATTN_ERR_ALIGN;
     // element offsets are formed in 64-bit; the grid is one dimension of query tiles
-    if ((long long)batch * n_q_heads * ((seqlen + 63) / 64) > INT_MAX) return ATTN_ERR_UNSUPPORTED;
+    // and one head's rows are addressed through a descriptor with a 32-bit range
+    if ((long long)batch * n_q_heads * ((seqlen + 63) / 64) > INT_MAX ||
+        ((long long)seqlen + 255) * head_dim * 2 > 0xffffffffLL)
+        return ATTN_ERR_UNSUPPORTED;
 
     attn::PrefillParams p;
     p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
     p.B = batch; p.N = seqlen; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
     p.causal = causal ? 1 : 0;
     p.scale = scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == ATTN_BF16) return run([&] { return attn::launch_prefill_bf16(p, s); });
+    return run([&] { return attn::launch_prefill_f32(p, s); });
+}
+
+int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *cu_seqlens, int batch, int max_seqlen, int total_tokens,
+                        int n_q_heads, int n_kv_heads, int head_dim, int dtype, int causal, float scale,
+                        void *stream)
+{
+    if (batch < 0 || max_seqlen < 0 || total_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
+        return ATTN_ERR_SHAPE;
+    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
+    if (!head_dim_ok(head_dim) || (dtype != ATTN_F32 && dtype != ATTN_BF16))
+        return ATTN_ERR_UNSUPPORTED;
+    if (batch == 0 || max_seqlen == 0 || total_tokens == 0) return ATTN_OK;
+    if (!q || !k || !v || !o || !lse || !cu_seqlens) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+        return ATTN_ERR_ALIGN;
+    // one sequence's rows of one head span (max_seqlen rounded up to a tile) rows
+    // of n_q_heads * head_dim elements, addressed with a 32-bit range
+    if ((long long)batch * n_q_heads * ((max_seqlen + 63) / 64) > INT_MAX ||
+        ((long long)max_seqlen + 255) * n_q_heads * head_dim * (dtype == ATTN_F32 ? 4 : 2) > 0xffffffffLL)
+        return ATTN_ERR_UNSUPPORTED;
+
+    attn::PrefillParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    p.B = batch; p.N = max_seqlen; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
+    p.causal = causal ? 1 : 0;
+    p.scale = scale;
+    p.cu_seqlens = cu_seqlens;
+    p.total = total_tokens;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (dtype == ATTN_BF16) return run([&] { return attn::launch_prefill_bf16(p, s); });
     return run([&] { return attn::launch_prefill_f32(p, s); });

@@ -15,6 +15,11 @@ struct PrefillParams {
     float *lse;
     int B, N, Hq, Hkv, head_dim, causal;
     float scale;
+    // packed variable-length batch (NULL: padded [B, H, N, d]): sequence b is
+    // tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of [total, H, d] tensors, lse is
+    // [Hq, total], and N is the longest sequence
+    const int32_t *cu_seqlens = nullptr;
+    int total = 0;
 };
 hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream);
 

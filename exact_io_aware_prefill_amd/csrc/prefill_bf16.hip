@@ -84,11 +84,21 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kMaxLaneSum = 256.f;            // a lane's tile sum above this redoes the tile
 constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer, 32-bit data format
 
+// Two layouts share the kernel.  Padded batch: q, o [B, Hq, N, d], k, v
+// [B, Hkv, N, d], lse [B, Hq, N] (cu_seqlens NULL).  Packed variable-length
+// batch: sequence b owns tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, o
+// [T, Hq, d], k, v [T, Hkv, d] and lse [Hq, T].  Row r of head h of sequence b
+// sits at base + b_off + h * head + r * row (in elements) with the strides below.
 struct Args {
     const uint16_t *q, *k, *v;
     uint16_t *o;
     float *lse;
+    const int32_t *cu_seqlens;  // packed layout, or NULL
     int B, N, Hq, Hkv, group, causal, n_qtiles, n_items;
+    int T;                      // packed: total tokens
+    long long q_head, q_row;    // strides of q and o (elements)
+    long long kv_head, kv_row;  // strides of k and v
+    long long lse_head;         // stride of lse between heads (rows are adjacent)
     int negate_q;      // 1 when the caller's scale is negative
     float scale_log2;  // |scale| * log2(e)
     float scale;       // |scale|
@@ -122,34 +132,39 @@ template <int D>
 struct TileLoader {
     static constexpr int RB = D * 2;                 // bytes per key row
     static constexpr int NC = D / 8;                 // 16-byte chunks per row
+    static constexpr int RPI = 64 / NC;              // key rows per instruction
     static constexpr int INSTR = kBlockN * NC / 64;  // wave instructions per tile
     static constexpr int PER_WAVE = (INSTR + kWaves - 1) / kWaves;
     static_assert(INSTR % kWaves == 0 || INSTR < kWaves, "tile instructions split evenly over the waves");
     // a lane's instructions fill rows 4*kWaves apart (D = 128) or 8*kWaves apart
     // (D = 64); with kWaves a multiple of 4 those rows share their permutation
     static_assert(kWaves % 4 == 0, "one per-lane offset needs kWaves to be a multiple of 4");
-    uint32_t voff;  // per-lane byte offset inside the 1 KiB an instruction fills
+    uint32_t voff;  // per-lane byte offset from the first row an instruction fills
+    uint32_t rowb;  // bytes between consecutive key rows in memory
 
     template <typename Swz>
-    __device__ __forceinline__ void init(int wave, int lane, Swz swz)
+    __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes, Swz swz)
     {
         const int u = wave * 64 + lane;  // LDS slot of this lane in its first instruction
         const int r = u / NC, pos = u % NC;
-        voff = (uint32_t)((r * RB) % 1024 + 16 * (pos ^ swz(r)));
+        rowb = row_bytes;
+        voff = (uint32_t)(lane / NC) * row_bytes + 16u * (uint32_t)(pos ^ swz(r));
     }
-    // Issue the loads of the tile starting at key k0 of one head (`bytes` long)
-    // into the LDS tile `dst`.  Each instruction's descriptor starts at its own
-    // 1 KiB and ends at the head's end, so rows past N read as zero.
-    __device__ __forceinline__ void load(const uint16_t *head, uint32_t bytes, int k0, int wave, uint16_t *dst) const
+    // Issue the loads of the tile starting at key k0 of one head (rows rowb apart,
+    // n rows) into the LDS tile `dst`.  Each instruction's descriptor starts at its
+    // own first row and ends at row n, so rows past n read as zero.
+    __device__ __forceinline__ void load(const uint16_t *head, int n, int k0, int wave, uint16_t *dst) const
     {
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int ins = wave + i * kWaves;
             if (INSTR < kWaves && ins >= INSTR) break;  // wave-uniform
-            const uint32_t skip = (uint32_t)k0 * RB + (uint32_t)ins * 1024u;
+            const int row0 = k0 + ins * RPI;
+            const long long left = (long long)max(n - row0, 0) * rowb;
             // readfirstlane keeps the descriptor in scalar registers
-            const uint32_t left = __builtin_amdgcn_readfirstlane(bytes > skip ? bytes - skip : 0u);
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char *>(head) + skip, left);
+            const uint32_t rec = __builtin_amdgcn_readfirstlane((uint32_t)min(left, 0xFFFFFFFFLL));
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(reinterpret_cast<const char *>(head) + (long long)row0 * rowb, rec);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)((char *)dst + ins * 1024), 16, voff, 0, 0, 0);
         }
     }
@@ -256,12 +271,32 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
     const int b = bg / a.Hkv, hk = bg % a.Hkv;
     const int h = hk * a.group + j;
     const int qtile = (r & 1) ? (r >> 1) : a.n_qtiles - 1 - (r >> 1);
-    const int bh = b * a.Hq + h;
     const int q0 = qtile * kBM;
-    const uint32_t head_bytes = (uint32_t)a.N * D * 2u;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + (size_t)bh * a.N * D, head_bytes);
-    const uint16_t *const kh = a.k + (size_t)(b * a.Hkv + hk) * a.N * D;
-    const uint16_t *const vh = a.v + (size_t)(b * a.Hkv + hk) * a.N * D;
+    // this sequence's first token and length
+    long long tok0;
+    int N;
+    if (a.cu_seqlens) {
+        // offsets outside [0, T] or a length above the launch's maximum are
+        // clamped, so nothing outside the packed tensors is touched
+        const int s0 = min(max(a.cu_seqlens[b], 0), a.T);
+        const int s1 = min(max(a.cu_seqlens[b + 1], s0), a.T);
+        tok0 = s0;
+        N = min(s1 - s0, a.N);
+    } else {
+        tok0 = (long long)b * a.N;
+        N = a.N;
+    }
+    if (q0 >= N) return;  // whole workgroup: no query row of this tile exists
+    // element offsets of this (sequence, head): packed rows are token-major
+    const long long qo = a.cu_seqlens ? tok0 * a.Hq * D + (long long)h * a.q_head
+                                      : ((long long)b * a.Hq + h) * a.q_head;
+    const long long kvo = a.cu_seqlens ? tok0 * a.Hkv * D + (long long)hk * a.kv_head
+                                       : ((long long)b * a.Hkv + hk) * a.kv_head;
+    const long long lse_off = a.cu_seqlens ? (long long)h * a.lse_head + tok0 : ((long long)b * a.Hq + h) * a.lse_head;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(a.q + qo, (uint32_t)min((long long)N * a.q_row * 2, 0xFFFFFFFFLL));
+    const uint16_t *const kh = a.k + kvo;
+    const uint16_t *const vh = a.v + kvo;
 
     const int wrow0 = q0 + wave * (kBlocks * 32);  // first query row of this wave
     // Q fragments (B operand of S^T = K Q^T), resident for the whole kernel;
@@ -271,7 +306,7 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
     for (int bb = 0; bb < kBlocks; ++bb)
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-            uint4 u = bload16(rq, (uint32_t)((wrow0 + 32 * bb + l32) * D + 16 * s + 8 * hh) * 2u, 0);
+            uint4 u = bload16(rq, (uint32_t)(((long long)(wrow0 + 32 * bb + l32) * a.q_row + 16 * s + 8 * hh) * 2), 0);
             if (a.negate_q) {  // scale < 0: s*scale = (-s)*|scale|, so the max stays on raw scores
                 u.x ^= 0x80008000u; u.y ^= 0x80008000u; u.z ^= 0x80008000u; u.w ^= 0x80008000u;
             }
@@ -295,8 +330,8 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
     const int xlane = (lane ^ 32) << 2;  // ds_bpermute address of the other half-wave
 
     TileLoader<D> kld, vld;
-    kld.init(wave, lane, [](int rr) { return k_swz<D>(rr); });
-    vld.init(wave, lane, [](int rr) { return v_swz<D>(rr); });
+    kld.init(wave, lane, (uint32_t)(a.kv_row * 2), [](int rr) { return k_swz<D>(rr); });
+    vld.init(wave, lane, (uint32_t)(a.kv_row * 2), [](int rr) { return v_swz<D>(rr); });
     const uint32_t kad = (uint32_t)(l32 * 2 * D + 16 * (hh ^ k_swz<D>(l32)));
     uint32_t vad;
     {
@@ -306,7 +341,7 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
         vad = (uint32_t)(row * 2 * D + 16 * (c ^ v_swz<D>(row)) + 8 * (q & 1));
     }
 
-    const int kend = a.causal ? min(a.N, q0 + kBM) : a.N;  // keys this tile may see
+    const int kend = a.causal ? min(N, q0 + kBM) : N;  // keys this tile may see
     const int ntiles = (kend + kBlockN - 1) / kBlockN;
 
     // ---- prologue ------------------------------------------------------------------
@@ -316,8 +351,8 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
         reinterpret_cast<uint4 *>(VB0)[i] = make_uint4(0, 0, 0, 0);
         reinterpret_cast<uint4 *>(VB1)[i] = make_uint4(0, 0, 0, 0);
     }
-    kld.load(kh, head_bytes, 0, wave, KB0);
-    if (ntiles > 1) kld.load(kh, head_bytes, kBlockN, wave, KB1);
+    kld.load(kh, N, 0, wave, KB0);
+    if (ntiles > 1) kld.load(kh, N, kBlockN, wave, KB1);
     wait_loads();
     __syncthreads();
     f32x16_t S[kBlocks][kKB];
@@ -337,14 +372,14 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
     auto step = [&](bf16x8_t (&Pp)[kBlocks][kKS], bf16x8_t (&Pc)[kBlocks][kKS], int t, const uint16_t *Kn,
                     const uint16_t *Vp, uint16_t *Kw, uint16_t *Vw) {
         const int k0 = t * kBlockN;
-        if (t + 2 < ntiles) kld.load(kh, head_bytes, k0 + 2 * kBlockN, wave, Kw);
-        vld.load(vh, head_bytes, k0, wave, Vw);
+        if (t + 2 < ntiles) kld.load(kh, N, k0 + 2 * kBlockN, wave, Kw);
+        vld.load(vh, N, k0, wave, Vw);
         // diagonal / ragged tile: mask keys past the row (causal) or past N
-        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > a.N) {
+        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > N) {
 #pragma unroll
             for (int bb = 0; bb < kBlocks; ++bb) {
                 const int qrow = wrow0 + 32 * bb + l32;
-                const int lim = (a.causal ? min(qrow, a.N - 1) : a.N - 1) - (k0 + 4 * hh);
+                const int lim = (a.causal ? min(qrow, N - 1) : N - 1) - (k0 + 4 * hh);
 #pragma unroll
                 for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
@@ -436,9 +471,9 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
         const int qrow = wrow0 + 32 * bb + l32;
         const float lt =
             l[bb] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, l[bb])));
-        if (qrow < a.N) {
+        if (qrow < N) {
             const float inv = 1.f / lt;
-            uint16_t *orow = a.o + ((size_t)bh * a.N + qrow) * D;
+            uint16_t *orow = a.o + qo + (long long)qrow * a.q_row;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -452,7 +487,7 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
                     *reinterpret_cast<uint2 *>(orow + d0) = pk;
                 }
             }
-            if (hh == 0) a.lse[(size_t)bh * a.N + qrow] = m[bb] * a.scale + log2f(lt) * kLn2;
+            if (hh == 0) a.lse[lse_off + qrow] = m[bb] * a.scale + log2f(lt) * kLn2;
         }
     }
 }
@@ -467,8 +502,21 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     a.v = static_cast<const uint16_t *>(p.v);
     a.o = static_cast<uint16_t *>(p.o);
     a.lse = p.lse;
+    a.cu_seqlens = p.cu_seqlens;
     a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.group = p.Hq / p.Hkv;
     a.causal = p.causal;
+    const long long D = p.head_dim;
+    if (p.cu_seqlens) {  // packed [T, H, d]; lse [Hq, T]; N is the longest sequence
+        a.T = p.total;
+        a.q_head = D; a.q_row = (long long)p.Hq * D;
+        a.kv_head = D; a.kv_row = (long long)p.Hkv * D;
+        a.lse_head = p.total;
+    } else {  // padded [B, H, N, d]; lse [B, Hq, N]
+        a.T = p.B * p.N;
+        a.q_head = (long long)p.N * D; a.q_row = D;
+        a.kv_head = (long long)p.N * D; a.kv_row = D;
+        a.lse_head = p.N;
+    }
     a.n_qtiles = (p.N + kBM - 1) / kBM;
     a.negate_q = p.scale < 0.f ? 1 : 0;
     // |scale| below 1e-30 is raised to 1e-30: every probability still rounds to
@@ -478,8 +526,9 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     const long long items = (long long)a.n_qtiles * p.B * p.Hq;
     if (items == 0) return hipSuccess;
     if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-    // per-head byte offsets, including the padded last query tile, must fit 32 bits
-    if ((long long)a.n_qtiles * kBM * p.head_dim * 2 > 0xffffffffLL) return hipErrorInvalidValue;
+    // per-head byte ranges, including the padded last query tile, must fit 32 bits
+    const long long rows = (long long)a.n_qtiles * kBM;
+    if (rows * a.q_row * 2 > 0xffffffffLL || rows * a.kv_row * 2 > 0xffffffffLL) return hipErrorInvalidValue;
     a.n_items = (int)items;
     if (p.head_dim == 128)
         hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)items), dim3(kWaves * 64), 0, stream, a);

@@ -18,10 +18,14 @@ namespace {
 constexpr int kRows = 64;  // query rows per workgroup (one wave)
 constexpr int kKeys = 32;  // keys per tile
 
+// Padded batch: q, o [B, Hq, N, d], k, v [B, Hkv, N, d], lse [B, Hq, N]
+// (cu_seqlens NULL).  Packed variable-length batch: sequence b is tokens
+// cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, o [T, Hq, d], k, v [T, Hkv, d], lse [Hq, T].
 struct Args {
     const float *q, *k, *v;
     float *o, *lse;
-    int B, N, Hq, Hkv, group, causal, n_qtiles;
+    const int32_t *cu_seqlens;
+    int B, N, Hq, Hkv, group, causal, n_qtiles, T;
     float scale;
 };
 
@@ -38,26 +42,47 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
     const int b = bh / a.Hq, h = bh % a.Hq, hk = h / a.group;
     const int q0 = qtile * kRows;
     const int qrow = q0 + tid;
-    const float *kp = a.k + (size_t)(b * a.Hkv + hk) * a.N * D;
-    const float *vp = a.v + (size_t)(b * a.Hkv + hk) * a.N * D;
+    // this sequence's rows: first element of row 0 and the stride between rows
+    int N;
+    size_t qbase, kvbase, qstride, kvstride, lsebase;
+    if (a.cu_seqlens) {  // offsets outside [0, T] and lengths above N are clamped
+        const int s0 = min(max(a.cu_seqlens[b], 0), a.T);
+        const int s1 = min(max(a.cu_seqlens[b + 1], s0), a.T);
+        N = min(s1 - s0, a.N);
+        qbase = ((size_t)s0 * a.Hq + h) * D;
+        kvbase = ((size_t)s0 * a.Hkv + hk) * D;
+        qstride = (size_t)a.Hq * D;
+        kvstride = (size_t)a.Hkv * D;
+        lsebase = (size_t)h * a.T + s0;
+    } else {
+        N = a.N;
+        qbase = (size_t)bh * a.N * D;
+        kvbase = (size_t)(b * a.Hkv + hk) * a.N * D;
+        qstride = D;
+        kvstride = D;
+        lsebase = (size_t)bh * a.N;
+    }
+    if (q0 >= N) return;  // whole workgroup: no query row of this tile exists
+    const float *kp = a.k + kvbase;
+    const float *vp = a.v + kvbase;
 
     float q[D], acc[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-        q[d] = (qrow < a.N) ? a.q[((size_t)bh * a.N + qrow) * D + d] : 0.f;
+        q[d] = (qrow < N) ? a.q[qbase + (size_t)qrow * qstride + d] : 0.f;
         acc[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
 
-    const int kend = a.causal ? min(a.N, q0 + kRows) : a.N;
+    const int kend = a.causal ? min(N, q0 + kRows) : N;
     for (int k0 = 0; k0 < kend; k0 += kKeys) {
         __syncthreads();
         for (int idx = tid; idx < kKeys * D / 4; idx += kRows) {
             const int r = idx / (D / 4), c = idx % (D / 4);
             float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-            if (k0 + r < a.N) {
-                kv = *reinterpret_cast<const float4 *>(kp + (size_t)(k0 + r) * D + 4 * c);
-                vv = *reinterpret_cast<const float4 *>(vp + (size_t)(k0 + r) * D + 4 * c);
+            if (k0 + r < N) {
+                kv = *reinterpret_cast<const float4 *>(kp + (size_t)(k0 + r) * kvstride + 4 * c);
+                vv = *reinterpret_cast<const float4 *>(vp + (size_t)(k0 + r) * kvstride + 4 * c);
             }
             *reinterpret_cast<float4 *>(&Ks[r * D + 4 * c]) = kv;
             *reinterpret_cast<float4 *>(&Vs[r * D + 4 * c]) = vv;
@@ -73,7 +98,7 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
             for (int d = 0; d < D; ++d) dot = fmaf(q[d], Ks[t * D + d], dot);
             float x = dot * a.scale;
             const int key = k0 + t;
-            if (key >= a.N || (a.causal && key > qrow)) x = -INFINITY;
+            if (key >= N || (a.causal && key > qrow)) x = -INFINITY;
             s[t] = x;
             mx = fmaxf(mx, x);
         }
@@ -93,17 +118,17 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
         m = m_new;
     }
 
-    if (qrow < a.N) {
-        float *orow = a.o + ((size_t)bh * a.N + qrow) * D;
+    if (qrow < N) {
+        float *orow = a.o + qbase + (size_t)qrow * qstride;
         if (l > 0.f) {
             const float inv = 1.f / l;
 #pragma unroll
             for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
-            a.lse[(size_t)bh * a.N + qrow] = m + logf(l);
+            a.lse[lsebase + qrow] = m + logf(l);
         } else {  // no visible key (not reachable for square causal or full attention)
 #pragma unroll
             for (int d = 0; d < D; ++d) orow[d] = 0.f;
-            a.lse[(size_t)bh * a.N + qrow] = -INFINITY;
+            a.lse[lsebase + qrow] = -INFINITY;
         }
     }
 }
@@ -118,7 +143,9 @@ hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream)
     a.v = static_cast<const float *>(p.v);
     a.o = static_cast<float *>(p.o);
     a.lse = p.lse;
+    a.cu_seqlens = p.cu_seqlens;
     a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.group = p.Hq / p.Hkv;
+    a.T = p.cu_seqlens ? p.total : p.B * p.N;
     a.causal = p.causal;
     a.n_qtiles = (p.N + kRows - 1) / kRows;
     a.scale = p.scale;

@@ -67,6 +67,32 @@ def prefill_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, dtype: 
     return PrefillInputs(q, k, v, causal, 1.0 / math.sqrt(d) if scale is None else scale, dtype)
 
 
+@dataclass
+class PackedPrefillInputs:
+    q: torch.Tensor           # [T, Hq, d]
+    k: torch.Tensor           # [T, Hkv, d]
+    v: torch.Tensor
+    cu_seqlens: torch.Tensor  # [B + 1] int32
+    max_seqlen: int
+    causal: bool
+    scale: float
+    dtype: str
+
+
+def prefill_packed_inputs(seed: int, lens, Hq: int, Hkv: int, d: int, dtype: str, causal: bool = True,
+                          scale: Optional[float] = None) -> PackedPrefillInputs:
+    """A packed batch of sequences with the given lengths (draw order: Q, K, V)."""
+    lens = [int(x) for x in lens]
+    T = sum(lens)
+    rng = np.random.default_rng(seed)
+    q = _draw(rng, (T, Hq, d), dtype)
+    k = _draw(rng, (T, Hkv, d), dtype)
+    v = _draw(rng, (T, Hkv, d), dtype)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    return PackedPrefillInputs(q, k, v, cu, max(lens) if lens else 0, causal,
+                               1.0 / math.sqrt(d) if scale is None else scale, dtype)
+
+
 def worked_example_inputs(d: int = 64) -> PrefillInputs:
     """The pofe.ai worked example (section "A worked example by hand": scores
     (2, 1, 4, 3), scalar values (1, 0, 2, -1)) embedded in a 4-token causal

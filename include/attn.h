@@ -9,6 +9,8 @@
  *     the row log-sum-exp is written out (sections "The online softmax, with
  *     every symbol defined" and "Prefill: tiles, loop order and the tensor
  *     cores");
+ *   - attn_prefill_varlen: the same over a packed batch of sequences of
+ *     different lengths (cumulative offsets, no padding);
  *   - attn_decode: one query token per sequence against a paged (or
  *     contiguous) KV cache, the keys split into chunks processed by separate
  *     workgroups, each chunk's (output, log-sum-exp) merged by a separate
@@ -80,11 +82,37 @@ extern "C" {
  *   head_dim in {64, 128}; dtype ATTN_BF16 (matrix cores, bf16 products with
  *   float32 accumulation; P is rounded to bf16 before the P*V product; O is
  *   rounded to nearest even) or ATTN_F32 (float32 arithmetic throughout).
- *   batch, seqlen >= 0 (an empty call does nothing); heads >= 1.
+ *   batch, seqlen >= 0 (an empty call does nothing); heads >= 1;
+ *   (seqlen + 255) * head_dim * 2 >= 2^32 is ATTN_ERR_UNSUPPORTED.
  */
 int attn_prefill(const void *q, const void *k, const void *v, void *o, float *lse,
                  int batch, int seqlen, int n_q_heads, int n_kv_heads, int head_dim,
                  int dtype, int causal, float scale, void *stream);
+
+/*
+ * attn_prefill_varlen -- attn_prefill over a packed batch of sequences of
+ * different lengths, without padding: engines batch prompts this way through
+ * a variable-length interface (pofe.ai page, section "Interaction with
+ * post-trained models").  Sequence b owns tokens cu_seqlens[b] ..
+ * cu_seqlens[b+1]-1; each sequence attends only to itself (causal within it).
+ *
+ *   q, o  [total_tokens, n_q_heads,  head_dim]  element type `dtype`
+ *   k, v  [total_tokens, n_kv_heads, head_dim]  element type `dtype`
+ *   lse   [n_q_heads, total_tokens] float32 (written; required)
+ *   cu_seqlens [batch + 1] int32 on the device: cu_seqlens[0] = 0, nondecreasing,
+ *         cu_seqlens[batch] = total_tokens (4-byte aligned)
+ *   max_seqlen >= every cu_seqlens[b+1] - cu_seqlens[b]; it sizes the launch.
+ *   The device-side offsets are the caller's responsibility; an offset outside
+ *   [0, total_tokens] or a length above max_seqlen is clamped (nothing outside the
+ *   tensors is touched, but those rows are not computed as intended).
+ *   dtype, head_dim, causal and scale as attn_prefill; same element arithmetic.
+ *   Larger than (max_seqlen + 255) * n_q_heads * head_dim * element size >= 2^32 is
+ *   ATTN_ERR_UNSUPPORTED.  batch, max_seqlen or total_tokens of 0 does nothing.
+ */
+int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                        const int32_t *cu_seqlens, int batch, int max_seqlen, int total_tokens,
+                        int n_q_heads, int n_kv_heads, int head_dim, int dtype, int causal, float scale,
+                        void *stream);
 
 /*
  * attn_decode -- one new query token per sequence against a KV cache, by

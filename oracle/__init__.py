@@ -108,6 +108,28 @@ def prefill(q, k, v, causal: bool, scale: float, row_step: int = 1):
     return o, lse
 
 
+def prefill_varlen(q, k, v, cu_seqlens, causal: bool, scale: float):
+    """Prefill of a packed batch without padding (the variable-length interface of the
+    pofe.ai page, section "Interaction with post-trained models"): sequence b is tokens
+    cu_seqlens[b] .. cu_seqlens[b+1]-1 of q [T, Hq, d], k, v [T, Hkv, d] and attends
+    only to itself; each sequence is the plain prefill above.  Returns (o [T, Hq, d],
+    lse [Hq, T]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = _i32(cu_seqlens)
+    T, Hq, d = q.shape
+    o = np.full_like(q, np.nan)
+    lse = np.full((Hq, T), np.nan)
+    for b in range(cu.shape[0] - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        if s1 <= s0:
+            continue
+        ob, lb = prefill(q[s0:s1].transpose(1, 0, 2)[None], k[s0:s1].transpose(1, 0, 2)[None],
+                         v[s0:s1].transpose(1, 0, 2)[None], causal, scale)
+        o[s0:s1] = ob[0].transpose(1, 0, 2)
+        lse[:, s0:s1] = lb[0]
+    return o, lse
+
+
 def prefill_tiled(q, k, v, causal: bool, scale: float, br: int, bc: int):
     """The pages' tiled online-softmax prefill with Br x Bc tiles (same layouts)."""
     q, k, v = _f64(q), _f64(k), _f64(v)

@@ -78,6 +78,31 @@ def test_prefill_argument_errors(kw, code):
     assert prefill(**kw) == code
 
 
+def varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=FAKE, B=3, maxs=100, T=250, Hq=8, Hkv=2, d=128,
+           dtype=1):
+    return attn.lib.attn_prefill_varlen(P(q), P(k), P(v), P(o), P(lse), P(cu), B, maxs, T, Hq, Hkv, d, dtype,
+                                        1, 0.1, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=0), attn.ATTN_ERR_NULL),
+    (dict(lse=0), attn.ATTN_ERR_NULL),
+    (dict(B=-1), attn.ATTN_ERR_SHAPE),
+    (dict(maxs=-1), attn.ATTN_ERR_SHAPE),
+    (dict(T=-5), attn.ATTN_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=3), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(cu=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    (dict(o=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(maxs=1 << 20, Hq=64, Hkv=8), attn.ATTN_ERR_UNSUPPORTED),   # a head's rows past 32-bit offsets
+    (dict(B=0, q=0, k=0, v=0, o=0, lse=0, cu=0), attn.ATTN_OK),
+    (dict(T=0, q=0, k=0, v=0, o=0, lse=0, cu=0), attn.ATTN_OK),
+])
+def test_prefill_varlen_argument_errors(kw, code):
+    assert varlen(**kw) == code
+
+
 def decode(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, d=128, P_=16,
            maxb=8, dtype=1, chunk=0, ws=FAKE, wsb=1 << 30):
     return attn.lib.attn_decode(P(q), P(kc), P(vc), P(bt), P(sl), P(o), P(lse), B, Hq, Hkv, d, P_,

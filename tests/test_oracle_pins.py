@@ -490,3 +490,52 @@ def test_append_writes_only_the_new_slot():
     for b, (page, slot) in enumerate([(5, 1), (0, 5), (1, 15)]):
         expect_k[page, slot] = kn[b]; expect_v[page, slot] = vn[b]
     assert np.array_equal(kp2, expect_k) and np.array_equal(vp2, expect_v)
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length prefill (pofe.ai page, section "Interaction with
+# post-trained models": engines batch prompts of different lengths without padding)
+# ---------------------------------------------------------------------------
+def _packed(rng, lens, Hq, Hkv, d):
+    T = sum(lens)
+    return (rng.standard_normal((T, Hq, d)), rng.standard_normal((T, Hkv, d)), rng.standard_normal((T, Hkv, d)),
+            np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+
+
+def test_varlen_sequences_do_not_see_each_other():
+    """Changing every token of one sequence leaves the others' outputs bit for bit."""
+    rng = np.random.default_rng(41)
+    lens = [5, 0, 17, 9]
+    q, k, v, cu = _packed(rng, lens, 4, 2, 8)
+    o, lse = oracle.prefill_varlen(q, k, v, cu, True, 0.35)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    s0, s1 = cu[2], cu[3]
+    q2[s0:s1] += 1.5; k2[s0:s1] -= 0.7; v2[s0:s1] *= 3.0
+    o2, lse2 = oracle.prefill_varlen(q2, k2, v2, cu, True, 0.35)
+    keep = np.r_[0:s0, s1:cu[-1]]
+    assert np.array_equal(o[keep], o2[keep]) and np.array_equal(lse[:, keep], lse2[:, keep])
+    assert not np.array_equal(o[s0:s1], o2[s0:s1])
+
+
+def test_varlen_packing_order_does_not_matter():
+    """Packing the same sequences in another order permutes the outputs, bit for bit."""
+    rng = np.random.default_rng(42)
+    lens = [3, 11, 1, 7]
+    q, k, v, cu = _packed(rng, lens, 2, 1, 8)
+    o, lse = oracle.prefill_varlen(q, k, v, cu, True, 0.5)
+    order = [2, 0, 3, 1]
+    idx = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in order])
+    cu2 = np.concatenate([[0], np.cumsum([lens[b] for b in order])]).astype(np.int32)
+    o2, lse2 = oracle.prefill_varlen(q[idx], k[idx], v[idx], cu2, True, 0.5)
+    assert np.array_equal(o2, o[idx]) and np.array_equal(lse2, lse[:, idx])
+
+
+def test_varlen_single_token_sequence_is_its_value():
+    """A one-token sequence attends only to itself: O = v, LSE = scale * <q, k>."""
+    rng = np.random.default_rng(43)
+    q, k, v, cu = _packed(rng, [4, 1, 6], 2, 2, 8)
+    o, lse = oracle.prefill_varlen(q, k, v, cu, True, 0.8)
+    t = cu[1]
+    for h in range(2):
+        assert np.array_equal(o[t, h], v[t, h])
+        assert abs(lse[h, t] - 0.8 * float(q[t, h] @ k[t, h])) < 1e-12
