@@ -54,13 +54,16 @@ def _load():
         i = ctypes.c_int
         dbl = ctypes.c_double
         lib.oracle_prefill.argtypes = [P, P, P, P, P, i, i, i, i, i, i, dbl, i]
+        lib.oracle_prefill_ext.argtypes = [P, P, P, P, P, i, i, i, i, i, i, dbl, i, dbl, i]
+        lib.oracle_decode_ext.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i, dbl, i, dbl]
         lib.oracle_prefill_tiled.argtypes = [P, P, P, P, P, i, i, i, i, i, i, dbl, i, i]
         lib.oracle_decode.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i, dbl]
         lib.oracle_split_decode.argtypes = [P, P, P, P, P, P, P, i, i, i, i, i, i, dbl, i, i, P, P]
         lib.oracle_lse_combine.argtypes = [P, P, P, i, i, i, P, P]
         lib.oracle_online_trace.argtypes = [P, P, i, i, P, P, P, P, P, P]
         lib.oracle_num_threads.argtypes = []
-        for f in (lib.oracle_prefill, lib.oracle_prefill_tiled, lib.oracle_decode,
+        for f in (lib.oracle_prefill, lib.oracle_prefill_ext, lib.oracle_decode_ext,
+                  lib.oracle_prefill_tiled, lib.oracle_decode,
                   lib.oracle_split_decode, lib.oracle_lse_combine, lib.oracle_online_trace,
                   lib.oracle_num_threads):
             f.restype = ctypes.c_int
@@ -89,11 +92,13 @@ def num_threads() -> int:
     return int(_load().oracle_num_threads())
 
 
-def prefill(q, k, v, causal: bool, scale: float, row_step: int = 1):
+def prefill(q, k, v, causal: bool, scale: float, row_step: int = 1, window: int = -1, softcap: float = 0.0):
     """Plain-definition prefill.  q: [B,Hq,N,d]; k, v: [B,Hkv,N,d].
 
     Returns (o [B,Hq,N,d], lse [B,Hq,N]) in float64.  With row_step > 1 only rows
-    i with i % row_step == 0 are computed; the rest are NaN.
+    i with i % row_step == 0 are computed; the rest are NaN.  window >= 0: row i
+    also needs j >= i - window (sliding window); softcap > 0: every score s
+    becomes softcap * tanh(s / softcap) before the softmax.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Hq, N, d = q.shape
@@ -101,14 +106,15 @@ def prefill(q, k, v, causal: bool, scale: float, row_step: int = 1):
     assert k.shape == (B, Hkv, N, d) and v.shape == k.shape
     o = np.full_like(q, np.nan)
     lse = np.full((B, Hq, N), np.nan)
-    rc = _load().oracle_prefill(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, N, d,
-                                int(bool(causal)), float(scale), int(row_step))
+    rc = _load().oracle_prefill_ext(_p(q), _p(k), _p(v), _p(o), _p(lse), B, Hq, Hkv, N, d,
+                                    int(bool(causal)), float(scale), int(window), float(softcap),
+                                    int(row_step))
     if rc != 0:
         raise ValueError("oracle_prefill rejected its arguments")
     return o, lse
 
 
-def prefill_varlen(q, k, v, cu_seqlens, causal: bool, scale: float):
+def prefill_varlen(q, k, v, cu_seqlens, causal: bool, scale: float, window: int = -1, softcap: float = 0.0):
     """Prefill of a packed batch without padding (the variable-length interface of the
     pofe.ai page, section "Interaction with post-trained models"): sequence b is tokens
     cu_seqlens[b] .. cu_seqlens[b+1]-1 of q [T, Hq, d], k, v [T, Hkv, d] and attends
@@ -124,7 +130,7 @@ def prefill_varlen(q, k, v, cu_seqlens, causal: bool, scale: float):
         if s1 <= s0:
             continue
         ob, lb = prefill(q[s0:s1].transpose(1, 0, 2)[None], k[s0:s1].transpose(1, 0, 2)[None],
-                         v[s0:s1].transpose(1, 0, 2)[None], causal, scale)
+                         v[s0:s1].transpose(1, 0, 2)[None], causal, scale, window=window, softcap=softcap)
         o[s0:s1] = ob[0].transpose(1, 0, 2)
         lse[:, s0:s1] = lb[0]
     return o, lse
@@ -145,9 +151,11 @@ def prefill_tiled(q, k, v, causal: bool, scale: float, br: int, bc: int):
 
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, page_size: int,
-           max_blocks: int):
+           max_blocks: int, window: int = -1, softcap: float = 0.0):
     """Plain-definition decode.  q: [B,Hq,d].  Cache [nblk,P,Hkv,d] with a block table
     [B,max_blocks], or contiguous [B,S,Hkv,d] when block_table is None (S = max_blocks*P).
+    The query is token seq_lens[b] - 1; window >= 0 limits it to keys
+    seq_lens[b] - 1 - window ..; softcap as in prefill.
     Returns (o [B,Hq,d], lse [B,Hq]) in float64."""
     q, kc, vc = _f64(q), _f64(k_cache), _f64(v_cache)
     B, Hq, d = q.shape
@@ -156,15 +164,16 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, scale: float, page_size: 
     sl = _i32(seq_lens)
     o = np.full_like(q, np.nan)
     lse = np.full((B, Hq), np.nan)
-    rc = _load().oracle_decode(_p(q), _p(kc), _p(vc), _p(bt), _p(sl), _p(o), _p(lse), B, Hq,
-                               Hkv, d, int(page_size), int(max_blocks), float(scale))
+    rc = _load().oracle_decode_ext(_p(q), _p(kc), _p(vc), _p(bt), _p(sl), _p(o), _p(lse), B, Hq,
+                                   Hkv, d, int(page_size), int(max_blocks), float(scale), int(window),
+                                   float(softcap))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     return o, lse
 
 
 def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, scale: float,
-                  page_size: int, max_blocks: int):
+                  page_size: int, max_blocks: int, window: int = -1, softcap: float = 0.0):
     """Decode step with the new token appended in place first (pofe.ai page, section
     "Minimal implementation": the cache and block table take the new keys and values,
     cache_seqlens counts the tokens already cached).  The new rows k_new, v_new
@@ -188,7 +197,8 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
             page = int(bt[b, t // page_size])
             kc[page, t % page_size] = kn[b]
             vc[page, t % page_size] = vn[b]
-    o, lse = decode(q, kc, vc, bt, (t_new + 1).astype(np.int32), scale, page_size, max_blocks)
+    o, lse = decode(q, kc, vc, bt, (t_new + 1).astype(np.int32), scale, page_size, max_blocks, window=window,
+                    softcap=softcap)
     return o, lse, kc, vc
 
 

@@ -47,34 +47,40 @@
 #endif
 
 /* ------------------------------------------------------------------------ */
-/* The plain definition for one query row (two passes, no rescaling).        */
-/* Keys/values are n rows of d doubles, `stride` doubles apart.              */
-/* `s` is caller scratch of at least n doubles.                              */
+/* The plain definition for one query row (two passes, no rescaling) over    */
+/* the keys j0 .. n-1.  Keys/values are rows of d doubles, `stride` doubles  */
+/* apart; `s` is caller scratch of at least n doubles.  With softcap > 0     */
+/* each score becomes softcap * tanh(s / softcap) before the softmax; a      */
+/* window is a j0 above 0.  (Sliding windows and logit soft-capping are      */
+/* variants the pofe.ai page lists in section "Interaction with              */
+/* post-trained models"; their definitions are the readings in the notes.)   */
 /* ------------------------------------------------------------------------ */
-static void plain_row(const double *q, const double *k, const double *v,
-                      size_t stride, int64_t n, int d, double scale,
-                      double *s, double *o, double *lse)
+static void plain_row_ext(const double *q, const double *k, const double *v,
+                          size_t stride, int64_t j0, int64_t n, int d, double scale,
+                          double softcap, double *s, double *o, double *lse)
 {
-    if (n <= 0) {
+    if (j0 < 0) j0 = 0;
+    if (n <= j0) {
         for (int c = 0; c < d; ++c) o[c] = 0.0;
         *lse = -INFINITY;
         return;
     }
-    /* scores s_j = scale * <q, k_j> */
-    for (int64_t j = 0; j < n; ++j) {
+    /* scores s_j = scale * <q, k_j>, soft-capped if asked */
+    for (int64_t j = j0; j < n; ++j) {
         const double *kj = k + (size_t)j * stride;
         double acc = 0.0;
         for (int c = 0; c < d; ++c) acc += q[c] * kj[c];
         s[j] = scale * acc;
+        if (softcap > 0.0) s[j] = softcap * tanh(s[j] / softcap);
     }
     /* m = max_j s_j */
-    double m = s[0];
-    for (int64_t j = 1; j < n; ++j)
+    double m = s[j0];
+    for (int64_t j = j0 + 1; j < n; ++j)
         if (s[j] > m) m = s[j];
     /* Z = sum_j exp(s_j - m);  O = (1/Z) sum_j exp(s_j - m) v_j */
     for (int c = 0; c < d; ++c) o[c] = 0.0;
     double z = 0.0;
-    for (int64_t j = 0; j < n; ++j) {
+    for (int64_t j = j0; j < n; ++j) {
         const double w = exp(s[j] - m);
         const double *vj = v + (size_t)j * stride;
         z += w;
@@ -90,11 +96,12 @@ static void plain_row(const double *q, const double *k, const double *v,
 /* rows of o and lse are left untouched.  causal != 0: row i sees keys 0..i; */
 /* otherwise all N keys.  Returns 0, or -1 on bad arguments / no memory.    */
 /* ------------------------------------------------------------------------ */
-int oracle_prefill(const double *q, const double *k, const double *v,
-                   double *o, double *lse, int B, int Hq, int Hkv, int N, int d,
-                   int causal, double scale, int row_step)
+int oracle_prefill_ext(const double *q, const double *k, const double *v,
+                       double *o, double *lse, int B, int Hq, int Hkv, int N, int d,
+                       int causal, double scale, int window, double softcap, int row_step)
 {
-    if (B < 0 || Hq <= 0 || Hkv <= 0 || N < 0 || d <= 0 || Hq % Hkv != 0 || row_step < 1)
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || N < 0 || d <= 0 || Hq % Hkv != 0 || row_step < 1 ||
+        softcap < 0.0)
         return -1;
     const int g = Hq / Hkv;
     const int64_t rows = (int64_t)B * Hq * N;
@@ -115,14 +122,23 @@ int oracle_prefill(const double *q, const double *k, const double *v,
                 const int hk = h / g;
                 const double *kb = k + ((size_t)b * Hkv + hk) * (size_t)N * d;
                 const double *vb = v + ((size_t)b * Hkv + hk) * (size_t)N * d;
+                /* visible keys: j <= i when causal; j >= i - window when window >= 0 */
                 const int64_t n = causal ? (int64_t)i + 1 : (int64_t)N;
-                plain_row(q + (size_t)r * d, kb, vb, (size_t)d, n, d, scale, s,
-                          o + (size_t)r * d, lse + r);
+                const int64_t j0 = window >= 0 ? (int64_t)i - window : 0;
+                plain_row_ext(q + (size_t)r * d, kb, vb, (size_t)d, j0, n, d, scale, softcap, s,
+                              o + (size_t)r * d, lse + r);
             }
             free(s);
         }
     }
     return err ? -1 : 0;
+}
+
+int oracle_prefill(const double *q, const double *k, const double *v,
+                   double *o, double *lse, int B, int Hq, int Hkv, int N, int d,
+                   int causal, double scale, int row_step)
+{
+    return oracle_prefill_ext(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, -1, 0.0, row_step);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -154,13 +170,13 @@ static int gather_seq(const double *cache, const int32_t *block_table,
 /* Decode (one query token per sequence) by the plain definition, keys       */
 /* 0..seq_lens[b]-1 gathered through the block table (or contiguous).       */
 /* ------------------------------------------------------------------------ */
-int oracle_decode(const double *q, const double *k_cache, const double *v_cache,
-                  const int32_t *block_table, const int32_t *seq_lens,
-                  double *o, double *lse, int B, int Hq, int Hkv, int d,
-                  int page_size, int max_blocks, double scale)
+int oracle_decode_ext(const double *q, const double *k_cache, const double *v_cache,
+                      const int32_t *block_table, const int32_t *seq_lens,
+                      double *o, double *lse, int B, int Hq, int Hkv, int d,
+                      int page_size, int max_blocks, double scale, int window, double softcap)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0 || page_size <= 0 ||
-        max_blocks < 0)
+        max_blocks < 0 || softcap < 0.0)
         return -1;
     const int g = Hq / Hkv;
     const int64_t cap = (int64_t)max_blocks * page_size;
@@ -180,10 +196,13 @@ int oracle_decode(const double *q, const double *k_cache, const double *v_cache,
 #pragma omp atomic write
             err = 1;
         } else {
+            /* the query is token len - 1: with a window it sees keys len-1-window .. len-1 */
+            const int64_t j0 = window >= 0 ? len - 1 - window : 0;
             for (int j = 0; j < g; ++j) {
                 const int h = hk * g + j;
                 const size_t r = (size_t)b * Hq + h;
-                plain_row(q + r * d, kk, vv, (size_t)d, len, d, scale, s, o + r * d, lse + r);
+                plain_row_ext(q + r * d, kk, vv, (size_t)d, j0, len, d, scale, softcap, s, o + r * d,
+                              lse + r);
             }
         }
         free(kk);
@@ -191,6 +210,15 @@ int oracle_decode(const double *q, const double *k_cache, const double *v_cache,
         free(s);
     }
     return err ? -1 : 0;
+}
+
+int oracle_decode(const double *q, const double *k_cache, const double *v_cache,
+                  const int32_t *block_table, const int32_t *seq_lens,
+                  double *o, double *lse, int B, int Hq, int Hkv, int d,
+                  int page_size, int max_blocks, double scale)
+{
+    return oracle_decode_ext(q, k_cache, v_cache, block_table, seq_lens, o, lse, B, Hq, Hkv, d,
+                             page_size, max_blocks, scale, -1, 0.0);
 }
 
 /* ------------------------------------------------------------------------ */

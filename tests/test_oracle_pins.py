@@ -539,3 +539,72 @@ def test_varlen_single_token_sequence_is_its_value():
     for h in range(2):
         assert np.array_equal(o[t, h], v[t, h])
         assert abs(lse[h, t] - 0.8 * float(q[t, h] @ k[t, h])) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Variants the pofe.ai page lists (section "Interaction with post-trained
+# models"): sliding windows and logit soft-capping
+# ---------------------------------------------------------------------------
+def test_window_matches_torch_sdpa_with_a_band_mask():
+    """Row i sees keys max(0, i - W) .. i: PyTorch float64 SDPA with the same
+    boolean band mask (a library routine) agrees to 1e-12."""
+    rng = np.random.default_rng(51)
+    B, Hq, Hkv, N, d, W = 2, 4, 2, 70, 16, 9
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d)); v = rng.standard_normal((B, Hkv, N, d))
+    o, lse = oracle.prefill(q, k, v, True, 0.3, window=W)
+    i = torch.arange(N)[:, None]; j = torch.arange(N)[None, :]
+    allowed = (j <= i) & (j >= i - W)
+    qt, kt, vt = (torch.from_numpy(x) for x in (q, k, v))
+    kt = kt.repeat_interleave(2, dim=1); vt = vt.repeat_interleave(2, dim=1)
+    ro = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=allowed, scale=0.3)
+    s = torch.matmul(qt, kt.transpose(-1, -2).contiguous()) * 0.3
+    rl = torch.logsumexp(s.masked_fill(~allowed, float("-inf")), dim=-1)
+    assert np.max(np.abs(o - ro.numpy())) < 1e-12 and np.max(np.abs(lse - rl.numpy())) < 1e-12
+
+
+def test_window_special_cases():
+    rng = np.random.default_rng(52)
+    B, Hq, Hkv, N, d = 1, 2, 1, 40, 8
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d)); v = rng.standard_normal((B, Hkv, N, d))
+    full = oracle.prefill(q, k, v, True, 0.4)
+    # a window as long as the sequence changes nothing, bit for bit
+    wide = oracle.prefill(q, k, v, True, 0.4, window=N - 1)
+    assert np.array_equal(wide[0], full[0]) and np.array_equal(wide[1], full[1])
+    # window 0: each row sees only itself, O = v_i and LSE = scale * <q_i, k_i>
+    o0, l0 = oracle.prefill(q, k, v, True, 0.4, window=0)
+    for h in range(Hq):
+        assert np.array_equal(o0[0, h], v[0, 0])
+        assert np.max(np.abs(l0[0, h] - 0.4 * np.einsum("nd,nd->n", q[0, h], k[0, 0]))) < 1e-12
+    # decode of token i with a window = prefill row i with the same window, bit for bit
+    ow, lw = oracle.prefill(q, k, v, True, 0.4, window=5)
+    for i in (0, 3, 17, 39):
+        od, ld = oracle.decode(q[:, :, i], _to_cache(k), _to_cache(v), None, np.array([i + 1], np.int32), 0.4, 8,
+                               N // 8, window=5)
+        assert np.array_equal(od, ow[:, :, i]) and np.array_equal(ld, lw[:, :, i])
+
+
+def test_softcap_limits():
+    """softcap * tanh(s / softcap) differs from s by at most |s|^3 / (3 softcap^2): with a
+    large cap the result is the uncapped one within that bound; with a tiny cap every
+    score is within +-cap, so the weights are uniform up to exp(+-2 cap) and O is the
+    mean of the visible values within 4 cap max|v|."""
+    rng = np.random.default_rng(53)
+    B, Hq, Hkv, N, d = 1, 2, 2, 30, 8
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d)); v = rng.standard_normal((B, Hkv, N, d))
+    scale = 0.35
+    o, lse = oracle.prefill(q, k, v, True, scale)
+    smax = float(np.max(np.abs(np.einsum("bhnd,bhmd->bhnm", q, k)))) * scale
+    C = 1000.0
+    oc, lc = oracle.prefill(q, k, v, True, scale, softcap=C)
+    bound = smax ** 3 / (3 * C * C)
+    assert np.max(np.abs(lc - lse)) <= bound * 1.01 + 1e-12
+    assert np.max(np.abs(oc - o)) <= 4 * bound * float(np.max(np.abs(v))) + 1e-12
+    c = 1e-3
+    ot, lt = oracle.prefill(q, k, v, True, scale, softcap=c)
+    for i in range(N):
+        mean = v[0, :, : i + 1].mean(axis=1)
+        assert np.max(np.abs(ot[0, :, i] - mean)) <= 4 * c * float(np.max(np.abs(v))) + 1e-12
+        assert np.max(np.abs(lt[0, :, i] - np.log(i + 1))) <= c + 1e-12
