@@ -248,14 +248,14 @@ def main():
         out["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                            "traffic": measured_traffic("prefill"),
-                           "kernel": "prefill_bf16_kernel<128>", "avg_launch_ms": pre_ms,
+                           "kernel": "prefill_bf16_kernel<128, false>", "avg_launch_ms": pre_ms,
                            "algorithmic_flop_per_launch": prefill_flop}
     if do_d:
         gbs = decode_bytes / (dec_ms * 1e-3) / 1e9
         out["decode"] = {"value": gbs, "unit": "GB/s", "avg_ms": dec_ms,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode"),
-                                      "kernels": "decode_split_kernel<128> + lse_combine_kernel<128>",
+                                      "kernels": "decode_split_kernel<128, false, false> + lse_combine_kernel<128>",
                                       "algorithmic_bytes_per_launch": decode_bytes}}
     if do_p and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(px, args.cpu_seconds)

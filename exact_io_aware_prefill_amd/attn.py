@@ -30,8 +30,9 @@ ATTN_ERR_HIP = -7
 ATTN_F32 = 0
 ATTN_BF16 = 1
 
-EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_decode", "attn_decode_append", "attn_decode_chunk_tokens",
-           "attn_decode_workspace_bytes", "attn_lse_combine", "attn_status_string")
+EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_ext", "attn_decode", "attn_decode_append",
+           "attn_decode_ext", "attn_decode_chunk_tokens", "attn_decode_workspace_bytes", "attn_lse_combine",
+           "attn_status_string")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -39,6 +40,12 @@ lib.attn_prefill.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, cty
 lib.attn_prefill.restype = _I
 lib.attn_prefill_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 lib.attn_prefill_varlen.restype = _I
+lib.attn_prefill_ext.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
+                                 ctypes.c_float, _P]
+lib.attn_prefill_ext.restype = _I
+lib.attn_decode_ext.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
+                                ctypes.c_float, _I, _P, ctypes.c_size_t, _P]
+lib.attn_decode_ext.restype = _I
 lib.attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                             _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode.restype = _I
@@ -109,6 +116,23 @@ def attn_prefill_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen: int, causal: bo
     _check(rc, "attn_prefill_varlen")
 
 
+def attn_prefill_ext(q, k, v, o, lse, cu_seqlens, max_seqlen: int, causal: bool, scale: float,
+                     window_left: int = -1, softcap: float = 0.0, stream=None) -> None:
+    """attn_prefill (cu_seqlens None: q [B, Hq, N, d]) or attn_prefill_varlen (q [T, Hq, d],
+    max_seqlen the longest sequence) with a sliding window (window_left >= 0: keys j >= i -
+    window_left) and logit soft-capping (softcap > 0)."""
+    if cu_seqlens is None:
+        B, Hq, N, d = q.shape
+        T, Hkv = 0, k.shape[1]
+    else:
+        T, Hq, d = q.shape
+        B, N, Hkv = cu_seqlens.numel() - 1, int(max_seqlen), k.shape[1]
+    rc = lib.attn_prefill_ext(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens), B, N, T, Hq, Hkv, d,
+                              _dtype_code(q), int(bool(causal)), float(scale), int(window_left), float(softcap),
+                              _stream(stream))
+    _check(rc, "attn_prefill_ext")
+
+
 def attn_decode_chunk_tokens(batch: int, n_kv_heads: int, page_size: int, max_blocks_per_seq: int,
                              chunk_tokens: int = 0) -> int:
     r = lib.attn_decode_chunk_tokens(batch, n_kv_heads, page_size, max_blocks_per_seq, chunk_tokens)
@@ -155,6 +179,22 @@ def attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seq
     _check(rc, "attn_decode_append")
 
 
+def attn_decode_ext(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, o, lse, page_size: int,
+                    max_blocks_per_seq: int, scale: float, window_left: int, softcap: float, chunk_tokens: int,
+                    workspace, stream=None) -> None:
+    """attn_decode (k_new, v_new None) or attn_decode_append (both given) with a sliding
+    window (the query, token L-1, sees tokens >= L-1-window_left) and logit soft-capping."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[-2]
+    rc = lib.attn_decode_ext(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                             _ptr(seq_lens), _ptr(o), _ptr(lse), B, Hq, Hkv, d, int(page_size),
+                             int(max_blocks_per_seq), _dtype_code(q), float(scale), int(window_left),
+                             float(softcap), int(chunk_tokens), _ptr(workspace),
+                             0 if workspace is None else workspace.numel() * workspace.element_size(),
+                             _stream(stream))
+    _check(rc, "attn_decode_ext")
+
+
 def attn_lse_combine(o_parts, lse_parts, n_splits, o, lse, stream=None) -> None:
     """o_parts [rows, S, d] f32; lse_parts [rows, S] f32; n_splits [rows] int32 or None;
     o [rows, d] (bf16 or f32); lse [rows] f32 or None."""
@@ -165,27 +205,39 @@ def attn_lse_combine(o_parts, lse_parts, n_splits, o, lse, stream=None) -> None:
 
 
 # ---- conveniences that allocate outputs with PyTorch (allocation only) ----------
-def prefill(q, k, v, causal: bool = True, scale: float | None = None, stream=None):
+def _plain(window_left, softcap) -> bool:
+    return window_left == -1 and softcap == 0.0
+
+
+def prefill(q, k, v, causal: bool = True, scale: float | None = None, stream=None, window_left: int = -1,
+            softcap: float = 0.0):
     B, Hq, N, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    attn_prefill(q, k, v, o, lse, causal, d ** -0.5 if scale is None else scale, stream)
+    scale = d ** -0.5 if scale is None else scale
+    if _plain(window_left, softcap):
+        attn_prefill(q, k, v, o, lse, causal, scale, stream)
+    else:
+        attn_prefill_ext(q, k, v, o, lse, None, N, causal, scale, window_left, softcap, stream)
     return o, lse
 
 
 def prefill_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, scale: float | None = None,
-                   stream=None):
+                   stream=None, window_left: int = -1, softcap: float = 0.0):
     T, Hq, d = q.shape
     o = torch.empty_like(q)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    attn_prefill_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, d ** -0.5 if scale is None else scale,
-                        stream)
+    scale = d ** -0.5 if scale is None else scale
+    if _plain(window_left, softcap):
+        attn_prefill_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, scale, stream)
+    else:
+        attn_prefill_ext(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, scale, window_left, softcap, stream)
     return o, lse
 
 
 def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, page_size: int,
                   max_blocks_per_seq: int, scale: float | None = None, chunk_tokens: int = 0, stream=None,
-                  workspace=None):
+                  workspace=None, window_left: int = -1, softcap: float = 0.0):
     """Decode step with the new token's k_new, v_new [B, Hkv, d] written into the caches
     in place at token cache_seqlens[b]; returns (o, lse) over cache_seqlens[b] + 1 tokens."""
     B, Hq, d = q.shape
@@ -195,14 +247,19 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse, page_size,
-                       max_blocks_per_seq, d ** -0.5 if scale is None else scale, chunk_tokens, workspace,
-                       stream)
+    scale = d ** -0.5 if scale is None else scale
+    if _plain(window_left, softcap):
+        attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse, page_size,
+                           max_blocks_per_seq, scale, chunk_tokens, workspace, stream)
+    else:
+        attn_decode_ext(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse, page_size,
+                        max_blocks_per_seq, scale, window_left, softcap, chunk_tokens, workspace, stream)
     return o, lse
 
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, page_size: int, max_blocks_per_seq: int,
-           scale: float | None = None, chunk_tokens: int = 0, stream=None, workspace=None):
+           scale: float | None = None, chunk_tokens: int = 0, stream=None, workspace=None, window_left: int = -1,
+           softcap: float = 0.0):
     B, Hq, d = q.shape
     Hkv = k_cache.shape[-2]
     need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
@@ -210,6 +267,11 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, page_size: int, max_block
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     o = torch.empty_like(q)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    attn_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, page_size, max_blocks_per_seq,
-                d ** -0.5 if scale is None else scale, chunk_tokens, workspace, stream)
+    scale = d ** -0.5 if scale is None else scale
+    if _plain(window_left, softcap):
+        attn_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, page_size, max_blocks_per_seq, scale,
+                    chunk_tokens, workspace, stream)
+    else:
+        attn_decode_ext(q, None, None, k_cache, v_cache, block_table, seq_lens, o, lse, page_size,
+                        max_blocks_per_seq, scale, window_left, softcap, chunk_tokens, workspace, stream)
     return o, lse

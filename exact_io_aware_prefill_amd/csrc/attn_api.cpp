@@ -4,6 +4,7 @@
 // include/attn.h.
 #include <hip/hip_runtime.h>
 #include <limits.h>
+#include <math.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -51,15 +52,63 @@ int resolve_chunk(int batch, int n_kv_heads, int page_size, int max_blocks, int 
     return (int)chunk;
 }
 
-// Shared body of attn_decode and attn_decode_append; `append` selects the latter
-// (k_new and v_new are then required).
+// Variant options: window -1 (none) or >= 0; softcap 0 (none) or finite > 0.
+bool variant_ok(int window_left, float softcap)
+{
+    return window_left >= -1 && softcap >= 0.f && isfinite(softcap);
+}
+
+// Shared body of the prefill entry points: padded layout (seqlen = N,
+// total_tokens unused) or, with `packed`, the packed layout described by
+// cu_seqlens (seqlen = the longest sequence).
+int prefill_impl(bool packed, const void *q, const void *k, const void *v, void *o, float *lse, const int32_t *cu_seqlens,
+                 int batch, int seqlen, int total_tokens, int n_q_heads, int n_kv_heads, int head_dim, int dtype,
+                 int causal, float scale, int window_left, float softcap, void *stream)
+{
+    if (batch < 0 || seqlen < 0 || (packed && total_tokens < 0) || n_q_heads <= 0 || n_kv_heads <= 0 ||
+        head_dim <= 0 || !variant_ok(window_left, softcap))
+        return ATTN_ERR_SHAPE;
+    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
+    if (!head_dim_ok(head_dim) || (dtype != ATTN_F32 && dtype != ATTN_BF16))
+        return ATTN_ERR_UNSUPPORTED;
+    if (batch == 0 || seqlen == 0 || (packed && total_tokens == 0)) return ATTN_OK;
+    if (!q || !k || !v || !o || !lse || (packed && !cu_seqlens)) return ATTN_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
+        (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
+        return ATTN_ERR_ALIGN;
+    // element offsets are formed in 64-bit; the grid is one dimension of query
+    // tiles, and one head's rows of one sequence (seqlen rounded up to a tile)
+    // are addressed through a descriptor with a 32-bit range
+    const long long row_bytes =
+        packed ? (long long)n_q_heads * head_dim * (dtype == ATTN_F32 ? 4 : 2) : (long long)head_dim * 2;
+    if ((long long)batch * n_q_heads * ((seqlen + 63) / 64) > INT_MAX ||
+        ((long long)seqlen + 255) * row_bytes > 0xffffffffLL)
+        return ATTN_ERR_UNSUPPORTED;
+
+    attn::PrefillParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
+    p.B = batch; p.N = seqlen; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
+    p.causal = causal ? 1 : 0;
+    p.scale = scale;
+    p.cu_seqlens = packed ? cu_seqlens : nullptr;
+    p.total = packed ? total_tokens : 0;
+    p.window = window_left;
+    p.softcap = softcap;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (dtype == ATTN_BF16) return run([&] { return attn::launch_prefill_bf16(p, s); });
+    return run([&] { return attn::launch_prefill_f32(p, s); });
+}
+
+// Shared body of the decode entry points; `append` selects the in-place append
+// (k_new and v_new are then both required).
 int decode_impl(bool append, const void *q, const void *k_new, const void *v_new, const void *k_cache,
                 const void *v_cache, const int32_t *block_table, const int32_t *seq_lens, void *o, float *lse_or_null, int batch,
                 int n_q_heads, int n_kv_heads, int head_dim, int page_size, int max_blocks_per_seq, int dtype,
-                float scale, int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream)
+                float scale, int window_left, float softcap, int chunk_tokens, void *workspace,
+                size_t workspace_bytes, void *stream)
 {
     if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 ||
-        max_blocks_per_seq <= 0 || chunk_tokens < 0)
+        max_blocks_per_seq <= 0 || chunk_tokens < 0 || !variant_ok(window_left, softcap))
         return ATTN_ERR_SHAPE;
     if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
     if (!head_dim_ok(head_dim) || dtype != ATTN_BF16 ||
@@ -97,6 +146,8 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
     const size_t rows = (size_t)batch * n_q_heads;
     p.k_new = k_new;
     p.v_new = v_new;
+    p.window = window_left;
+    p.softcap = softcap;
     p.o_parts = static_cast<float *>(workspace);
     p.lse_parts = p.o_parts + rows * (size_t)max_chunks * head_dim;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -126,29 +177,8 @@ int attn_prefill(const void *q, const void *k, const void *v, void *o, float *ls
                  int seqlen, int n_q_heads, int n_kv_heads, int head_dim, int dtype, int causal,
                  float scale, void *stream)
 {
-    if (batch < 0 || seqlen < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
-        return ATTN_ERR_SHAPE;
-    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
-    if (!head_dim_ok(head_dim) || (dtype != ATTN_F32 && dtype != ATTN_BF16))
-        return ATTN_ERR_UNSUPPORTED;
-    if (batch == 0 || seqlen == 0) return ATTN_OK;
-    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
-        return ATTN_ERR_ALIGN;
-    // element offsets are formed in 64-bit; the grid is one dimension of query tiles
-    // and one head's rows are addressed through a descriptor with a 32-bit range
-    if ((long long)batch * n_q_heads * ((seqlen + 63) / 64) > INT_MAX ||
-        ((long long)seqlen + 255) * head_dim * 2 > 0xffffffffLL)
-        return ATTN_ERR_UNSUPPORTED;
-
-    attn::PrefillParams p;
-    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
-    p.B = batch; p.N = seqlen; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
-    p.causal = causal ? 1 : 0;
-    p.scale = scale;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == ATTN_BF16) return run([&] { return attn::launch_prefill_bf16(p, s); });
-    return run([&] { return attn::launch_prefill_f32(p, s); });
+    return prefill_impl(false, q, k, v, o, lse, nullptr, batch, seqlen, 0, n_q_heads, n_kv_heads, head_dim, dtype,
+                        causal, scale, -1, 0.f, stream);
 }
 
 int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -156,32 +186,18 @@ int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o, fl
                         int n_q_heads, int n_kv_heads, int head_dim, int dtype, int causal, float scale,
                         void *stream)
 {
-    if (batch < 0 || max_seqlen < 0 || total_tokens < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0)
-        return ATTN_ERR_SHAPE;
-    if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
-    if (!head_dim_ok(head_dim) || (dtype != ATTN_F32 && dtype != ATTN_BF16))
-        return ATTN_ERR_UNSUPPORTED;
-    if (batch == 0 || max_seqlen == 0 || total_tokens == 0) return ATTN_OK;
-    if (!q || !k || !v || !o || !lse || !cu_seqlens) return ATTN_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-        (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
-        return ATTN_ERR_ALIGN;
-    // one sequence's rows of one head span (max_seqlen rounded up to a tile) rows
-    // of n_q_heads * head_dim elements, addressed with a 32-bit range
-    if ((long long)batch * n_q_heads * ((max_seqlen + 63) / 64) > INT_MAX ||
-        ((long long)max_seqlen + 255) * n_q_heads * head_dim * (dtype == ATTN_F32 ? 4 : 2) > 0xffffffffLL)
-        return ATTN_ERR_UNSUPPORTED;
+    return prefill_impl(true, q, k, v, o, lse, cu_seqlens, batch, max_seqlen, total_tokens, n_q_heads, n_kv_heads,
+                        head_dim, dtype, causal, scale, -1, 0.f, stream);
+}
 
-    attn::PrefillParams p;
-    p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
-    p.B = batch; p.N = max_seqlen; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
-    p.causal = causal ? 1 : 0;
-    p.scale = scale;
-    p.cu_seqlens = cu_seqlens;
-    p.total = total_tokens;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == ATTN_BF16) return run([&] { return attn::launch_prefill_bf16(p, s); });
-    return run([&] { return attn::launch_prefill_f32(p, s); });
+int attn_prefill_ext(const void *q, const void *k, const void *v, void *o, float *lse,
+                     const int32_t *cu_seqlens_or_null, int batch, int seqlen, int total_tokens,
+                     int n_q_heads, int n_kv_heads, int head_dim, int dtype, int causal, float scale,
+                     int window_left, float softcap, void *stream)
+{
+    return prefill_impl(cu_seqlens_or_null != nullptr, q, k, v, o, lse, cu_seqlens_or_null, batch, seqlen,
+                        total_tokens, n_q_heads, n_kv_heads, head_dim, dtype, causal, scale, window_left, softcap,
+                        stream);
 }
 
 int attn_decode_chunk_tokens(int batch, int n_kv_heads, int page_size, int max_blocks_per_seq,
@@ -208,8 +224,8 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 size_t workspace_bytes, void *stream)
 {
     return decode_impl(false, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, o, lse_or_null, batch,
-                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale, chunk_tokens,
-                       workspace, workspace_bytes, stream);
+                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale, -1, 0.f,
+                       chunk_tokens, workspace, workspace_bytes, stream);
 }
 
 int attn_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
@@ -219,8 +235,19 @@ int attn_decode_append(const void *q, const void *k_new, const void *v_new, void
                        void *workspace, size_t workspace_bytes, void *stream)
 {
     return decode_impl(true, q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse_or_null, batch,
-                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale, chunk_tokens,
-                       workspace, workspace_bytes, stream);
+                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale, -1, 0.f,
+                       chunk_tokens, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_ext(const void *q, const void *k_new_or_null, const void *v_new_or_null, void *k_cache,
+                    void *v_cache, const int32_t *block_table, const int32_t *seq_lens, void *o,
+                    float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,
+                    int max_blocks_per_seq, int dtype, float scale, int window_left, float softcap,
+                    int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return decode_impl(k_new_or_null || v_new_or_null, q, k_new_or_null, v_new_or_null, k_cache, v_cache,
+                       block_table, seq_lens, o, lse_or_null, batch, n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale,
+                       window_left, softcap, chunk_tokens, workspace, workspace_bytes, stream);
 }
 
 int attn_lse_combine(const float *o_parts, const float *lse_parts, const int32_t *n_splits_or_null,

@@ -20,6 +20,10 @@ struct PrefillParams {
     // [Hq, total], and N is the longest sequence
     const int32_t *cu_seqlens = nullptr;
     int total = 0;
+    // sliding window (row i sees keys >= i - window; -1: none) and logit
+    // soft-cap (scores s become softcap * tanh(s / softcap); 0: none)
+    int window = -1;
+    float softcap = 0.f;
 };
 hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream);
 
@@ -42,6 +46,10 @@ struct DecodeParams {
     // in-place append (both NULL for plain decode): rows [B, Hkv, head_dim]
     // written into the cache at token seq_lens[b], which the query then attends
     const void *k_new = nullptr, *v_new = nullptr;
+    // sliding window (the query, token L-1, sees tokens >= L-1-window; -1: none)
+    // and logit soft-cap (0: none), as for prefill
+    int window = -1;
+    float softcap = 0.f;
 };
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 

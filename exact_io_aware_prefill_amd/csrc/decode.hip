@@ -37,8 +37,17 @@
 //   * Each wave keeps two steps in flight (two register sets), so a workgroup
 //     has 512 tokens of keys and values in flight: a whole 512-token chunk is
 //     requested at once.
+//   * A separate instantiation adds a sliding window and logit soft-capping (two
+//     of the variants the page's section "Interaction with post-trained models"
+//     lists).  With a window the query (token L-1) sees tokens L-1-w .. L-1:
+//     chunks wholly before the window exit at once (the combine starts at the
+//     first live chunk), waves skip their steps that end before it, and the one
+//     step that straddles its start is masked.  Soft-capping maps each score s to
+//     cap * tanh(s / cap) before the masking.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "attn_kernels.h"
 
@@ -68,6 +77,10 @@ struct SplitArgs {
     int Hq, Hkv, group, page, max_blocks, chunk, max_chunks;
     long long seq_tokens;  // tokens per sequence of the contiguous layout (= capacity)
     float scale_log2;
+    // variant only: window (-1: none); soft-cap as x = cap_log2 * tanh(raw * scale / cap)
+    // in base-2 units, with cap_log2 = cap * log2(e) and cap_k = 2 log2(e) scale / cap
+    int window;
+    float cap_log2, cap_k;
 };
 
 // Tokens the query attends for sequence b, and the index of the appended token
@@ -162,10 +175,25 @@ __device__ __forceinline__ void issue_step(const SplitArgs &a, StepRegs<D> &s, c
     }
 }
 
-template <int D>
-__device__ __forceinline__ void consume_step(const StepRegs<D> &s, char *slab, const bf16x8_t *qf, f32x4_t *acc,
-                                             float &m, float &l, int tb, int t_end, float scale_log2, int G,
-                                             const uint32_t *vstore, uint32_t vread)
+// First token the query sees: L-1-window with a window (variant only), else 0.
+template <bool EXT>
+__device__ __forceinline__ int window_start(const SplitArgs &a, int L)
+{
+    return (EXT && a.window >= 0) ? max(0, L - 1 - a.window) : 0;
+}
+
+// tanh(y) = 1 - 2 / (e^{2y} + 1), exact at y -> +-inf (rcp(+inf) = 0, rcp(1) = 1);
+// returns cap_log2 * tanh(raw * scale / cap) with cap_k = 2 log2(e) scale / cap.
+__device__ __forceinline__ float soft_cap_log2(float raw, float cap_log2, float cap_k)
+{
+    const float r = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(raw * cap_k) + 1.f);
+    return fmaf(-2.f * cap_log2, r, cap_log2);
+}
+
+template <int D, bool EXT>
+__device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<D> &s, char *slab,
+                                             const bf16x8_t *qf, f32x4_t *acc, float &m, float &l, int tb,
+                                             int t_lo, int t_end, int G, const uint32_t *vstore, uint32_t vread)
 {
     using Gm = Geo<D>;
     // scores of the two 16-token blocks
@@ -185,21 +213,24 @@ __device__ __forceinline__ void consume_step(const StepRegs<D> &s, char *slab, c
         *reinterpret_cast<uint4 *>(slab + vstore[i % 2] + (i & ~1) * Gm::RPI * Gm::RB) = s.v[i];
 
     // online softmax over this step (lane: query l16, tokens 4G+i of each block)
-    const bool tail = tb + kStep > t_end;
+    const bool tail = tb + kStep > t_end || (EXT && tb < t_lo);
+    const bool capped = EXT && a.cap_log2 > 0.f;
     float x[8];
     float mx = -INFINITY;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float xv = st[blk][i] * scale_log2;
-            if (tail && tb + 16 * blk + 4 * G + i >= t_end) xv = -INFINITY;
+            float xv = capped ? soft_cap_log2(st[blk][i], a.cap_log2, a.cap_k) : st[blk][i] * a.scale_log2;
+            const int tok = tb + 16 * blk + 4 * G + i;
+            if (tail && (tok >= t_end || (EXT && tok < t_lo))) xv = -INFINITY;
             x[4 * blk + i] = xv;
             mx = fmaxf(mx, xv);
         }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);  // finite: the step's first token is in the sequence
+    // finite: every step a wave runs holds a token in [t_lo, t_end)
+    const float m_new = fmaxf(m, mx);
     const float c = __builtin_amdgcn_exp2f(m - m_new);
     float rs = 0.f;
     bf16x8_t pf;
@@ -227,9 +258,9 @@ __device__ __forceinline__ void consume_step(const StepRegs<D> &s, char *slab, c
     }
 }
 
-// APPEND selects the in-place append variant (a separate instantiation, so the
-// plain decode keeps its register budget).
-template <int D, bool APPEND>
+// APPEND selects the in-place append variant, EXT the window / soft-cap variant
+// (separate instantiations, so the plain decode keeps its register budget).
+template <int D, bool APPEND, bool EXT>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
 {
     using Gm = Geo<D>;
@@ -247,6 +278,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
     const int t_begin = chunk * a.chunk;
     if (t_begin >= L) return;  // whole workgroup exits together: this chunk is empty
     const int t_end = min(t_begin + a.chunk, L);
+    const int t_lo = window_start<EXT>(a, L);
+    if (EXT && t_end <= t_lo) return;  // the chunk ends before the window: the combine skips it
     // append: only the workgroup whose chunk holds the new token touches it
     const bool has_new = APPEND && t_new >= t_begin && t_new < t_end;  // workgroup-uniform
 
@@ -320,15 +353,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
                 reinterpret_cast<const uint4 *>(a.v_new + src)[tid - D / 8];
         __syncthreads();
     }
+    // with a window, skip this wave's steps that end before it starts
+    if (EXT && tb + kStep <= t_lo) tb += ((t_lo - tb - kStep) / stride + 1) * stride;
     StepRegs<D> r0, r1;
     issue_step<D>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
     while (tb < t_end) {
         issue_step<D>(a, r1, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-        consume_step<D>(r0, slab, qf, acc, m, l, tb, t_end, a.scale_log2, G, vstore, vread);
+        consume_step<D, EXT>(a, r0, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread);
         tb += stride;
         if (tb >= t_end) break;
         issue_step<D>(a, r0, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-        consume_step<D>(r1, slab, qf, acc, m, l, tb, t_end, a.scale_log2, G, vstore, vread);
+        consume_step<D, EXT>(a, r1, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread);
         tb += stride;
     }
 
@@ -383,6 +418,7 @@ struct CombineArgs {
     const int32_t *seq_lens;  // decode: splits = ceil(tokens / chunk), or NULL
     int Hq, chunk, max_splits, capacity;
     int append;  // decode with append: tokens = min(seq_lens, capacity - 1) + 1
+    int window;  // decode with a window (-1: none): splits before the window's chunk are skipped
     void *o;
     int o_bf16;
     float *lse;
@@ -399,22 +435,26 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
     const size_t row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = tid % C4, sg = tid / C4;
-    int ns;
+    int ns, first = 0;
     if (a.seq_lens) {
         const int sl = a.seq_lens[row / a.Hq];
         const int L = a.append ? max(0, min(sl, a.capacity - 1)) + 1 : max(0, min(sl, a.capacity));
         ns = (L + a.chunk - 1) / a.chunk;
+        if (a.window >= 0) first = max(0, L - 1 - a.window) / a.chunk;  // the chunk holding the window's start
     } else if (a.n_splits) {
         ns = a.n_splits[row];
     } else {
         ns = a.max_splits;
     }
     ns = max(0, min(ns, a.max_splits));
-    const float *lam = a.lse_parts + row * a.max_splits;
-    // descriptors over the row's first ns partials: loads past them return zero,
+    first = min(first, ns);
+    // from here on, split k means split first + k of the row
+    const float *lam = a.lse_parts + row * a.max_splits + first;
+    ns -= first;
+    // descriptors over the row's ns live partials: loads past them return zero,
     // so every load is unconditional and all of them can be in flight together
-    const __amdgpu_buffer_rsrc_t ro =
-        make_rsrc(reinterpret_cast<const char *>(a.o_parts + row * a.max_splits * D), (uint32_t)ns * D * 4u);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+        reinterpret_cast<const char *>(a.o_parts + (row * a.max_splits + first) * D), (uint32_t)ns * D * 4u);
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(reinterpret_cast<const char *>(lam), (uint32_t)ns * 4u);
     auto load_part = [&](int k, f32x4_t &vk, float &lk) {
         vk = __builtin_bit_cast(f32x4_t, bload16(ro, (uint32_t)k * (D * 4) + 16u * col, 0));
@@ -523,19 +563,28 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     a.max_chunks = p.max_chunks;
     a.seq_tokens = (long long)p.max_blocks * p.page_size;
     a.scale_log2 = p.scale * kLog2e;
+    // a window that reaches back past the first slot limits nothing
+    a.window = (p.window >= 0 && (long long)p.window < a.seq_tokens) ? p.window : -1;
+    a.cap_log2 = p.softcap > 0.f ? p.softcap * kLog2e : 0.f;
+    a.cap_k = p.softcap > 0.f ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
+    const bool ext = a.window >= 0 || p.softcap > 0.f;
     const dim3 grid((unsigned)((long long)p.max_chunks * p.Hkv), (unsigned)p.B);
     const bool append = a.k_new != nullptr;
-    if (p.head_dim == 128) {
-        if (append)
-            hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, dim3(kThreads), 0, stream, a);
+    auto kernel = [&](auto dconst) {
+        constexpr int DD = decltype(dconst)::value;
+        if (append && ext)
+            hipLaunchKernelGGL((decode_split_kernel<DD, true, true>), grid, dim3(kThreads), 0, stream, a);
+        else if (append)
+            hipLaunchKernelGGL((decode_split_kernel<DD, true, false>), grid, dim3(kThreads), 0, stream, a);
+        else if (ext)
+            hipLaunchKernelGGL((decode_split_kernel<DD, false, true>), grid, dim3(kThreads), 0, stream, a);
         else
-            hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, dim3(kThreads), 0, stream, a);
-    } else {
-        if (append)
-            hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, dim3(kThreads), 0, stream, a);
-        else
-            hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, dim3(kThreads), 0, stream, a);
-    }
+            hipLaunchKernelGGL((decode_split_kernel<DD, false, false>), grid, dim3(kThreads), 0, stream, a);
+    };
+    if (p.head_dim == 128)
+        kernel(std::integral_constant<int, 128>());
+    else
+        kernel(std::integral_constant<int, 64>());
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -549,6 +598,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     c.max_splits = p.max_chunks;
     c.capacity = p.max_blocks * p.page_size;
     c.append = p.k_new != nullptr;
+    c.window = a.window;
     c.o = p.o;
     c.o_bf16 = 1;
     c.lse = p.lse;
@@ -568,6 +618,7 @@ hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream)
     c.max_splits = p.max_splits;
     c.capacity = 0;
     c.append = 0;
+    c.window = -1;
     c.o = p.o;
     c.o_bf16 = p.o_bf16 ? 1 : 0;
     c.lse = p.lse;

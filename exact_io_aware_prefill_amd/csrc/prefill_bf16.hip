@@ -53,11 +53,20 @@
 //     longest tiles start first and the causal work stays balanced over time.
 //     (Remapping ids so that each XCD gets a contiguous slice of this list, to
 //     keep a KV head's tiles in one XCD's L2, measured 2% slower.)
+//   * A second instantiation adds a sliding window (row i sees keys i - w .. i;
+//     the tile loop starts at the first tile of row q0's window and tiles that
+//     reach below a row's window are masked as the diagonal is) and logit
+//     soft-capping (each raw score becomes cap * tanh(score / cap) before the
+//     masking), two of the variants the same page's section "Interaction with
+//     post-trained models" lists as ones a kernel must support.  A row can
+//     then meet tiles with no visible key before its window starts; its state
+//     stays empty until it does.
 //
 // This file is compiled with -fno-honor-nans (inputs must be finite): the row
 // max then maps to v_max3_f32 without NaN-quieting copies.  Infinities, which
 // the masking relies on, keep their IEEE meaning.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include "attn_kernels.h"
@@ -102,6 +111,12 @@ struct Args {
     int negate_q;      // 1 when the caller's scale is negative
     float scale_log2;  // |scale| * log2(e)
     float scale;       // |scale|
+    // Variant kernel only.  window >= 0: row i sees keys >= i - window (-1: no
+    // limit).  cap_raw > 0: raw scores x become cap_raw * tanh(x / cap_raw), with
+    // cap_raw = softcap / |scale|, so that x * |scale| is softcap * tanh(s / softcap);
+    // cap_k = 2 log2(e) / cap_raw.
+    int window;
+    float cap_raw, cap_k;
 };
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -246,7 +261,17 @@ __device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[kKB], float sl
     return rs0 + rs1;
 }
 
-template <int D>
+// Logit soft-cap of one raw score: cap * tanh(x / cap), with tanh(y) = 1 - 2 / (e^{2y} + 1)
+// (exact for y -> +-inf: the reciprocal of +inf is 0, of 1 is 1), cap_k = 2 log2(e) / cap.
+__device__ __forceinline__ float soft_cap(float x, float cap, float cap_k)
+{
+    const float r = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(x * cap_k) + 1.f);
+    return fmaf(-2.f * cap, r, cap);
+}
+
+// EXT selects the variant with a sliding window and logit soft-capping (a separate
+// instantiation, so the plain kernel keeps its instruction schedule).
+template <int D, bool EXT>
 __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kernel(Args a)
 {
     constexpr int NT = kWaves * 64;
@@ -342,7 +367,9 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
     }
 
     const int kend = a.causal ? min(N, q0 + kBM) : N;  // keys this tile may see
-    const int ntiles = (kend + kBlockN - 1) / kBlockN;
+    // with a window, the first tile that holds a key of row q0's window
+    const int kbeg = (EXT && a.window >= 0) ? max(0, q0 - a.window) / kBlockN * kBlockN : 0;
+    const int ntiles = (kend - kbeg + kBlockN - 1) / kBlockN;  // >= 1: key q0 is visible to row q0
 
     // ---- prologue ------------------------------------------------------------------
     // V buffers start as zeros: "tile -1" is multiplied by P = 0, and rows past N
@@ -351,8 +378,8 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
         reinterpret_cast<uint4 *>(VB0)[i] = make_uint4(0, 0, 0, 0);
         reinterpret_cast<uint4 *>(VB1)[i] = make_uint4(0, 0, 0, 0);
     }
-    kld.load(kh, N, 0, wave, KB0);
-    if (ntiles > 1) kld.load(kh, N, kBlockN, wave, KB1);
+    kld.load(kh, N, kbeg, wave, KB0);
+    if (ntiles > 1) kld.load(kh, N, kbeg + kBlockN, wave, KB1);
     wait_loads();
     __syncthreads();
     f32x16_t S[kBlocks][kKB];
@@ -371,20 +398,33 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
     // K(t+2) into Kw and V(t) into Vw.
     auto step = [&](bf16x8_t (&Pp)[kBlocks][kKS], bf16x8_t (&Pc)[kBlocks][kKS], int t, const uint16_t *Kn,
                     const uint16_t *Vp, uint16_t *Kw, uint16_t *Vw) {
-        const int k0 = t * kBlockN;
+        const int k0 = kbeg + t * kBlockN;
         if (t + 2 < ntiles) kld.load(kh, N, k0 + 2 * kBlockN, wave, Kw);
         vld.load(vh, N, k0, wave, Vw);
-        // diagonal / ragged tile: mask keys past the row (causal) or past N
-        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > N) {
+        if (EXT && a.cap_raw > 0.f) {  // soft-cap before masking, so masked scores stay -inf
+#pragma unroll
+            for (int bb = 0; bb < kBlocks; ++bb)
+#pragma unroll
+                for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) S[bb][kb][i] = soft_cap(S[bb][kb][i], a.cap_raw, a.cap_k);
+        }
+        // diagonal / ragged tile: mask keys past the row (causal) or past N; with a
+        // window also keys before row - window
+        const bool win = EXT && a.window >= 0 && k0 < wrow0 + kBlocks * 32 - 1 - a.window;
+        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > N || win) {
 #pragma unroll
             for (int bb = 0; bb < kBlocks; ++bb) {
                 const int qrow = wrow0 + 32 * bb + l32;
                 const int lim = (a.causal ? min(qrow, N - 1) : N - 1) - (k0 + 4 * hh);
+                const int low = win ? qrow - a.window - (k0 + 4 * hh) : INT_MIN;
 #pragma unroll
                 for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) S[bb][kb][i] = -INFINITY;
+                    for (int i = 0; i < 16; ++i) {
+                        const int e = 32 * kb + 8 * (i >> 2) + (i & 3);
+                        if (e > lim || (EXT && e < low)) S[bb][kb][i] = -INFINITY;
+                    }
             }
         }
         // ---- matrix cores: PV(t-1); vector ALUs: probabilities of tile t against
@@ -426,14 +466,18 @@ __global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kerne
                     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[bb][kb][i]);
                 mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
                 const float m_new = fmaxf(m[bb], mx);
-                const float c = __builtin_amdgcn_exp2f((m[bb] - m_new) * sl2);  // 0 while m = -inf
+                // 0 while m = -inf.  Only the variant can meet a row with no visible key
+                // yet (m_new = -inf); its state stays (m, l, acc) = (-inf, 0, 0), and a
+                // reference of 0 gives the masked scores probability 0.
+                const bool none = EXT && m_new == -INFINITY;
+                const float c = none ? 1.f : __builtin_amdgcn_exp2f((m[bb] - m_new) * sl2);
                 l[bb] *= c;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) acc[bb][db][i] *= c;
                 m[bb] = m_new;
-                rs[bb] = softmax_tile(S[bb], sl2, m[bb] * sl2, Pc[bb]);
+                rs[bb] = softmax_tile(S[bb], sl2, none ? 0.f : m[bb] * sl2, Pc[bb]);
             }
         }
 #pragma unroll
@@ -523,6 +567,11 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     // exactly 1 (the scale-0 result), and the reference max stays finite.
     a.scale = fmaxf(fabsf(p.scale), 1e-30f);
     a.scale_log2 = a.scale * kLog2e;
+    // a window reaching back past the first key limits nothing
+    a.window = (p.window >= 0 && p.window < p.N) ? p.window : -1;
+    a.cap_raw = p.softcap > 0.f ? p.softcap / a.scale : 0.f;
+    a.cap_k = p.softcap > 0.f ? 2.f * kLog2e / a.cap_raw : 0.f;
+    const bool ext = a.window >= 0 || p.softcap > 0.f;
     const long long items = (long long)a.n_qtiles * p.B * p.Hq;
     if (items == 0) return hipSuccess;
     if (items > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -530,10 +579,18 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     const long long rows = (long long)a.n_qtiles * kBM;
     if (rows * a.q_row * 2 > 0xffffffffLL || rows * a.kv_row * 2 > 0xffffffffLL) return hipErrorInvalidValue;
     a.n_items = (int)items;
-    if (p.head_dim == 128)
-        hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3((unsigned)items), dim3(kWaves * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3((unsigned)items), dim3(kWaves * 64), 0, stream, a);
+    const dim3 grid((unsigned)items), block(kWaves * 64);
+    if (p.head_dim == 128) {
+        if (ext)
+            hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, a);
+    } else {
+        if (ext)
+            hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

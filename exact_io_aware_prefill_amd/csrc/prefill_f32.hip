@@ -7,6 +7,11 @@
 // rounding anywhere, natural-base exponentials from the accurate device math
 // library.  One wave per (sequence, head, 64-row query tile), one query row per
 // lane; 32-key tiles of K and V are staged in LDS and read as broadcasts.
+// Sliding windows and logit soft-capping (two of the variants the page's section
+// "Interaction with post-trained models" lists) are run-time options here:
+// window >= 0 starts the key loop at the tile of row q0 - window and masks keys
+// before row - window; softcap > 0 maps each score s to softcap * tanh(s / softcap)
+// before masking, with the device library's tanhf.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,6 +32,8 @@ struct Args {
     const int32_t *cu_seqlens;
     int B, N, Hq, Hkv, group, causal, n_qtiles, T;
     float scale;
+    int window;     // -1: none
+    float softcap;  // 0: none
 };
 
 template <int D>
@@ -75,7 +82,8 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
     float m = -INFINITY, l = 0.f;
 
     const int kend = a.causal ? min(N, q0 + kRows) : N;
-    for (int k0 = 0; k0 < kend; k0 += kKeys) {
+    const int kbeg = a.window >= 0 ? max(0, q0 - a.window) / kKeys * kKeys : 0;
+    for (int k0 = kbeg; k0 < kend; k0 += kKeys) {
         __syncthreads();
         for (int idx = tid; idx < kKeys * D / 4; idx += kRows) {
             const int r = idx / (D / 4), c = idx % (D / 4);
@@ -97,8 +105,9 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
 #pragma unroll
             for (int d = 0; d < D; ++d) dot = fmaf(q[d], Ks[t * D + d], dot);
             float x = dot * a.scale;
+            if (a.softcap > 0.f) x = a.softcap * tanhf(x / a.softcap);
             const int key = k0 + t;
-            if (key >= N || (a.causal && key > qrow)) x = -INFINITY;
+            if (key >= N || (a.causal && key > qrow) || (a.window >= 0 && key < qrow - a.window)) x = -INFINITY;
             s[t] = x;
             mx = fmaxf(mx, x);
         }
@@ -149,6 +158,8 @@ hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream)
     a.causal = p.causal;
     a.n_qtiles = (p.N + kRows - 1) / kRows;
     a.scale = p.scale;
+    a.window = (p.window >= 0 && p.window < p.N) ? p.window : -1;  // a longer window limits nothing
+    a.softcap = p.softcap > 0.f ? p.softcap : 0.f;
     const long long nblk = (long long)a.n_qtiles * p.B * p.Hq;
     if (nblk == 0) return hipSuccess;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;

@@ -19,6 +19,10 @@
  *   - attn_decode_append: the same decode step with the new token's key and
  *     value written into the cache in place first (section "Minimal
  *     implementation");
+ *   - attn_prefill_ext / attn_decode_ext: the same operations with a sliding
+ *     window and logit soft-capping, two of the attention variants the
+ *     page's section "Interaction with post-trained models" names as ones a
+ *     kernel has to support;
  *   - attn_lse_combine: that reduction on its own -- the combine rule for
  *     independent partials, a softmax over the partials' log-sum-exps
  *     (section "The online softmax, with every symbol defined" and the
@@ -115,6 +119,31 @@ int attn_prefill_varlen(const void *q, const void *k, const void *v, void *o, fl
                         void *stream);
 
 /*
+ * attn_prefill_ext -- attn_prefill (cu_seqlens_or_null == NULL; seqlen is N and
+ * total_tokens is ignored) or attn_prefill_varlen (cu_seqlens_or_null != NULL;
+ * seqlen is max_seqlen), with two options:
+ *
+ *   window_left  -1: no window.  >= 0: the query at position i of its sequence
+ *                also needs key position j >= i - window_left (a sliding window
+ *                of window_left + 1 keys when causal; without causal, keys
+ *                i - window_left .. end).  Below -1 is ATTN_ERR_SHAPE.
+ *   softcap      0: none.  > 0 (finite): each score s = scale * <q, k> becomes
+ *                softcap * tanh(s / softcap) before masking and the softmax;
+ *                negative or non-finite is ATTN_ERR_SHAPE.  dtype ATTN_BF16
+ *                forms tanh(y) as 1 - 2 / (e^{2y} + 1) with the hardware
+ *                exponential and reciprocal (about 1e-7 * softcap absolute error
+ *                in a score); ATTN_F32 calls the device library's tanhf.
+ *   Every row still sees at least its own key (causal) or the last key, so no
+ *   row is empty.  With window_left = -1 and softcap = 0 the results are those
+ *   of attn_prefill / attn_prefill_varlen (the same kernels run).  Layouts,
+ *   element arithmetic, limits and errors as those two calls.
+ */
+int attn_prefill_ext(const void *q, const void *k, const void *v, void *o, float *lse,
+                     const int32_t *cu_seqlens_or_null, int batch, int seqlen, int total_tokens,
+                     int n_q_heads, int n_kv_heads, int head_dim, int dtype, int causal, float scale,
+                     int window_left, float softcap, void *stream);
+
+/*
  * attn_decode -- one new query token per sequence against a KV cache, by
  * split-KV: the first seq_lens[b] tokens of sequence b are cut into chunks of
  * `chunk_tokens`; one workgroup per (sequence, KV head, chunk) computes the
@@ -175,6 +204,22 @@ int attn_decode_append(const void *q, const void *k_new, const void *v_new, void
                        float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim,
                        int page_size, int max_blocks_per_seq, int dtype, float scale, int chunk_tokens,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_ext -- attn_decode (k_new_or_null and v_new_or_null both NULL) or
+ * attn_decode_append (both set; one of them NULL is ATTN_ERR_NULL), with the
+ * options of attn_prefill_ext: the query is token L - 1 of its sequence, where L
+ * is the number of tokens it attends (seq_lens[b], or cache_seqlens[b] + 1 with
+ * the append), so window_left >= 0 limits it to tokens L - 1 - window_left ..
+ * L - 1 (chunks wholly before that are not read); softcap > 0 caps every score
+ * as in attn_prefill_ext (hardware exponential and reciprocal).  Arguments,
+ * workspace, layouts and limits as attn_decode / attn_decode_append.
+ */
+int attn_decode_ext(const void *q, const void *k_new_or_null, const void *v_new_or_null, void *k_cache,
+                    void *v_cache, const int32_t *block_table, const int32_t *seq_lens, void *o,
+                    float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,
+                    int max_blocks_per_seq, int dtype, float scale, int window_left, float softcap,
+                    int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * attn_decode_chunk_tokens -- the chunk size attn_decode uses for these

@@ -103,6 +103,33 @@ def test_prefill_varlen_argument_errors(kw, code):
     assert varlen(**kw) == code
 
 
+def prefill_ext(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu=0, B=2, N=100, T=0, Hq=8, Hkv=2, d=128, dtype=1,
+                causal=1, window=-1, cap=0.0):
+    return attn.lib.attn_prefill_ext(P(q), P(k), P(v), P(o), P(lse), P(cu), B, N, T, Hq, Hkv, d, dtype, causal,
+                                     0.1, window, cap, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-2), attn.ATTN_ERR_SHAPE),
+    (dict(cap=-1.0), attn.ATTN_ERR_SHAPE),
+    (dict(cap=float("inf")), attn.ATTN_ERR_SHAPE),
+    (dict(cap=float("nan")), attn.ATTN_ERR_SHAPE),
+    (dict(window=-2, q=0), attn.ATTN_ERR_SHAPE),          # option errors come before pointer checks
+    (dict(q=0, window=3), attn.ATTN_ERR_NULL),
+    (dict(lse=0, cap=30.0), attn.ATTN_ERR_NULL),
+    (dict(Hq=6, Hkv=4, window=3), attn.ATTN_ERR_GQA),
+    (dict(d=96, cap=5.0), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(o=MIS, window=0), attn.ATTN_ERR_ALIGN),
+    (dict(cu=FAKE + 2, T=250), attn.ATTN_ERR_ALIGN),      # packed: cu_seqlens must be 4-byte aligned
+    (dict(cu=FAKE, T=-1), attn.ATTN_ERR_SHAPE),           # packed: total_tokens >= 0
+    (dict(cu=0, T=-1, q=0, window=5), attn.ATTN_ERR_NULL),  # padded: total_tokens is ignored
+    (dict(B=0, q=0, k=0, v=0, o=0, lse=0, window=7, cap=1.0), attn.ATTN_OK),
+    (dict(cu=FAKE, T=0, q=0, k=0, v=0, o=0, lse=0), attn.ATTN_OK),
+])
+def test_prefill_ext_argument_errors(kw, code):
+    assert prefill_ext(**kw) == code
+
+
 def decode(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, d=128, P_=16,
            maxb=8, dtype=1, chunk=0, ws=FAKE, wsb=1 << 30):
     return attn.lib.attn_decode(P(q), P(kc), P(vc), P(bt), P(sl), P(o), P(lse), B, Hq, Hkv, d, P_,
@@ -153,6 +180,29 @@ def decode_append(q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, 
 ])
 def test_decode_append_argument_errors(kw, code):
     assert decode_append(**kw) == code
+
+
+def decode_ext(q=FAKE, kn=0, vn=0, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, d=128,
+               P_=16, maxb=8, dtype=1, window=-1, cap=0.0, chunk=0, ws=FAKE, wsb=1 << 30):
+    return attn.lib.attn_decode_ext(P(q), P(kn), P(vn), P(kc), P(vc), P(bt), P(sl), P(o), P(lse), B, Hq, Hkv, d,
+                                    P_, maxb, dtype, 0.1, window, cap, chunk, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-5), attn.ATTN_ERR_SHAPE),
+    (dict(cap=-0.5), attn.ATTN_ERR_SHAPE),
+    (dict(cap=float("inf")), attn.ATTN_ERR_SHAPE),
+    (dict(kn=FAKE), attn.ATTN_ERR_NULL),                  # append needs both new rows
+    (dict(vn=FAKE), attn.ATTN_ERR_NULL),
+    (dict(kn=MIS, vn=FAKE), attn.ATTN_ERR_ALIGN),
+    (dict(q=0, window=4), attn.ATTN_ERR_NULL),
+    (dict(d=80, cap=3.0), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=0, window=4), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=0, window=4), attn.ATTN_ERR_WORKSPACE),
+    (dict(B=0, q=0, kc=0, vc=0, bt=0, sl=0, o=0, ws=0, window=4, cap=2.0), attn.ATTN_OK),
+])
+def test_decode_ext_argument_errors(kw, code):
+    assert decode_ext(**kw) == code
 
 
 def test_decode_contiguous_accepts_any_page_size_for_capacity():
