@@ -14,7 +14,7 @@
 namespace {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
 
 // Clear a stale error left by an unrelated earlier call, launch, and map the result.
 template <typename F>

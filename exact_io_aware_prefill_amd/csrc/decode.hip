@@ -12,9 +12,10 @@
 // Lambda) o_k.
 //
 // gfx950 mapping of the split kernel
-//   * 8 waves per workgroup; wave w takes 32-token steps w, w+8, ... of the
-//     chunk with its own online-softmax state; the eight states are merged
-//     through LDS at the end (the same combine rule, inside the workgroup).
+//   * 8 waves per workgroup (4 for head_dim 256); wave w takes 32-token steps
+//     w, w+8, ... of the chunk with its own online-softmax state; the waves'
+//     states are merged through LDS at the end (the same combine rule, inside
+//     the workgroup).
 //   * A step is two 16-token blocks.  A block never crosses a page (pages hold
 //     a multiple of 16 tokens), so each block is addressed through one scalar
 //     buffer descriptor: one block-table lookup per 16 tokens, and tokens past
@@ -59,8 +60,10 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
+// Waves per split workgroup: 8 (two per SIMD).  d = 256 holds twice the K/V
+// registers per step, so its workgroups are 4 waves of one per SIMD, with the
+// same bytes in flight per compute unit.
+template <int D> constexpr int split_waves() { return D == 256 ? 4 : 8; }
 constexpr int kStep = 32;  // tokens per wave step (two 16-token blocks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -121,9 +124,10 @@ __device__ __forceinline__ long long token_index(const SplitArgs &a, int b, int 
     return (long long)b * a.seq_tokens + t;
 }
 
-// slot permutation of the V slab rows (see the header comment)
+// slot permutation of the V slab rows (see the header comment; D = 256 rows are
+// two bank lines and use the D = 128 permutation)
 template <int D>
-__device__ __forceinline__ int slab_swz(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+__device__ __forceinline__ int slab_swz(int r) { return D >= 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
 
 template <int D>
 struct Geo {
@@ -133,6 +137,9 @@ struct Geo {
     static constexpr int VI = kStep / RPI;    // V load instructions per step
     static constexpr int VIB = VI / 2;        // ... per 16-token block
     static constexpr int SLAB = kStep * RB;   // bytes of one wave's slab
+    // the slab permutation repeats every 8 rows: every VP load instructions
+    static constexpr int VP = RPI >= 8 ? 1 : 8 / RPI;
+    static_assert(VI % VP == 0, "whole permutation periods per step");
 };
 
 // Registers of one step: K as score A operands [block][k-step], V rows as loaded.
@@ -210,7 +217,7 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
     // these stores land after the previous step's transpose reads of the slab.
 #pragma unroll
     for (int i = 0; i < Gm::VI; ++i)
-        *reinterpret_cast<uint4 *>(slab + vstore[i % 2] + (i & ~1) * Gm::RPI * Gm::RB) = s.v[i];
+        *reinterpret_cast<uint4 *>(slab + vstore[i % Gm::VP] + (i - i % Gm::VP) * Gm::RPI * Gm::RB) = s.v[i];
 
     // online softmax over this step (lane: query l16, tokens 4G+i of each block)
     const bool tail = tb + kStep > t_end || (EXT && tb < t_lo);
@@ -261,9 +268,10 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
 // APPEND selects the in-place append variant, EXT the window / soft-cap variant
 // (separate instantiations, so the plain decode keeps its register budget).
 template <int D, bool APPEND, bool EXT>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
+__global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(SplitArgs a)
 {
     using Gm = Geo<D>;
+    constexpr int kWaves = split_waves<D>();
     // one slab per wave; reused at the end for the eight waves' [16][D] float outputs
     static_assert(Gm::SLAB == 16 * D * 4, "slab must hold a wave's 16 x D float output");
     __shared__ __attribute__((aligned(1024))) char slabs[kWaves * Gm::SLAB];
@@ -308,12 +316,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
     lo.k = (uint32_t)l16 * rstride + 16u * G;
     lo.v = (uint32_t)lo.vtok * rstride + 16u * vchunk;
     char *slab = slabs + wave * Gm::SLAB;
-    // slab byte offsets of this lane's V row stores for even and odd load
-    // instructions (instruction i covers rows i*RPI..; the slot permutation
-    // repeats every 8 rows, i.e. every two instructions for D = 128)
-    uint32_t vstore[2];
+    // slab byte offsets of this lane's V row stores by load instruction modulo
+    // VP (instruction i covers rows i*RPI..; the slot permutation repeats every
+    // 8 rows, i.e. every two instructions for D = 128, four for D = 256)
+    uint32_t vstore[Gm::VP];
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
+    for (int par = 0; par < Gm::VP; ++par) {
         const int r = Gm::RPI * par + lo.vtok;
         vstore[par] = (uint32_t)(r * Gm::RB + 16 * (vchunk ^ slab_swz<D>(r)));
     }
@@ -382,23 +390,28 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(SplitArgs a)
 #pragma unroll
     for (int nb = 0; nb < D / 16; ++nb) *reinterpret_cast<f32x4_t *>(&wo[l16 * D + 4 * ((4 * nb + G) ^ l16)]) = acc[nb];
     __syncthreads();
-    // wave w merges d-block w of the eight waves and writes the chunk's partial
+    // wave w merges d-blocks w, w + kWaves, ... of all waves and writes the chunk's partial
     if (wave < D / 16 && l16 < g) {
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[0][w][l16]);
-        float Lsum = 0.f;
-        f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+        float Lsum = 0.f, e[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float e = __builtin_amdgcn_exp2f(ml[0][w][l16] - M);  // 0 for a wave that saw no token
-            Lsum += e * ml[1][w][l16];
-            sum += e * *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(slabs + w * Gm::SLAB) +
-                                                          l16 * D + 4 * ((4 * wave + G) ^ l16));
+            e[w] = __builtin_amdgcn_exp2f(ml[0][w][l16] - M);  // 0 for a wave that saw no token
+            Lsum += e[w] * ml[1][w][l16];
         }
         const size_t row = (size_t)b * a.Hq + (size_t)hk * g + l16;
         const float inv = 1.f / Lsum;  // Lsum >= 1: the row's largest term is exp2(0)
-        *reinterpret_cast<f32x4_t *>(&a.o_parts[(row * a.max_chunks + chunk) * D + 16 * wave + 4 * G]) = sum * inv;
+#pragma unroll
+        for (int nb = wave; nb < D / 16; nb += kWaves) {
+            f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+                sum += e[w] * *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(slabs + w * Gm::SLAB) +
+                                                                 l16 * D + 4 * ((4 * nb + G) ^ l16));
+            *reinterpret_cast<f32x4_t *>(&a.o_parts[(row * a.max_chunks + chunk) * D + 16 * nb + 4 * G]) = sum * inv;
+        }
         if (wave == 0 && G == 0) a.lse_parts[row * a.max_chunks + chunk] = (M + log2f(Lsum)) * kLn2;
     }
 }
@@ -539,6 +552,13 @@ hipError_t launch_combine(const CombineArgs &c, int rows, hipStream_t stream)
     return hipGetLastError();
 }
 
+hipError_t launch_combine_d(int head_dim, const CombineArgs &c, int rows, hipStream_t stream)
+{
+    if (head_dim == 128) return launch_combine<128>(c, rows, stream);
+    if (head_dim == 64) return launch_combine<64>(c, rows, stream);
+    return launch_combine<256>(c, rows, stream);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
@@ -572,6 +592,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     const bool append = a.k_new != nullptr;
     auto kernel = [&](auto dconst) {
         constexpr int DD = decltype(dconst)::value;
+        constexpr int kThreads = split_waves<DD>() * 64;
         if (append && ext)
             hipLaunchKernelGGL((decode_split_kernel<DD, true, true>), grid, dim3(kThreads), 0, stream, a);
         else if (append)
@@ -583,8 +604,10 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     };
     if (p.head_dim == 128)
         kernel(std::integral_constant<int, 128>());
-    else
+    else if (p.head_dim == 64)
         kernel(std::integral_constant<int, 64>());
+    else
+        kernel(std::integral_constant<int, 256>());
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -603,7 +626,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     c.o_bf16 = 1;
     c.lse = p.lse;
     const int rows = p.B * p.Hq;
-    return p.head_dim == 128 ? launch_combine<128>(c, rows, stream) : launch_combine<64>(c, rows, stream);
+    return launch_combine_d(p.head_dim, c, rows, stream);
 }
 
 hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream)
@@ -622,7 +645,7 @@ hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream)
     c.o = p.o;
     c.o_bf16 = p.o_bf16 ? 1 : 0;
     c.lse = p.lse;
-    return p.head_dim == 128 ? launch_combine<128>(c, p.rows, stream) : launch_combine<64>(c, p.rows, stream);
+    return launch_combine_d(p.head_dim, c, p.rows, stream);
 }
 
 }  // namespace attn

@@ -12,9 +12,10 @@
 //
 // gfx950 mapping
 //   * workgroup = 4 waves x 32 query rows (128 rows); key/value tile = 32 keys.
-//     The kernel fits in 166 VGPRs so three workgroups (three waves per SIMD)
-//     are resident per compute unit: the operand reads from LDS are the
-//     limiter, and the other waves' matrix work covers each wave's LDS latency.
+//     The kernel fits in 166 VGPRs (d = 128) so three workgroups (three waves
+//     per SIMD) are resident per compute unit: the operand reads from LDS are
+//     the limiter, and the other waves' matrix work covers each wave's LDS
+//     latency.  d = 256 runs two waves per SIMD.
 //     (kBlocks > 1 would give each wave several 32-row blocks sharing every K
 //     and V operand read, at the cost of registers and hence resident waves.)
 //   * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
@@ -69,6 +70,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "attn_kernels.h"
 
 namespace attn {
@@ -83,7 +86,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kWaves = 4;      // waves per workgroup
 constexpr int kBlocks = 1;     // 32-row query blocks per wave
-constexpr int kWavesPerSimd = 3;  // resident waves per SIMD the register budget is sized for
+constexpr int kWavesPerSimd = 3;  // resident waves per SIMD the register budget is sized for (d <= 128)
 constexpr int kBM = kWaves * kBlocks * 32;  // query rows per workgroup
 constexpr int kBlockN = 32;    // keys per tile
 constexpr int kKB = kBlockN / 32;  // 32-key score blocks per tile
@@ -131,18 +134,29 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// Resident waves per SIMD the register budget is sized for.  d = 256 keeps twice
+// the Q fragments and accumulators in registers (about 330 live values), so it
+// runs two waves per SIMD and spills the excess to scratch: measured faster than
+// one wave per SIMD with every value in (accumulation) registers, whose operand
+// latency is then exposed.
+template <int D> constexpr int waves_per_simd() { return D == 256 ? 2 : kWavesPerSimd; }
+
 // Chunk permutations of the LDS tiles (16-byte chunk c of key row r sits at
 // slot c ^ swz(r)).  D = 128: a row is one 256-byte bank line; the K operand
 // reads of 16 consecutive rows and the V transpose reads of 4 rows x 64 bytes
-// land on distinct banks.  D = 64: two rows share a bank line.
-template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D> __device__ __forceinline__ int v_swz(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+// land on distinct banks.  D = 256: a row is two bank lines, same permutation.
+// D = 64: two rows share a bank line.
+template <int D> __device__ __forceinline__ int k_swz(int r) { return D >= 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D> __device__ __forceinline__ int v_swz(int r) { return D >= 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
-// Memory -> LDS loader of one K or V tile (64 rows of D bf16).  A tile is
-// 64*D/8 chunks = D/8 wave instructions of 64 chunks (1 KiB each); wave w issues
+// Memory -> LDS loader of one K or V tile (32 rows of D bf16).  A tile is
+// 32*D/8 chunks = D/16 wave instructions of 64 chunks (1 KiB each); wave w issues
 // instructions w, w + 4, ...  With that interleave the slot a lane fills has the
-// same row permutation in all of its instructions, so one per-lane offset serves
-// them all and the per-instruction part goes into the (scalar) buffer base.
+// same row permutation in all of its instructions (d <= 128), so one per-lane
+// offset serves them all and the per-instruction part goes into the (scalar)
+// buffer base.  D = 256: an instruction covers 2 rows, so a lane's rows are 8
+// apart and the K permutation (r & 15) alternates; odd instructions flip bit 3 of
+// the chunk slot (`odd_xor`), the V permutation (r & 3) does not change.
 template <int D>
 struct TileLoader {
     static constexpr int RB = D * 2;                 // bytes per key row
@@ -154,8 +168,10 @@ struct TileLoader {
     // a lane's instructions fill rows 4*kWaves apart (D = 128) or 8*kWaves apart
     // (D = 64); with kWaves a multiple of 4 those rows share their permutation
     static_assert(kWaves % 4 == 0, "one per-lane offset needs kWaves to be a multiple of 4");
-    uint32_t voff;  // per-lane byte offset from the first row an instruction fills
-    uint32_t rowb;  // bytes between consecutive key rows in memory
+    static_assert(D != 256 || kWaves == 4, "the d = 256 odd-instruction flip assumes 4 waves");
+    uint32_t voff;     // per-lane byte offset from the first row an instruction fills
+    uint32_t rowb;     // bytes between consecutive key rows in memory
+    uint32_t odd_xor;  // D = 256: offset flip of odd instructions (0 when the permutation repeats)
 
     template <typename Swz>
     __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes, Swz swz)
@@ -164,6 +180,8 @@ struct TileLoader {
         const int r = u / NC, pos = u % NC;
         rowb = row_bytes;
         voff = (uint32_t)(lane / NC) * row_bytes + 16u * (uint32_t)(pos ^ swz(r));
+        // the lane's row in an odd instruction is r + RPI * kWaves
+        odd_xor = 16u * (uint32_t)(swz(r) ^ swz(r + RPI * kWaves));
     }
     // Issue the loads of the tile starting at key k0 of one head (rows rowb apart,
     // n rows) into the LDS tile `dst`.  Each instruction's descriptor starts at its
@@ -180,7 +198,8 @@ struct TileLoader {
             const uint32_t rec = __builtin_amdgcn_readfirstlane((uint32_t)min(left, 0xFFFFFFFFLL));
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(reinterpret_cast<const char *>(head) + (long long)row0 * rowb, rec);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)((char *)dst + ins * 1024), 16, voff, 0, 0, 0);
+            const uint32_t off = (D == 256 && (i & 1)) ? (voff ^ odd_xor) : voff;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)((char *)dst + ins * 1024), 16, off, 0, 0, 0);
         }
     }
 };
@@ -272,7 +291,7 @@ __device__ __forceinline__ float soft_cap(float x, float cap, float cap_k)
 // EXT selects the variant with a sliding window and logit soft-capping (a separate
 // instantiation, so the plain kernel keeps its instruction schedule).
 template <int D, bool EXT>
-__global__ __launch_bounds__(kWaves * 64, kWavesPerSimd) void prefill_bf16_kernel(Args a)
+__global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16_kernel(Args a)
 {
     constexpr int NT = kWaves * 64;
     constexpr int TE = kBlockN * D;  // elements per K or V tile
@@ -580,17 +599,19 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     if (rows * a.q_row * 2 > 0xffffffffLL || rows * a.kv_row * 2 > 0xffffffffLL) return hipErrorInvalidValue;
     a.n_items = (int)items;
     const dim3 grid((unsigned)items), block(kWaves * 64);
-    if (p.head_dim == 128) {
+    auto launch = [&](auto dconst) {
+        constexpr int DD = decltype(dconst)::value;
         if (ext)
-            hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, a);
+            hipLaunchKernelGGL((prefill_bf16_kernel<DD, true>), grid, block, 0, stream, a);
         else
-            hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, a);
-    } else {
-        if (ext)
-            hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, a);
-        else
-            hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, a);
-    }
+            hipLaunchKernelGGL((prefill_bf16_kernel<DD, false>), grid, block, 0, stream, a);
+    };
+    if (p.head_dim == 128)
+        launch(std::integral_constant<int, 128>());
+    else if (p.head_dim == 64)
+        launch(std::integral_constant<int, 64>());
+    else
+        launch(std::integral_constant<int, 256>());
     return hipGetLastError();
 }
 

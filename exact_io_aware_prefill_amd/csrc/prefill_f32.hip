@@ -5,8 +5,12 @@
 // tensor cores" and "The online softmax, with every symbol defined"), for
 // float32 inputs whose results must stay within float32 rounding: no bf16
 // rounding anywhere, natural-base exponentials from the accurate device math
-// library.  One wave per (sequence, head, 64-row query tile), one query row per
-// lane; 32-key tiles of K and V are staged in LDS and read as broadcasts.
+// library.  One wave per (sequence, head, query tile); 32-key tiles of K and V are
+// staged in LDS and read as broadcasts.  Head dims up to 128 take one query row per
+// lane (64-row tiles); d = 256 splits each row over two lanes (lane r and r + 32
+// hold dims 0..127 and 128..255 of row r; 32-row tiles), which add their partial
+// dot products with one cross-lane exchange, so q and the accumulator fit in
+// registers.
 // Sliding windows and logit soft-capping (two of the variants the page's section
 // "Interaction with post-trained models" lists) are run-time options here:
 // window >= 0 starts the key loop at the tile of row q0 - window and masks keys
@@ -20,8 +24,10 @@
 namespace attn {
 namespace {
 
-constexpr int kRows = 64;  // query rows per workgroup (one wave)
-constexpr int kKeys = 32;  // keys per tile
+constexpr int kLanes = 64;  // one wave per workgroup
+constexpr int kKeys = 32;   // keys per tile
+template <int D> constexpr int lanes_per_row() { return D > 128 ? 2 : 1; }
+template <int D> constexpr int rows_per_tile() { return kLanes / lanes_per_row<D>(); }
 
 // Padded batch: q, o [B, Hq, N, d], k, v [B, Hkv, N, d], lse [B, Hq, N]
 // (cu_seqlens NULL).  Packed variable-length batch: sequence b is tokens
@@ -37,18 +43,22 @@ struct Args {
 };
 
 template <int D>
-__global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
+__global__ __launch_bounds__(kLanes) void prefill_f32_kernel(Args a)
 {
+    constexpr int LPR = lanes_per_row<D>();
+    constexpr int ROWS = rows_per_tile<D>();
+    constexpr int DH = D / LPR;  // dims held by one lane
     __shared__ __attribute__((aligned(16))) float Ks[kKeys * D];
     __shared__ __attribute__((aligned(16))) float Vs[kKeys * D];
 
     const int tid = threadIdx.x;
+    const int half = tid / ROWS;  // which dims of its row this lane holds (0 unless d = 256)
     const int nbh = a.B * a.Hq;
     const int qtile = a.n_qtiles - 1 - (int)(blockIdx.x / nbh);
     const int bh = (int)(blockIdx.x % nbh);
     const int b = bh / a.Hq, h = bh % a.Hq, hk = h / a.group;
-    const int q0 = qtile * kRows;
-    const int qrow = q0 + tid;
+    const int q0 = qtile * ROWS;
+    const int qrow = q0 + tid % ROWS;
     // this sequence's rows: first element of row 0 and the stride between rows
     int N;
     size_t qbase, kvbase, qstride, kvstride, lsebase;
@@ -73,19 +83,19 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
     const float *kp = a.k + kvbase;
     const float *vp = a.v + kvbase;
 
-    float q[D], acc[D];
+    float q[DH], acc[DH];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-        q[d] = (qrow < N) ? a.q[qbase + (size_t)qrow * qstride + d] : 0.f;
+    for (int d = 0; d < DH; ++d) {
+        q[d] = (qrow < N) ? a.q[qbase + (size_t)qrow * qstride + half * DH + d] : 0.f;
         acc[d] = 0.f;
     }
     float m = -INFINITY, l = 0.f;
 
-    const int kend = a.causal ? min(N, q0 + kRows) : N;
+    const int kend = a.causal ? min(N, q0 + ROWS) : N;
     const int kbeg = a.window >= 0 ? max(0, q0 - a.window) / kKeys * kKeys : 0;
     for (int k0 = kbeg; k0 < kend; k0 += kKeys) {
         __syncthreads();
-        for (int idx = tid; idx < kKeys * D / 4; idx += kRows) {
+        for (int idx = tid; idx < kKeys * D / 4; idx += kLanes) {
             const int r = idx / (D / 4), c = idx % (D / 4);
             float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
             if (k0 + r < N) {
@@ -103,7 +113,9 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
         for (int t = 0; t < kKeys; ++t) {
             float dot = 0.f;
 #pragma unroll
-            for (int d = 0; d < D; ++d) dot = fmaf(q[d], Ks[t * D + d], dot);
+            for (int d = 0; d < DH; ++d) dot = fmaf(q[d], Ks[t * D + half * DH + d], dot);
+            // both lanes of a row form the same sum (float addition commutes)
+            if (LPR == 2) dot += __shfl_xor(dot, ROWS);
             float x = dot * a.scale;
             if (a.softcap > 0.f) x = a.softcap * tanhf(x / a.softcap);
             const int key = k0 + t;
@@ -116,28 +128,28 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(Args a)
         const float c = expf(m - m_use);
         l *= c;
 #pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] *= c;
+        for (int d = 0; d < DH; ++d) acc[d] *= c;
 #pragma unroll
         for (int t = 0; t < kKeys; ++t) {
             const float p = expf(s[t] - m_use);
             l += p;
 #pragma unroll
-            for (int d = 0; d < D; ++d) acc[d] = fmaf(p, Vs[t * D + d], acc[d]);
+            for (int d = 0; d < DH; ++d) acc[d] = fmaf(p, Vs[t * D + half * DH + d], acc[d]);
         }
         m = m_new;
     }
 
     if (qrow < N) {
-        float *orow = a.o + qbase + (size_t)qrow * qstride;
+        float *orow = a.o + qbase + (size_t)qrow * qstride + half * DH;
         if (l > 0.f) {
             const float inv = 1.f / l;
 #pragma unroll
-            for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
-            a.lse[lsebase + qrow] = m + logf(l);
+            for (int d = 0; d < DH; ++d) orow[d] = acc[d] * inv;
+            if (half == 0) a.lse[lsebase + qrow] = m + logf(l);
         } else {  // no visible key (not reachable for square causal or full attention)
 #pragma unroll
-            for (int d = 0; d < D; ++d) orow[d] = 0.f;
-            a.lse[lsebase + qrow] = -INFINITY;
+            for (int d = 0; d < DH; ++d) orow[d] = 0.f;
+            if (half == 0) a.lse[lsebase + qrow] = -INFINITY;
         }
     }
 }
@@ -156,7 +168,8 @@ hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream)
     a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.group = p.Hq / p.Hkv;
     a.T = p.cu_seqlens ? p.total : p.B * p.N;
     a.causal = p.causal;
-    a.n_qtiles = (p.N + kRows - 1) / kRows;
+    const int rows = p.head_dim == 256 ? rows_per_tile<256>() : rows_per_tile<128>();
+    a.n_qtiles = (p.N + rows - 1) / rows;
     a.scale = p.scale;
     a.window = (p.window >= 0 && p.window < p.N) ? p.window : -1;  // a longer window limits nothing
     a.softcap = p.softcap > 0.f ? p.softcap : 0.f;
@@ -164,9 +177,11 @@ hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream)
     if (nblk == 0) return hipSuccess;
     if (nblk > 0x7fffffffLL) return hipErrorInvalidValue;
     if (p.head_dim == 128)
-        hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((unsigned)nblk), dim3(kRows), 0, stream, a);
+        hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((unsigned)nblk), dim3(kLanes), 0, stream, a);
+    else if (p.head_dim == 64)
+        hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((unsigned)nblk), dim3(kLanes), 0, stream, a);
     else
-        hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((unsigned)nblk), dim3(kRows), 0, stream, a);
+        hipLaunchKernelGGL(prefill_f32_kernel<256>, dim3((unsigned)nblk), dim3(kLanes), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -50,6 +50,8 @@
  *     LSE = -inf.
  *   - Grouped-query attention: query head h reads KV head h / (n_q_heads /
  *     n_kv_heads) (consecutive query heads share a KV head).
+ *   - Head sizes 64, 128 and 256 (256 being the largest the page's section
+ *     "Interaction with post-trained models" names) on every entry point.
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -83,7 +85,7 @@ extern "C" {
  *   o    [batch, n_q_heads,  seqlen, head_dim]  element type `dtype` (written)
  *   lse  [batch, n_q_heads,  seqlen] float32, row log-sum-exp (written; required)
  *   causal != 0: row i attends keys 0..i; causal == 0: all keys.
- *   head_dim in {64, 128}; dtype ATTN_BF16 (matrix cores, bf16 products with
+ *   head_dim in {64, 128, 256}; dtype ATTN_BF16 (matrix cores, bf16 products with
  *   float32 accumulation; P is rounded to bf16 before the P*V product; O is
  *   rounded to nearest even) or ATTN_F32 (float32 arithmetic throughout).
  *   batch, seqlen >= 0 (an empty call does nothing); heads >= 1;
@@ -168,7 +170,7 @@ int attn_prefill_ext(const void *q, const void *k, const void *v, void *o, float
  *               partials; contents on entry are ignored.
  *   Size limits (else ATTN_ERR_UNSUPPORTED): batch <= 65535, batch*n_q_heads < 2^24,
  *   chunks per sequence < 2^22 and chunks per sequence * n_kv_heads < 2^23.
- *   head_dim in {64, 128}; n_q_heads / n_kv_heads <= 16; dtype ATTN_BF16 only
+ *   head_dim in {64, 128, 256}; n_q_heads / n_kv_heads <= 16; dtype ATTN_BF16 only
  *   (bf16 products on matrix cores with float32 accumulation, P rounded to bf16
  *   before the P*V product, partials and the combine in float32, O rounded to
  *   nearest even).  A paged cache needs page_size a multiple of 16 (no 16-token
@@ -247,7 +249,7 @@ size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
  *   o         [rows, head_dim] element type `o_dtype` (ATTN_F32 or ATTN_BF16)
  *   lse_or_null [rows] float32 (written when not NULL)
  *   A row whose partials are all empty gets o = 0, Lambda = -inf.
- *   head_dim in {64, 128}; rows >= 0; 1 <= max_splits < 2^22 and rows < 2^24
+ *   head_dim in {64, 128, 256}; rows >= 0; 1 <= max_splits < 2^22 and rows < 2^24
  *   (larger is ATTN_ERR_UNSUPPORTED).
  */
 int attn_lse_combine(const float *o_parts, const float *lse_parts,

@@ -67,7 +67,8 @@ def prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, N=16, Hq=4, Hkv=2, d=
     (dict(d=0), attn.ATTN_ERR_SHAPE),
     (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
     (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
-    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=512), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=32), attn.ATTN_ERR_UNSUPPORTED),
     (dict(dtype=7), attn.ATTN_ERR_UNSUPPORTED),
     (dict(k=MIS), attn.ATTN_ERR_ALIGN),
     (dict(o=MIS), attn.ATTN_ERR_ALIGN),

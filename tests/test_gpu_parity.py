@@ -134,7 +134,7 @@ def test_worked_example_through_lse_combine(attn):
     assert (o[0, 1:] == 0).all()
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
 def test_lse_combine_random_partials(attn, d, odt):
     say("case: lse_combine random partials d=%d out=%s" % (d, odt))
