@@ -608,3 +608,25 @@ def test_softcap_limits():
         mean = v[0, :, : i + 1].mean(axis=1)
         assert np.max(np.abs(ot[0, :, i] - mean)) <= 4 * c * float(np.max(np.abs(v))) + 1e-12
         assert np.max(np.abs(lt[0, :, i] - np.log(i + 1))) <= c + 1e-12
+
+
+def test_softcap_applies_to_the_scaled_score():
+    """The cap bounds the scaled score s = scale * <q, k>, not the raw dot product: with a
+    large scale and a tiny cap every capped score is still within +-cap, so the weights
+    stay uniform (capping <q, k> first and scaling after would leave scores up to
+    scale * cap apart and fail the bound below)."""
+    rng = np.random.default_rng(54)
+    B, Hq, Hkv, N, d = 1, 2, 1, 24, 8
+    q = rng.standard_normal((B, Hq, N, d))
+    k = rng.standard_normal((B, Hkv, N, d)); v = rng.standard_normal((B, Hkv, N, d))
+    scale, c = 40.0, 1e-3
+    ot, lt = oracle.prefill(q, k, v, True, scale, softcap=c)
+    for i in range(N):
+        mean = v[0, 0, : i + 1].mean(axis=0)
+        assert np.max(np.abs(ot[0, :, i] - mean)) <= 4 * c * float(np.max(np.abs(v))) + 1e-12
+        assert np.max(np.abs(lt[0, :, i] - np.log(i + 1))) <= c + 1e-12
+    # the same holds for decode of the last token
+    kc = k[0].transpose(1, 0, 2)[None].copy()  # [1, N, Hkv, d]
+    vc = v[0].transpose(1, 0, 2)[None].copy()
+    od, ld = oracle.decode(q[:, :, N - 1], kc, vc, None, np.array([N], dtype=np.int32), scale, N, 1, softcap=c)
+    assert np.max(np.abs(od[0] - v[0, 0].mean(axis=0))) <= 4 * c * float(np.max(np.abs(v))) + 1e-12
