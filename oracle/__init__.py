@@ -62,6 +62,8 @@ def _load():
         lib.oracle_lse_combine.argtypes = [P, P, P, i, i, i, P, P]
         lib.oracle_online_trace.argtypes = [P, P, i, i, P, P, P, P, P, P]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_e4m3_decode.argtypes = [P, P, ctypes.c_int64]
+        lib.oracle_e4m3_decode.restype = ctypes.c_int
         for f in (lib.oracle_prefill, lib.oracle_prefill_ext, lib.oracle_decode_ext,
                   lib.oracle_prefill_tiled, lib.oracle_decode,
                   lib.oracle_split_decode, lib.oracle_lse_combine, lib.oracle_online_trace,
@@ -256,3 +258,45 @@ def online_trace(scores, values, block: int):
         raise ValueError("oracle_online_trace rejected its arguments")
     return {"m": m[:cnt], "l": l[:cnt], "o_tilde": ot[:cnt], "c": c[:cnt],
             "o": float(o[0]), "lse": float(lse[0])}
+
+
+def _u8(a) -> np.ndarray:
+    """Contiguous uint8 view of byte codes (torch float8 / uint8 tensors or arrays)."""
+    if hasattr(a, "detach"):
+        a = a.detach().cpu()
+        if a.dtype != __import__("torch").uint8:
+            a = a.view(__import__("torch").uint8)
+        a = a.numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.uint8))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """FP8 E4M3 (OCP, finite-only variant) byte codes -> float64 values, from the
+    format definition in oracle.c (NaN for the two NaN codes)."""
+    c = _u8(codes)
+    out = np.empty(c.shape, dtype=np.float64)
+    if _load().oracle_e4m3_decode(_p(c), _p(out), c.size) != 0:
+        raise ValueError("oracle_e4m3_decode rejected its arguments")
+    return out
+
+
+def prefill_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale: float):
+    """Attention on FP8 inputs: the plain prefill of the dequantised tensors.
+
+    q8 [B, Hq, N, d], k8, v8 [B, Hkv, N, d] are E4M3 byte codes; descale_* are
+    [B, Hkv] float factors (None = 1), shared by the query heads of one KV head:
+    Q = descale_q[b, h / g] * decode(q8), K and V likewise.  The result is
+    prefill(Q, K, V, causal, scale) in float64 -- what the method computes on the
+    dequantised inputs, with no rounding of the probabilities."""
+    q, k, v = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    g = Hq // Hkv
+
+    def ds(x):
+        return np.ones((B, Hkv)) if x is None else _f64(x).reshape(B, Hkv)
+    dq, dk, dv = ds(descale_q), ds(descale_k), ds(descale_v)
+    q = q * np.repeat(dq, g, axis=1)[:, :, None, None]
+    k = k * dk[:, :, None, None]
+    v = v * dv[:, :, None, None]
+    return prefill(q, k, v, causal, scale)

@@ -487,6 +487,36 @@ int oracle_split_decode(const double *q, const double *k_cache, const double *v_
 }
 
 /* number of OpenMP threads the oracle will use */
+/* ------------------------------------------------------------------------ */
+/* FP8 inputs.  One byte in the OCP 8-bit floating-point format E4M3 (the    */
+/* "FN" variant: finite values only): bit 7 sign, bits 6..3 exponent with    */
+/* bias 7, bits 2..0 mantissa.  Exponent field 0 holds subnormals            */
+/* (mantissa / 8 * 2^-6); the code with every exponent and mantissa bit set  */
+/* (0x7f, 0xff) is NaN; there is no infinity, so the largest value is        */
+/* 1.75 * 2^8 = 448.  Written from that definition; the pages name FP8       */
+/* attention ([pofe] "The bottleneck it attacks", the FlashAttention-3 line) */
+/* but not its format, which is the one the gfx950 matrix cores take.        */
+/* ------------------------------------------------------------------------ */
+double oracle_e4m3_value(uint8_t code)
+{
+    const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+int oracle_e4m3_decode(const uint8_t *in, double *out, int64_t n)
+{
+    if (n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_value(in[i]);
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -630,3 +630,65 @@ def test_softcap_applies_to_the_scaled_score():
     vc = v[0].transpose(1, 0, 2)[None].copy()
     od, ld = oracle.decode(q[:, :, N - 1], kc, vc, None, np.array([N], dtype=np.int32), scale, N, 1, softcap=c)
     assert np.max(np.abs(od[0] - v[0, 0].mean(axis=0))) <= 4 * c * float(np.max(np.abs(v))) + 1e-12
+
+
+# ---------------------------------------------------------------- FP8 (E4M3) inputs
+def test_e4m3_decode_matches_the_format_and_torch():
+    """Every byte code decodes as PyTorch's float8_e4m3fn does (a library routine), and
+    the format's landmarks hold: largest 448, smallest normal 2^-6, smallest subnormal
+    2^-9, 1.0 = 0x38, the sign bit, and NaN only at 0x7f / 0xff."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert np.flatnonzero(np.isnan(got)).tolist() == [0x7f, 0xff]
+    assert got[0x7e] == 448.0 and np.nanmax(got) == 448.0
+    assert got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9 and got[0x07] == 7 * 2.0 ** -9
+    assert got[0x38] == 1.0 and got[0xb8] == -1.0 and got[0x00] == 0.0 and np.signbit(got[0x80])
+    # within a binade the 8 mantissa steps are 1/8 apart
+    assert np.allclose(np.diff(got[0x38:0x40]), 0.125, rtol=0, atol=0)
+
+
+def test_fp8_prefill_reproduces_the_worked_example():
+    """The page's worked example with every value exact in E4M3 (codes written by hand
+    from the format: 1 = 0x38, 2 = 0x40, 3 = 0x44, 4 = 0x48, -1 = 0xb8, 0 = 0x00):
+    row 3 is the printed 1.1381 and the closed form."""
+    N, d = 4, 16
+    q8 = np.zeros((1, 1, N, d), np.uint8); k8 = np.zeros_like(q8); v8 = np.zeros_like(q8)
+    q8[0, 0, :, 0] = 0x38
+    k8[0, 0, :, 0] = [0x40, 0x38, 0x48, 0x44]
+    v8[0, 0, :, 0] = [0x38, 0x00, 0x40, 0xb8]
+    o, lse = oracle.prefill_fp8(q8, k8, v8, None, None, None, True, 1.0)
+    e = math.e
+    assert abs(o[0, 0, 3, 0] - (e**2 + 2 * e**4 - e**3) / (e**2 + e + e**4 + e**3)) < 1e-12
+    assert round(o[0, 0, 3, 0], 4) == 1.1381
+    assert abs(lse[0, 0, 3] - math.log(e**2 + e + e**4 + e**3)) < 1e-12
+
+
+def test_fp8_prefill_descale_invariants():
+    """Descales are per (sequence, KV head) multipliers of the decoded values: doubling
+    descale_q and halving scale changes nothing; tripling descale_v triples O and keeps
+    the LSE; changing one KV head's descale_k changes only that group's query heads."""
+    rng = np.random.default_rng(61)
+    B, Hq, Hkv, N, d = 2, 4, 2, 40, 16
+    codes = lambda shape: rng.integers(0, 256, size=shape).astype(np.uint8) & 0x7e | (
+        rng.integers(0, 2, size=shape).astype(np.uint8) << 7)  # no NaN codes, and both signs
+    q8, k8, v8 = codes((B, Hq, N, d)), codes((B, Hkv, N, d)), codes((B, Hkv, N, d))
+    # keep scores moderate: small exponents only
+    q8 &= 0xbf; k8 &= 0xbf
+    dq = rng.uniform(0.001, 0.01, (B, Hkv)); dk = rng.uniform(0.001, 0.01, (B, Hkv)); dv = rng.uniform(0.5, 2, (B, Hkv))
+    o, lse = oracle.prefill_fp8(q8, k8, v8, dq, dk, dv, True, 0.25)
+    o2, lse2 = oracle.prefill_fp8(q8, k8, v8, 2 * dq, dk, dv, True, 0.125)
+    assert np.max(np.abs(o2 - o)) < 1e-12 and np.max(np.abs(lse2 - lse)) < 1e-12
+    o3, lse3 = oracle.prefill_fp8(q8, k8, v8, dq, dk, 3 * dv, True, 0.25)
+    assert np.max(np.abs(o3 - 3 * o)) < 1e-12 and np.max(np.abs(lse3 - lse)) < 1e-12
+    dk2 = dk.copy(); dk2[1, 0] *= 2
+    o4, lse4 = oracle.prefill_fp8(q8, k8, v8, dq, dk2, dv, True, 0.25)
+    g = Hq // Hkv
+    changed = np.zeros((B, Hq), bool); changed[1, 0:g] = True
+    assert np.array_equal(o4[~changed], o[~changed]) and np.array_equal(lse4[~changed], lse[~changed])
+    assert np.max(np.abs(o4[changed] - o[changed])) > 1e-6
+    # the changed group equals the same call with the scale doubled for that sequence
+    o5, lse5 = oracle.prefill_fp8(q8[1:], k8[1:], v8[1:], dq[1:], dk[1:], dv[1:], True, 0.5)
+    assert np.max(np.abs(o5[0, 0:g] - o4[1, 0:g])) < 1e-12
