@@ -30,7 +30,8 @@ ATTN_ERR_HIP = -7
 ATTN_F32 = 0
 ATTN_BF16 = 1
 
-EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_ext", "attn_decode", "attn_decode_append",
+EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_ext", "attn_prefill_fp8", "attn_decode",
+           "attn_decode_append",
            "attn_decode_ext", "attn_decode_chunk_tokens", "attn_decode_workspace_bytes", "attn_lse_combine",
            "attn_status_string")
 
@@ -43,6 +44,8 @@ lib.attn_prefill_varlen.restype = _I
 lib.attn_prefill_ext.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                                  ctypes.c_float, _P]
 lib.attn_prefill_ext.restype = _I
+lib.attn_prefill_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
+lib.attn_prefill_fp8.restype = _I
 lib.attn_decode_ext.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                                 ctypes.c_float, _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode_ext.restype = _I
@@ -131,6 +134,17 @@ def attn_prefill_ext(q, k, v, o, lse, cu_seqlens, max_seqlen: int, causal: bool,
                               _dtype_code(q), int(bool(causal)), float(scale), int(window_left), float(softcap),
                               _stream(stream))
     _check(rc, "attn_prefill_ext")
+
+
+def attn_prefill_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal: bool, scale: float,
+                     stream=None) -> None:
+    """q8 [B, Hq, N, d], k8, v8 [B, Hkv, N, d]: E4M3 codes (torch.float8_e4m3fn or uint8);
+    o [B, Hq, N, d] bf16, lse [B, Hq, N] float32; descale_* [B, Hkv] float32 or None."""
+    B, Hq, N, d = q8.shape
+    rc = lib.attn_prefill_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), _ptr(descale_q), _ptr(descale_k),
+                              _ptr(descale_v), B, N, Hq, k8.shape[1], d, int(bool(causal)), float(scale),
+                              _stream(stream))
+    _check(rc, "attn_prefill_fp8")
 
 
 def attn_decode_chunk_tokens(batch: int, n_kv_heads: int, page_size: int, max_blocks_per_seq: int,
@@ -232,6 +246,16 @@ def prefill_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, sc
         attn_prefill_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, scale, stream)
     else:
         attn_prefill_ext(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, scale, window_left, softcap, stream)
+    return o, lse
+
+
+def prefill_fp8(q8, k8, v8, descale_q=None, descale_k=None, descale_v=None, causal: bool = True,
+                scale: float | None = None, stream=None):
+    B, Hq, N, d = q8.shape
+    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+    attn_prefill_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, d ** -0.5 if scale is None else scale,
+                     stream)
     return o, lse
 
 

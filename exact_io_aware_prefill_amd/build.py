@@ -19,10 +19,10 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
-# per-source extra flags: the bf16 prefill assumes finite inputs so its row max
-# compiles to v_max3_f32 without NaN-quieting copies (infinities stay IEEE)
-EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"]}
+SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "prefill_fp8.hip", "decode.hip"]
+# per-source extra flags: the bf16 and fp8 prefills assume finite inputs so their
+# row max compiles to v_max3_f32 without NaN-quieting copies (infinities stay IEEE)
+EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"], "prefill_fp8.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:

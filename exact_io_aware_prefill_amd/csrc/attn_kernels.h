@@ -30,6 +30,17 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream);
 // Tiled prefill, float32 arithmetic (prefill_f32.hip).
 hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream);
 
+// Tiled prefill on FP8 (E4M3) inputs, bf16 output (prefill_fp8.hip).
+struct PrefillFp8Params {
+    const void *q, *k, *v;  // [B, Hq | Hkv, N, head_dim] E4M3 codes
+    void *o;                // [B, Hq, N, head_dim] bf16
+    float *lse;             // [B, Hq, N]
+    const float *descale_q, *descale_k, *descale_v;  // [B, Hkv] or NULL (1)
+    int B, N, Hq, Hkv, head_dim, causal;
+    float scale;
+};
+hipError_t launch_prefill_fp8(const PrefillFp8Params &p, hipStream_t stream);
+
 // Split-KV decode: per-chunk partials, then the combine (decode.hip).
 struct DecodeParams {
     const void *q, *k_cache, *v_cache;

@@ -1,0 +1,412 @@
+// Tiled exact prefill attention on FP8 (E4M3) inputs for gfx950 matrix cores.
+//
+// Method: the same tiled prefill with an online softmax as the bf16 kernel
+// (pofe.ai, "FlashAttention for inference: tiled prefill and split-KV decoding",
+// sections "Prefill: tiles, loop order and the tensor cores" and "The online
+// softmax, with every symbol defined"), on 8-bit inputs, which the page names as
+// the FlashAttention-3 direction (section "The bottleneck it attacks").  Scores
+// are s = scale * dq * dk * <q8, k8> with per-(sequence, KV head) descale
+// factors; the output is O = dv * sum_j p_j v8_j / l, written in bf16, and the
+// row log-sum-exp over the scaled scores in float32.
+//
+// gfx950 mapping
+//   * Both products run on v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3 operands,
+//     unit block scales, float32 accumulation), transposed as in the bf16
+//     kernel: S^T = K Q^T (A = K rows from LDS, B = the wave's 32 Q rows in
+//     registers), O^T += V^T P^T (A = V^T from LDS, B = the probabilities).
+//     The contraction depth is 64, so a key/value tile is 64 keys (two 32-key
+//     score blocks) and one P*V product covers the whole tile.
+//   * Operand slot s of A and slot s of B meet in the product (checked on the
+//     GPU with an in-bounds probe).  A lane of the score accumulator holds
+//     query l % 32 and, in block kb, keys 32 kb + 8 (r >> 2) + 4 (l >> 5) +
+//     (r & 3) for register r; packed to E4M3 in register order these are the
+//     lane's B slots 16 kb + r.  The V^T operand then needs, for slot 8t + k,
+//     the value of key 16 t + 8 (k >> 2) + 4 (l >> 5) + (k & 3): one
+//     ds_read_b64_tr_b8 per t, in which lanes 2k and 2k+1 of each 16-lane
+//     group read the two halves of that key row's 16 bytes and lane j receives
+//     byte j (dim j) of the 8 rows.
+//   * Probabilities are exp2 of the scores against the running reference
+//     (lazy max, as the bf16 kernel: a lane whose tile sum exceeds 256 redoes
+//     the tile against the true max), so each is <= 256 < 448 and rounds to
+//     E4M3 without saturating (round to nearest even).  The row sum l is kept
+//     in float32 from the unrounded values, so the LSE does not see the
+//     8-bit rounding; O does, by at most 2^-4 relative per term (and 2^-10
+//     absolute below the normal range).
+//   * K and V tiles go straight from memory into LDS (buffer loads with the LDS
+//     destination bit), double-buffered.  16-byte chunk c of key row r sits at
+//     slot c ^ swz(r); the permutations make the K operand reads (16 rows per
+//     pass) and the transpose reads (8 rows x 2 chunks per 32 lanes) bank-
+//     conflict free and are the same for every row a lane's load
+//     instructions fill.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "attn_kernels.h"
+
+namespace attn {
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kWaves = 4;                 // waves per workgroup, 32 query rows each
+constexpr int kBM = kWaves * 32;          // query rows per workgroup
+constexpr int kBlockN = 64;               // keys per tile (the product's depth)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kMaxLaneSum = 256.f;      // a lane's tile sum above this redoes the tile
+constexpr uint32_t kBufferFlags = 0x00020000u;
+constexpr int kUnitScale = 127;           // E8M0 block scale 2^0
+
+struct Args {
+    const uint8_t *q, *k, *v;  // [B, Hq | Hkv, N, D] E4M3 codes
+    uint16_t *o;               // [B, Hq, N, D] bf16
+    float *lse;                // [B, Hq, N]
+    const float *dq, *dk, *dv; // [B, Hkv] descales, or NULL (1)
+    int B, N, Hq, Hkv, group, causal, n_qtiles;
+    float scale;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kBufferFlags);
+}
+
+// Chunk permutations (see the header).  D = 128: rows are 128 bytes (two per
+// bank line).  D = 64: rows are 64 bytes (four per bank line).
+template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r >> 1) & 7 : (r >> 2) & 3; }
+template <int D> __device__ __forceinline__ int v_swz(int r)
+{
+    return D == 128 ? 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) : 2 * ((r >> 3) & 1);
+}
+
+// Memory -> LDS loader of one 64-row tile of D bytes per row: D/16 wave
+// instructions of 64 16-byte chunks, wave w issuing instructions w, w + 4.
+// A lane's rows in its instructions are 32 apart, which no permutation above
+// distinguishes, so one per-lane offset serves them all.
+template <int D>
+struct TileLoader {
+    static constexpr int NC = D / 16;           // chunks per row
+    static constexpr int RPI = 64 / NC;         // rows per instruction
+    static constexpr int INSTR = kBlockN * NC / 64;
+    static constexpr int PER_WAVE = INSTR / kWaves;
+    static_assert(INSTR % kWaves == 0, "tile instructions split evenly over the waves");
+    static_assert(RPI * kWaves == 32 || PER_WAVE == 1, "a lane's rows are 32 apart");
+    uint32_t voff;
+
+    template <typename Swz>
+    __device__ __forceinline__ void init(int wave, int lane, Swz swz)
+    {
+        const int u = wave * 64 + lane;
+        const int r = u / NC, pos = u % NC;
+        voff = (uint32_t)(lane / NC) * D + 16u * (uint32_t)(pos ^ swz(r));
+    }
+    // rows past n read as zero: each instruction's descriptor ends at row n
+    __device__ __forceinline__ void load(const uint8_t *head, int n, int k0, int wave, uint8_t *dst) const
+    {
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int ins = wave + i * kWaves;
+            const int row0 = k0 + ins * RPI;
+            const uint32_t rec = __builtin_amdgcn_readfirstlane((uint32_t)max(n - row0, 0) * (uint32_t)D);
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (long long)row0 * D, rec);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + ins * 1024), 16, voff, 0, 0, 0);
+        }
+    }
+};
+
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ f32x16_t mfma8(i32x8_t a, i32x8_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kUnitScale, 0, kUnitScale);
+}
+
+// S^T = K Q^T for the tile's two 32-key blocks.  kad0/kad1: the lane's byte
+// offsets of its two 16-byte K chunks for d-step 0 (d-step ds is a XOR by 64 ds).
+template <int D>
+__device__ __forceinline__ void qk_tile(f32x16_t (&S)[2], const uint8_t *Ks, const i32x8_t (&qf)[D / 64],
+                                        uint32_t kad0, uint32_t kad1)
+{
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kb][i] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < D / 64; ++ds)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const uint8_t *base = Ks + kb * 32 * D;
+            const uint4 lo = *reinterpret_cast<const uint4 *>(base + (kad0 ^ (64u * ds)));
+            const uint4 hi = *reinterpret_cast<const uint4 *>(base + (kad1 ^ (64u * ds)));
+            const i32x8_t kf = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            S[kb] = mfma8(kf, qf[ds], S[kb]);
+        }
+}
+
+// O^T += V^T P^T over the tile: one product per 32 dims, its A operand from four
+// transpose reads (vad: the lane's address for t = 0, d-block 0; t adds 16 rows,
+// d-block db is a XOR by 32 db).
+template <int D>
+__device__ __forceinline__ void pv_tile(f32x16_t (&acc)[D / 32], const uint8_t *Vs, i32x8_t pf, uint32_t vad)
+{
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        i32x8_t vf;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const i32x2_t x =
+                __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t *)(Vs + 16 * t * D + (vad ^ (32u * db))));
+            vf[2 * t] = x[0];
+            vf[2 * t + 1] = x[1];
+        }
+        acc[db] = mfma8(vf, pf, acc[db]);
+    }
+}
+
+// Probabilities of one tile against reference mb (= m * sl2), packed to E4M3 in
+// the order of the P*V operand's slots, and the lane's float32 sum of the
+// unrounded values.
+__device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[2], float sl2, float mb, i32x8_t &pf)
+{
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        const int kb = w >> 2, r0 = 4 * (w & 3);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb][r0], sl2, -mb));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][r0 + 1], sl2, -mb));
+        const float p2 = __builtin_amdgcn_exp2f(fmaf(S[kb][r0 + 2], sl2, -mb));
+        const float p3 = __builtin_amdgcn_exp2f(fmaf(S[kb][r0 + 3], sl2, -mb));
+        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        packed = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, packed, true);
+        pf[w] = packed;
+        rs0 += p0 + p2;
+        rs1 += p1 + p3;
+    }
+    return rs0 + rs1;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
+{
+    constexpr int NT = kWaves * 64;
+    constexpr int TB = kBlockN * D;  // bytes per K or V tile
+    __shared__ __attribute__((aligned(1024))) uint8_t KB0[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t KB1[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t VB0[TB];
+    __shared__ __attribute__((aligned(1024))) uint8_t VB1[TB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+
+    // ---- work item: (b, kv head, zig-zag q tile, q head), query head fastest ----
+    const int item = blockIdx.x;
+    const int j = item % a.group;
+    const int r = (item / a.group) % a.n_qtiles;
+    const int bg = item / (a.group * a.n_qtiles);
+    const int b = bg / a.Hkv, hk = bg % a.Hkv;
+    const int h = hk * a.group + j;
+    const int qtile = (r & 1) ? (r >> 1) : a.n_qtiles - 1 - (r >> 1);
+    const int q0 = qtile * kBM;
+    const int N = a.N;
+
+    // effective scale of the raw 8-bit dot products, and the output factor
+    const float dq = a.dq ? a.dq[b * a.Hkv + hk] : 1.f;
+    const float dk = a.dk ? a.dk[b * a.Hkv + hk] : 1.f;
+    const float dv = a.dv ? a.dv[b * a.Hkv + hk] : 1.f;
+    const float eff = a.scale * dq * dk;
+    const bool negate = eff < 0.f;  // s * eff = (-s) * |eff|: flip Q's sign bits
+    const float aeff = fmaxf(fabsf(eff), 1e-30f);
+    const float sl2 = aeff * kLog2e;
+
+    const long long qo = ((long long)b * a.Hq + h) * N * D;
+    const long long kvo = ((long long)b * a.Hkv + hk) * N * D;
+    const uint8_t *const kh = a.k + kvo;
+    const uint8_t *const vh = a.v + kvo;
+    const int wrow0 = q0 + wave * 32;
+
+    // Q fragments: lane (query l32, half hh) holds dims 64 ds + 32 hh .. + 31
+    i32x8_t qf[D / 64];
+    {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qo, (uint32_t)N * D);
+        const uint32_t qrow_off = (uint32_t)(wrow0 + l32) * D + 32u * hh;
+        const int flip = negate ? (int)0x80808080u : 0;
+#pragma unroll
+        for (int ds = 0; ds < D / 64; ++ds) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint4 u = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              rq, qrow_off + 64u * ds + 16u * e, 0, 0));
+                qf[ds][4 * e + 0] = (int)u.x ^ flip;
+                qf[ds][4 * e + 1] = (int)u.y ^ flip;
+                qf[ds][4 * e + 2] = (int)u.z ^ flip;
+                qf[ds][4 * e + 3] = (int)u.w ^ flip;
+            }
+        }
+    }
+
+    f32x16_t acc[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const int xlane = (lane ^ 32) << 2;
+
+    TileLoader<D> kld, vld;
+    kld.init(wave, lane, [](int rr) { return k_swz<D>(rr); });
+    vld.init(wave, lane, [](int rr) { return v_swz<D>(rr); });
+    const uint32_t kad0 = (uint32_t)(l32 * D + 16 * ((2 * hh) ^ k_swz<D>(l32)));
+    const uint32_t kad1 = (uint32_t)(l32 * D + 16 * ((2 * hh + 1) ^ k_swz<D>(l32)));
+    uint32_t vad;
+    {
+        const int g = lane >> 4, j16 = lane & 15, k = j16 >> 1, half8 = j16 & 1;
+        const int r0 = 4 * hh + 8 * (k >> 2) + (k & 3);
+        vad = (uint32_t)(r0 * D + 16 * ((g & 1) ^ v_swz<D>(r0)) + 8 * half8);
+    }
+
+    const int kend = a.causal ? min(N, q0 + kBM) : N;
+    const int ntiles = (kend + kBlockN - 1) / kBlockN;
+
+    // ---- prologue: V buffers start as zeros (tile -1 is multiplied by P = 0, and
+    // rows past N must be finite)
+    for (int i = tid; i < TB / 16; i += NT) {
+        reinterpret_cast<uint4 *>(VB0)[i] = make_uint4(0, 0, 0, 0);
+        reinterpret_cast<uint4 *>(VB1)[i] = make_uint4(0, 0, 0, 0);
+    }
+    kld.load(kh, N, 0, wave, KB0);
+    if (ntiles > 1) kld.load(kh, N, kBlockN, wave, KB1);
+    wait_loads();
+    __syncthreads();
+    f32x16_t S[2];
+    qk_tile<D>(S, KB0, qf, kad0, kad1);
+    i32x8_t P0, P1;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) P1[w] = 0;
+    __syncthreads();
+
+    auto step = [&](i32x8_t &Pp, i32x8_t &Pc, int t, const uint8_t *Kn, const uint8_t *Vp, uint8_t *Kw,
+                    uint8_t *Vw) {
+        const int k0 = t * kBlockN;
+        if (t + 2 < ntiles) kld.load(kh, N, k0 + 2 * kBlockN, wave, Kw);
+        vld.load(vh, N, k0, wave, Vw);
+        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > N) {
+            const int qrow = wrow0 + l32;
+            const int lim = (a.causal ? min(qrow, N - 1) : N - 1) - (k0 + 4 * hh);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) S[kb][i] = -INFINITY;
+        }
+        pv_tile<D>(acc, Vp, Pp, vad);
+        float rs = softmax_tile(S, sl2, m * sl2, Pc);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+        }
+        if (__ballot(m == -INFINITY || rs > kMaxLaneSum)) {
+            asm volatile("" ::"v"(Pc));
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb][i]);
+            mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
+            const float m_new = fmaxf(m, mx);
+            const float c = __builtin_amdgcn_exp2f((m - m_new) * sl2);  // 0 while m = -inf
+            l *= c;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[db][i] *= c;
+            m = m_new;
+            rs = softmax_tile(S, sl2, m * sl2, Pc);
+        }
+        l += rs;
+        if (t + 1 < ntiles) {
+            qk_tile<D>(S, Kn, qf, kad0, kad1);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int i = 0; i < (D / 64) * 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+        }
+        wait_loads();
+        __syncthreads();
+    };
+
+    for (int t = 0; t < ntiles; t += 2) {
+        step(P1, P0, t, KB1, VB1, KB0, VB0);
+        if (t + 1 < ntiles) step(P0, P1, t + 1, KB0, VB0, KB1, VB1);
+    }
+    if (ntiles & 1)
+        pv_tile<D>(acc, VB0, P0, vad);
+    else
+        pv_tile<D>(acc, VB1, P1, vad);
+
+    // ---- epilogue: O = dv * acc / l (bf16), LSE = m * |eff| + ln l
+    const int qrow = wrow0 + l32;
+    const float lt = l + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, l)));
+    if (qrow < N) {
+        const float f = dv / lt;
+        uint16_t *orow = a.o + qo + (long long)qrow * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int ig = 0; ig < 4; ++ig) {
+                const int d0 = 32 * db + 8 * ig + 4 * hh;
+                uint16_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[db][4 * ig + e] * f));
+                uint2 pk;
+                pk.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+                pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+                *reinterpret_cast<uint2 *>(orow + d0) = pk;
+            }
+        if (hh == 0) a.lse[((long long)b * a.Hq + h) * N + qrow] = m * aeff + log2f(lt) * kLn2;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_fp8(const PrefillFp8Params &p, hipStream_t stream)
+{
+    Args a;
+    a.q = static_cast<const uint8_t *>(p.q);
+    a.k = static_cast<const uint8_t *>(p.k);
+    a.v = static_cast<const uint8_t *>(p.v);
+    a.o = static_cast<uint16_t *>(p.o);
+    a.lse = p.lse;
+    a.dq = p.descale_q;
+    a.dk = p.descale_k;
+    a.dv = p.descale_v;
+    a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.group = p.Hq / p.Hkv;
+    a.causal = p.causal;
+    a.scale = p.scale;
+    a.n_qtiles = (p.N + kBM - 1) / kBM;
+    const long long items = (long long)a.n_qtiles * p.B * p.Hq;
+    if (items == 0) return hipSuccess;
+    if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+    // one head's rows, including the padded last query tile, are addressed with 32-bit offsets
+    if ((long long)a.n_qtiles * kBM * p.head_dim > 0xffffffffLL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)items), block(kWaves * 64);
+    if (p.head_dim == 128)
+        hipLaunchKernelGGL(prefill_fp8_kernel<128>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(prefill_fp8_kernel<64>, grid, block, 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -93,6 +93,42 @@ def prefill_packed_inputs(seed: int, lens, Hq: int, Hkv: int, d: int, dtype: str
                                1.0 / math.sqrt(d) if scale is None else scale, dtype)
 
 
+@dataclass
+class Fp8PrefillInputs:
+    q8: torch.Tensor  # [B, Hq, N, d] float8_e4m3fn codes
+    k8: torch.Tensor  # [B, Hkv, N, d]
+    v8: torch.Tensor
+    descale_q: torch.Tensor  # [B, Hkv] float32
+    descale_k: torch.Tensor
+    descale_v: torch.Tensor
+    causal: bool
+    scale: float
+
+
+def _to_e4m3(x: torch.Tensor, descale: torch.Tensor, group: int) -> torch.Tensor:
+    """x [B, H, N, d] float32 -> E4M3 codes of x / descale[b, h // group] (PyTorch's
+    round-to-nearest conversion; |x| / descale <= 448 by construction)."""
+    ds = descale.repeat_interleave(group, dim=1)[:, :, None, None]
+    return (x / ds).to(torch.float8_e4m3fn)
+
+
+def prefill_fp8_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, causal: bool = True,
+                       scale: Optional[float] = None) -> Fp8PrefillInputs:
+    """Q, K, V drawn as in prefill_inputs (float32), then quantised to E4M3 with one
+    descale per (sequence, KV head): the group's largest magnitude maps to 448."""
+    rng = np.random.default_rng(seed)
+    q = _draw(rng, (B, Hq, N, d), F32)
+    k = _draw(rng, (B, Hkv, N, d), F32)
+    v = _draw(rng, (B, Hkv, N, d), F32)
+    g = Hq // Hkv
+
+    def descale(x):  # heads of one KV group are adjacent, so [B, Hkv, rest]
+        return torch.clamp(x.abs().reshape(B, Hkv, -1).amax(dim=-1), min=1e-12) / 448.0
+    dq, dk, dv = descale(q), descale(k), descale(v)
+    return Fp8PrefillInputs(_to_e4m3(q, dq, g), _to_e4m3(k, dk, 1), _to_e4m3(v, dv, 1), dq.float(), dk.float(),
+                            dv.float(), causal, 1.0 / math.sqrt(d) if scale is None else scale)
+
+
 def worked_example_inputs(d: int = 64) -> PrefillInputs:
     """The pofe.ai worked example (section "A worked example by hand": scores
     (2, 1, 4, 3), scalar values (1, 0, 2, -1)) embedded in a 4-token causal

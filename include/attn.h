@@ -23,6 +23,9 @@
  *     window and logit soft-capping, two of the attention variants the
  *     page's section "Interaction with post-trained models" names as ones a
  *     kernel has to support;
+ *   - attn_prefill_fp8: the prefill on 8-bit (E4M3) inputs with descale
+ *     factors, the FP8 direction the page names for FlashAttention-3 (section
+ *     "The bottleneck it attacks");
  *   - attn_lse_combine: that reduction on its own -- the combine rule for
  *     independent partials, a softmax over the partials' log-sum-exps
  *     (section "The online softmax, with every symbol defined" and the
@@ -51,7 +54,8 @@
  *   - Grouped-query attention: query head h reads KV head h / (n_q_heads /
  *     n_kv_heads) (consecutive query heads share a KV head).
  *   - Head sizes 64, 128 and 256 (256 being the largest the page's section
- *     "Interaction with post-trained models" names) on every entry point.
+ *     "Interaction with post-trained models" names) on every entry point except
+ *     attn_prefill_fp8 (64 and 128).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -144,6 +148,31 @@ int attn_prefill_ext(const void *q, const void *k, const void *v, void *o, float
                      const int32_t *cu_seqlens_or_null, int batch, int seqlen, int total_tokens,
                      int n_q_heads, int n_kv_heads, int head_dim, int dtype, int causal, float scale,
                      int window_left, float softcap, void *stream);
+
+/*
+ * attn_prefill_fp8 -- attn_prefill on FP8 inputs: O = softmax(s) V with scores
+ * s = scale * descale_q * descale_k * <q8, k8> and values descale_v * v8.
+ *
+ *   q    [batch, n_q_heads,  seqlen, head_dim]  E4M3 codes (OCP 8-bit float,
+ *        finite-only variant: bias 7, max 448), one byte each
+ *   k, v [batch, n_kv_heads, seqlen, head_dim]  E4M3 codes
+ *   o    [batch, n_q_heads,  seqlen, head_dim]  bfloat16 (written)
+ *   lse  [batch, n_q_heads,  seqlen] float32, natural log over the scaled scores
+ *   descale_q/k/v_or_null [batch, n_kv_heads] float32 on the device, 4-byte
+ *        aligned, one factor per (sequence, KV head) shared by the group's query
+ *        heads; NULL means 1.
+ *   head_dim in {64, 128}; causal and scale as attn_prefill.  Arithmetic: both
+ *   products on the FP8 matrix cores with float32 accumulation; the
+ *   probabilities are rounded to E4M3 (nearest even, each <= 256) before the
+ *   P*V product, so O carries up to 2^-4 relative error per term (2^-10
+ *   absolute below E4M3's normal range); the row sums and the LSE use the
+ *   unrounded float32 values.  NaN codes (0x7f, 0xff) in the inputs are the
+ *   caller's error.  (seqlen + 127) * head_dim >= 2^32 is ATTN_ERR_UNSUPPORTED.
+ */
+int attn_prefill_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                     const float *descale_q_or_null, const float *descale_k_or_null,
+                     const float *descale_v_or_null, int batch, int seqlen, int n_q_heads, int n_kv_heads,
+                     int head_dim, int causal, float scale, void *stream);
 
 /*
  * attn_decode -- one new query token per sequence against a KV cache, by

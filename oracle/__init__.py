@@ -280,7 +280,7 @@ def e4m3_decode(codes) -> np.ndarray:
     return out
 
 
-def prefill_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale: float):
+def prefill_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale: float, row_step: int = 1):
     """Attention on FP8 inputs: the plain prefill of the dequantised tensors.
 
     q8 [B, Hq, N, d], k8, v8 [B, Hkv, N, d] are E4M3 byte codes; descale_* are
@@ -299,4 +299,4 @@ def prefill_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale
     q = q * np.repeat(dq, g, axis=1)[:, :, None, None]
     k = k * dk[:, :, None, None]
     v = v * dv[:, :, None, None]
-    return prefill(q, k, v, causal, scale)
+    return prefill(q, k, v, causal, scale, row_step=row_step)

@@ -1,0 +1,144 @@
+"""GPU parity of the FP8 (E4M3) prefill against the fp64 oracle on the same codes.
+
+The oracle computes attention on the dequantised inputs with no rounding of the
+probabilities.  The kernel rounds each probability to E4M3 before the P*V product
+(nearest even; 3 mantissa bits, so at most 2^-4 relative error, or 2^-10 absolute
+below the normal range) and writes O in bf16.  With p_j relative to the row's true
+max, l = sum_j p_j and n visible keys, that bounds the error of a row by
+
+    |dO| <= descale_v * max|v8| * (2^-4 + n 2^-10 / l) + 2^-8 |O| + 1e-5,
+
+which the tests check element by element; the LSE keeps the bf16 path's 1e-3 bar
+(the row sums use the unrounded float32 probabilities).  A second, typical-error
+check asserts the RMS error is far below that worst case."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_prefill_amd import workloads as W
+from gpu_common import dev, say
+
+pytestmark = pytest.mark.gpu
+LSE_TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def attn():
+    from exact_io_aware_prefill_amd import attn as a  # raises if libattn.so is missing
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return a
+
+
+def row_bounds(x, rows=None):
+    """Per-row error bound of the formula above, from the dequantised inputs."""
+    q = oracle.e4m3_decode(x.q8); k = oracle.e4m3_decode(x.k8); v = oracle.e4m3_decode(x.v8)
+    B, Hq, N, d = q.shape
+    g = Hq // k.shape[1]
+    dq = x.descale_q.double().numpy(); dk = x.descale_k.double().numpy(); dv = x.descale_v.double().numpy()
+    rows = np.arange(N) if rows is None else rows
+    bound = np.zeros((B, Hq, len(rows)))
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // g
+            s = (q[b, h, rows] @ k[b, hk].T) * (x.scale * dq[b, hk] * dk[b, hk])
+            if x.causal:
+                s = np.where(np.arange(N)[None, :] <= rows[:, None], s, -np.inf)
+            n = np.isfinite(s).sum(axis=1)
+            mx = s.max(axis=1)
+            lsum = np.exp(s - mx[:, None]).sum(axis=1)
+            vmax = np.abs(v[b, hk]).max() * dv[b, hk]
+            bound[b, h] = vmax * (2.0 ** -4 + n * 2.0 ** -10 / lsum)
+    return bound
+
+
+def check_fp8(name, o, lse, ro, rl, bound):
+    og = o.float().cpu().numpy(); lg = lse.cpu().numpy()
+    err = np.abs(og - ro)
+    lim = bound[..., None] + 2.0 ** -8 * np.abs(ro) + 1e-5
+    worst = float((err / lim).max())
+    rms = float(np.sqrt(np.mean(err ** 2)))
+    rms_ref = float(np.sqrt(np.mean(ro ** 2)))
+    el = float(np.abs(lg - rl).max())
+    say("%s: O max_abs=%.3e rms=%.3e (ref rms %.3e) worst err/bound=%.3f | LSE max_abs=%.3e"
+        % (name, float(err.max()), rms, rms_ref, worst, el))
+    assert worst <= 1.0, name
+    assert rms <= 2.0 ** -4 * max(rms_ref, 1e-3), name  # typical error well inside the worst case
+    assert el <= LSE_TOL, name
+
+
+def run(attn, x):
+    o, lse = attn.prefill_fp8(dev(x.q8), dev(x.k8), dev(x.v8), dev(x.descale_q), dev(x.descale_k),
+                              dev(x.descale_v), x.causal, x.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def test_fp8_worked_example(attn):
+    """The page's worked example, every value exact in E4M3: row 3 is 1.1381 up to the
+    E4M3 rounding of the four probabilities."""
+    say("case: fp8 worked example")
+    N, d = 4, 64
+    q8 = torch.zeros(1, 1, N, d, dtype=torch.uint8); k8 = torch.zeros_like(q8); v8 = torch.zeros_like(q8)
+    q8[0, 0, :, 0] = 0x38
+    k8[0, 0, :, 0] = torch.tensor([0x40, 0x38, 0x48, 0x44], dtype=torch.uint8)
+    v8[0, 0, :, 0] = torch.tensor([0x38, 0x00, 0x40, 0xb8], dtype=torch.uint8)
+    o, lse = attn.prefill_fp8(dev(q8), dev(k8), dev(v8), None, None, None, True, 1.0)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_fp8(q8, k8, v8, None, None, None, True, 1.0)
+    assert abs(ro[0, 0, 3, 0] - 1.1381) < 5e-5
+    assert abs(float(o[0, 0, 3, 0]) - ro[0, 0, 3, 0]) <= 2 * 2.0 ** -4 + 2.0 ** -8 * 1.2
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) <= 1e-5
+    assert (o[0, 0, :, 1:] == 0).all()
+
+
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 300, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill_ragged(attn, N, d, causal):
+    say("case: fp8 prefill N=%d d=%d causal=%s" % (N, d, causal))
+    x = W.prefill_fp8_inputs(3000 + N + d, 2, 8, 2, N, d, causal=causal)
+    o, lse = run(attn, x)
+    ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, causal, x.scale)
+    check_fp8("fp8 N=%d d=%d causal=%d" % (N, d, causal), o, lse, ro, rl, row_bounds(x))
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1.0])
+def test_fp8_prefill_scales(attn, scale):
+    """A negative scale (Q's sign bits are flipped instead), zero (uniform weights) and
+    a large one (peaky rows)."""
+    say("case: fp8 prefill scale=%g" % scale)
+    x = W.prefill_fp8_inputs(3100, 1, 4, 2, 333, 128, scale=scale)
+    o, lse = run(attn, x)
+    ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, True, scale)
+    check_fp8("fp8 scale=%g" % scale, o, lse, ro, rl, row_bounds(x))
+
+
+def test_fp8_prefill_without_descales(attn):
+    """NULL descales mean 1: the codes are the values."""
+    say("case: fp8 prefill, no descales")
+    x = W.prefill_fp8_inputs(3200, 1, 4, 4, 200, 64)
+    x.descale_q = torch.ones_like(x.descale_q); x.descale_k = torch.ones_like(x.descale_k)
+    x.descale_v = torch.ones_like(x.descale_v)
+    # the raw codes reach 448: scale the scores back to the O(1) range the LSE bar assumes
+    x.scale = 1.0 / (float(x.q8.float().std()) * float(x.k8.float().std()) * math.sqrt(64))
+    o, lse = attn.prefill_fp8(dev(x.q8), dev(x.k8), dev(x.v8), None, None, None, True, x.scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, None, None, None, True, x.scale)
+    check_fp8("fp8 no descales", o, lse, ro, rl, row_bounds(x))
+
+
+def test_fp8_prefill_16k_sampled_rows(attn):
+    """The 16k-token prompt (28 query / 4 KV heads, d = 128) in FP8, every 61st row."""
+    N, step = 16384, 61
+    say("case: fp8 prefill N=%d sampled every %d" % (N, step))
+    x = W.prefill_fp8_inputs(3, 1, 28, 4, N, 128)
+    o, lse = run(attn, x)
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, True, x.scale,
+                                row_step=step)
+    rows = np.arange(0, N, step)
+    check_fp8("fp8 16k (sampled)", o[:, :, rows], lse[:, :, rows], ro[:, :, rows], rl[:, :, rows],
+              row_bounds(x, rows))
