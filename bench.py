@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak (published)
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E peak (published)
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak (published)
 METRIC = "causal prefill TFLOP/s (N=16k, d=128) + split-KV decode HBM GB/s at 32k"
 CSRC = os.path.join(ROOT, "exact_io_aware_prefill_amd", "csrc")
 # HBM traffic per launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script,
@@ -34,6 +35,8 @@ TRAFFIC = {
                 "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel"},
     "decode": {"file": os.path.join(ROOT, "profiles", "decode_split_s32768_traffic.json"),
                "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel"},
+    "fp8": {"file": os.path.join(ROOT, "profiles", "prefill_fp8_n16384_traffic.json"),
+            "src": os.path.join(CSRC, "prefill_fp8.hip"), "kernel": "prefill_fp8_kernel"},
 }
 COPY_BYTES = 1 << 30  # reference dispatch for the counters: a 1 GiB device-to-device copy
 N_KV_COPIES = 8
@@ -46,8 +49,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle leg")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one half of the step (profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "fp8"], default=None,
+                    help="time one part only (profiling runs)")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 prefill measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference dispatch for HBM counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -217,6 +221,34 @@ def main():
     pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
 
+    # FP8 prefill of the same prompt (E4M3 inputs), timed on its own after the step
+    fp8 = None
+    if args.only in (None, "fp8") and not args.no_fp8:
+        fx = W.prefill_fp8_inputs(pcfg["seed"], B, Hq, k.shape[1], N, d)
+        q8, k8, v8 = fx.q8.to(dev), fx.k8.to(dev), fx.v8.to(dev)
+        dsq, dsk, dsv = fx.descale_q.to(dev), fx.descale_k.to(dev), fx.descale_v.to(dev)
+        o8 = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=dev)
+        l8 = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+
+        def run_fp8():
+            attn.attn_prefill_fp8(q8, k8, v8, o8, l8, dsq, dsk, dsv, True, fx.scale)
+        for _ in range(args.warmup):
+            run_fp8()
+        torch.cuda.synchronize()
+        ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            ev8[i][0].record()
+            run_fp8()
+            ev8[i][1].record()
+        torch.cuda.synchronize()
+        fp8_ms = sum(e[0].elapsed_time(e[1]) for e in ev8) / args.steps
+        a8 = prefill_flop / (fp8_ms * 1e-3) / 1e12
+        fp8 = {"value": a8, "unit": "TFLOP/s", "avg_launch_ms": fp8_ms, "dtype": "fp8-e4m3 in, bf16 out",
+               "config": {"workload": pcfg["name"].replace("bf16", "fp8e4m3"), "descales": "per (sequence, KV head)"},
+               "roofline": {"bound": "mfma", "achieved": a8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                            "frac": a8 / PEAK_FP8_TFLOPS, "traffic": measured_traffic("fp8"),
+                            "kernel": "prefill_fp8_kernel<128>", "algorithmic_flop_per_launch": prefill_flop}}
+
     if args.copy_calibration:  # reference dispatch for the HBM byte counters: copy 1 GiB
         src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -257,6 +289,8 @@ def main():
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode"),
                                       "kernels": "decode_split_kernel<128, false, false> + lse_combine_kernel<128>",
                                       "algorithmic_bytes_per_launch": decode_bytes}}
+    if fp8 is not None:
+        out["fp8_prefill"] = fp8
     if do_p and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(px, args.cpu_seconds)
     print(json.dumps(out), flush=True)

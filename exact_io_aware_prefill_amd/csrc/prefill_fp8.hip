@@ -32,6 +32,11 @@
 //     in float32 from the unrounded values, so the LSE does not see the
 //     8-bit rounding; O does, by at most 2^-4 relative per term (and 2^-10
 //     absolute below the normal range).
+//   * Step t issues QK(t+1) into a second score buffer and PV(t-1), then the
+//     softmax of tile t; scheduling groups spread the softmax's vector work
+//     over the eight products (two LDS reads and twenty VALU instructions after
+//     each), so the matrix cores and the VALUs overlap inside the wave.  Two
+//     waves per SIMD (about 205 VGPRs).
 //   * K and V tiles go straight from memory into LDS (buffer loads with the LDS
 //     destination bit), double-buffered.  16-byte chunk c of key row r sits at
 //     slot c ^ swz(r); the permutations make the K operand reads (16 rows per
@@ -285,15 +290,17 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     if (ntiles > 1) kld.load(kh, N, kBlockN, wave, KB1);
     wait_loads();
     __syncthreads();
-    f32x16_t S[2];
-    qk_tile<D>(S, KB0, qf, kad0, kad1);
+    f32x16_t SA[2], SB[2];
+    qk_tile<D>(SA, KB0, qf, kad0, kad1);
     i32x8_t P0, P1;
 #pragma unroll
     for (int w = 0; w < 8; ++w) P1[w] = 0;
     __syncthreads();
 
-    auto step = [&](i32x8_t &Pp, i32x8_t &Pc, int t, const uint8_t *Kn, const uint8_t *Vp, uint8_t *Kw,
-                    uint8_t *Vw) {
+    // step t: S holds tile t's scores, Sn receives tile t+1's (issued first, so
+    // both products overlap the softmax of tile t)
+    auto step = [&](f32x16_t (&S)[2], f32x16_t (&Sn)[2], i32x8_t &Pp, i32x8_t &Pc, int t, const uint8_t *Kn,
+                    const uint8_t *Vp, uint8_t *Kw, uint8_t *Vw) {
         const int k0 = t * kBlockN;
         if (t + 2 < ntiles) kld.load(kh, N, k0 + 2 * kBlockN, wave, Kw);
         vld.load(vh, N, k0, wave, Vw);
@@ -306,14 +313,15 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
                 for (int i = 0; i < 16; ++i)
                     if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) S[kb][i] = -INFINITY;
         }
+        if (t + 1 < ntiles) qk_tile<D>(Sn, Kn, qf, kad0, kad1);
         pv_tile<D>(acc, Vp, Pp, vad);
         float rs = softmax_tile(S, sl2, m * sl2, Pc);
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i) {
+        for (int i = 0; i < (D / 64) * 2 + D / 32; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
         }
         if (__ballot(m == -INFINITY || rs > kMaxLaneSum)) {
             asm volatile("" ::"v"(Pc));
@@ -334,22 +342,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
             rs = softmax_tile(S, sl2, m * sl2, Pc);
         }
         l += rs;
-        if (t + 1 < ntiles) {
-            qk_tile<D>(S, Kn, qf, kad0, kad1);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int i = 0; i < (D / 64) * 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-        }
         wait_loads();
         __syncthreads();
     };
 
     for (int t = 0; t < ntiles; t += 2) {
-        step(P1, P0, t, KB1, VB1, KB0, VB0);
-        if (t + 1 < ntiles) step(P0, P1, t + 1, KB0, VB0, KB1, VB1);
+        step(SA, SB, P1, P0, t, KB1, VB1, KB0, VB0);
+        if (t + 1 < ntiles) step(SB, SA, P0, P1, t + 1, KB0, VB0, KB1, VB1);
     }
     if (ntiles & 1)
         pv_tile<D>(acc, VB0, P0, vad);
