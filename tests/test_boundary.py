@@ -131,6 +131,31 @@ def test_prefill_ext_argument_errors(kw, code):
     assert prefill_ext(**kw) == code
 
 
+def prefill_fp8(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dq=0, dk=0, dv=0, B=1, N=16, Hq=4, Hkv=2, d=128,
+                causal=1):
+    return attn.lib.attn_prefill_fp8(P(q), P(k), P(v), P(o), P(lse), P(dq), P(dk), P(dv), B, N, Hq, Hkv, d, causal,
+                                     0.1, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), attn.ATTN_ERR_NULL),
+    (dict(lse=0), attn.ATTN_ERR_NULL),
+    (dict(B=-1), attn.ATTN_ERR_SHAPE),
+    (dict(N=-1), attn.ATTN_ERR_SHAPE),
+    (dict(Hkv=0), attn.ATTN_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
+    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),     # fp8: head sizes 64 and 128
+    (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(k=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(dv=FAKE + 2), attn.ATTN_ERR_ALIGN),     # descales are float arrays: 4-byte aligned
+    (dict(dq=FAKE + 4, q=0), attn.ATTN_ERR_NULL),  # 4-byte aligned descale is fine; NULL q is not
+    (dict(N=1 << 30), attn.ATTN_ERR_UNSUPPORTED),  # a head's rows past 32-bit offsets
+    (dict(B=0, q=0, k=0, v=0, o=0, lse=0), attn.ATTN_OK),
+])
+def test_prefill_fp8_argument_errors(kw, code):
+    assert prefill_fp8(**kw) == code
+
+
 def decode(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, d=128, P_=16,
            maxb=8, dtype=1, chunk=0, ws=FAKE, wsb=1 << 30):
     return attn.lib.attn_decode(P(q), P(kc), P(vc), P(bt), P(sl), P(o), P(lse), B, Hq, Hkv, d, P_,
