@@ -193,9 +193,9 @@ struct TileLoader {
             const int ins = wave + i * kWaves;
             if (INSTR < kWaves && ins >= INSTR) break;  // wave-uniform
             const int row0 = k0 + ins * RPI;
-            const long long left = (long long)max(n - row0, 0) * rowb;
-            // readfirstlane keeps the descriptor in scalar registers
-            const uint32_t rec = __builtin_amdgcn_readfirstlane((uint32_t)min(left, 0xFFFFFFFFLL));
+            // (n - row0) * rowb < 2^32: the launcher bounds a head's padded rows to
+            // 32-bit byte offsets.  readfirstlane keeps the descriptor in scalar registers.
+            const uint32_t rec = __builtin_amdgcn_readfirstlane((uint32_t)max(n - row0, 0) * rowb);
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(reinterpret_cast<const char *>(head) + (long long)row0 * rowb, rec);
             const uint32_t off = (D == 256 && (i & 1)) ? (voff ^ odd_xor) : voff;
@@ -262,7 +262,7 @@ __device__ __forceinline__ void pv_tile(f32x16_t (&acc)[kBlocks][D / 32], const 
 // the lane's float32 sum of the unrounded probabilities.
 __device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[kKB], float sl2, float mb, bf16x8_t (&pf)[kKS])
 {
-    float rs0 = 0.f, rs1 = 0.f;
+    float rs0, rs1;
     uint32_t w[kKS][4];
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb)
@@ -272,8 +272,8 @@ __device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[kKB], float sl
             const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][i + 1], sl2, -mb));
             const bf16x2_t pk = {(__bf16)p0, (__bf16)p1};
             w[2 * kb + (i >> 3)][(i & 7) >> 1] = __builtin_bit_cast(uint32_t, pk);
-            rs0 += p0;
-            rs1 += p1;
+            rs0 = (kb == 0 && i == 0) ? p0 : rs0 + p0;  // the first term starts the sum (no 0 + p)
+            rs1 = (kb == 0 && i == 0) ? p1 : rs1 + p1;
         }
 #pragma unroll
     for (int j = 0; j < kKS; ++j) pf[j] = __builtin_bit_cast(bf16x8_t, make_uint4(w[j][0], w[j][1], w[j][2], w[j][3]));
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
         bool redo = m[0] == -INFINITY;
 #pragma unroll
         for (int bb = 0; bb < kBlocks; ++bb) redo = redo || rs[bb] > kMaxLaneSum;
-        if (__ballot(redo)) {
+        if (__builtin_amdgcn_ballot_w64(redo)) {
             // an (empty) use of the first attempt on this path too, so the compiler
             // computes it above, between the products, instead of below the branch
 #pragma unroll

@@ -179,7 +179,7 @@ __device__ __forceinline__ void pv_tile(f32x16_t (&acc)[D / 32], const uint8_t *
 // unrounded values.
 __device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[2], float sl2, float mb, i32x8_t &pf)
 {
-    float rs0 = 0.f, rs1 = 0.f;
+    float rs0, rs1;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
         const int kb = w >> 2, r0 = 4 * (w & 3);
@@ -190,8 +190,8 @@ __device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[2], float sl2,
         int packed = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
         packed = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, packed, true);
         pf[w] = packed;
-        rs0 += p0 + p2;
-        rs1 += p1 + p3;
+        rs0 = w == 0 ? p0 + p2 : rs0 + (p0 + p2);  // the first terms start the sums (no 0 + p)
+        rs1 = w == 0 ? p1 + p3 : rs1 + (p1 + p3);
     }
     return rs0 + rs1;
 }
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
         }
-        if (__ballot(m == -INFINITY || rs > kMaxLaneSum)) {
+        if (__builtin_amdgcn_ballot_w64(m == -INFINITY || rs > kMaxLaneSum)) {
             asm volatile("" ::"v"(Pc));
             float mx = -INFINITY;
 #pragma unroll
