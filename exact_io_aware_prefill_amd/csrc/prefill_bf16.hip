@@ -449,6 +449,9 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
         // ---- matrix cores: PV(t-1); vector ALUs: probabilities of tile t against
         // the reference max from before the tile (the first tile, with no
         // reference yet, always takes the rare path)
+        // raised wave priority while this block issues: the arbiter then favours the
+        // wave whose products and softmax interleave, over waves in their QK part
+        __builtin_amdgcn_s_setprio(1);
         pv_tile<D>(acc, Vp, Pp, vad);
         float rs[kBlocks];
 #pragma unroll
@@ -464,6 +467,7 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
         // ---- rare: some probability may exceed 2^8 (or a row has no reference yet):
         // raise the reference to the true running max, rescale, redo the tile
         bool redo = m[0] == -INFINITY;
