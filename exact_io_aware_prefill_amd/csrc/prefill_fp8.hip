@@ -187,7 +187,9 @@ __device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[2], float sl2,
         const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb][r0 + 1], sl2, -mb));
         const float p2 = __builtin_amdgcn_exp2f(fmaf(S[kb][r0 + 2], sl2, -mb));
         const float p3 = __builtin_amdgcn_exp2f(fmaf(S[kb][r0 + 3], sl2, -mb));
-        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        // the conversion keeps the other half of its destination: start from the
+        // register's stale contents (replaced by the second conversion), not a zero
+        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, pf[w], false);
         packed = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, packed, true);
         pf[w] = packed;
         rs0 = w == 0 ? p0 + p2 : rs0 + (p0 + p2);  // the first terms start the sums (no 0 + p)
@@ -294,7 +296,10 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     qk_tile<D>(SA, KB0, qf, kad0, kad1);
     i32x8_t P0, P1;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) P1[w] = 0;
+    for (int w = 0; w < 8; ++w) {
+        P0[w] = 0;  // the packing reads each register's old contents (one half survives a step)
+        P1[w] = 0;  // "tile -1": P = 0 against the zeroed VB1
+    }
     __syncthreads();
 
     // step t: S holds tile t's scores, Sn receives tile t+1's (issued first, so
