@@ -264,6 +264,44 @@ def main():
                             "frac": a8 / PEAK_FP8_TFLOPS, "traffic": measured_traffic("fp8"),
                             "kernel": "prefill_fp8_kernel<128>", "algorithmic_flop_per_launch": prefill_flop}}
 
+    # Decode over an E4M3 copy of the same 32k cache (one byte per element), timed as
+    # the bf16 decode: back-to-back calls rotating the copies, between two events
+    fp8_dec = None
+    if do_d and not args.no_fp8:
+        fd = W.decode_fp8_inputs(dcfg["seed"], 1, dq.shape[1], kcs[0].shape[2], d, [kcs[0].shape[1]],
+                                 kcs[0].shape[1], False)
+        k8s = [fd.k_cache8.to(dev)] + [None] * (N_KV_COPIES - 1)
+        v8s = [fd.v_cache8.to(dev)] + [None] * (N_KV_COPIES - 1)
+        for i in range(1, N_KV_COPIES):
+            k8s[i], v8s[i] = k8s[0].clone(), v8s[0].clone()
+        q8d, dsk, dsv = fd.q.to(dev), fd.descale_k.to(dev), fd.descale_v.to(dev)
+        o8d = torch.empty_like(q8d)
+        l8d = torch.empty((q8d.shape[0], q8d.shape[1]), dtype=torch.float32, device=dev)
+
+        def run_decode8(i):
+            attn.attn_decode_fp8(q8d, k8s[i % N_KV_COPIES], v8s[i % N_KV_COPIES], dsk, dsv, None, sl, o8d, l8d,
+                                 fd.page_size, fd.max_blocks, fd.scale, chunk, ws)
+        for i in range(args.warmup):
+            run_decode8(i)
+        reps = 5 * args.steps
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(reps):
+            run_decode8(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ms8 = e0.elapsed_time(e1) / reps
+        bytes8 = (k8s[0].numel() + v8s[0].numel()) + q8d.numel() * 2 + o8d.numel() * 2 + l8d.numel() * 4
+        fp8_dec = {"value": bytes8 / (ms8 * 1e-3) / 1e9, "unit": "GB/s", "avg_ms": ms8,
+                   "timing": "%d back-to-back calls between two events" % reps,
+                   "dtype": "fp8-e4m3 cache, bf16 q/o",
+                   "roofline": {"bound": "hbm", "achieved": bytes8 / (ms8 * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": bytes8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                "kernels": "decode_split_kernel<128, false, false, true> + lse_combine_kernel<128>",
+                                "algorithmic_bytes_per_launch": bytes8},
+                   "speedup_vs_bf16_cache": dec_bb_ms / ms8}
+
     if args.copy_calibration:  # reference dispatch for the HBM byte counters: copy 1 GiB
         src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -304,10 +342,12 @@ def main():
                          "avg_ms_events_around_each_call": dec_ms,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode"),
-                                      "kernels": "decode_split_kernel<128, false, false> + lse_combine_kernel<128>",
+                                      "kernels": "decode_split_kernel<128, false, false, false> + lse_combine_kernel<128>",
                                       "algorithmic_bytes_per_launch": decode_bytes}}
     if fp8 is not None:
         out["fp8_prefill"] = fp8
+    if fp8_dec is not None:
+        out["fp8_decode"] = fp8_dec
     if do_p and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(px, args.cpu_seconds)
     print(json.dumps(out), flush=True)

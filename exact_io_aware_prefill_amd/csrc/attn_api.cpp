@@ -105,14 +105,15 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
                 const void *v_cache, const int32_t *block_table, const int32_t *seq_lens, void *o, float *lse_or_null, int batch,
                 int n_q_heads, int n_kv_heads, int head_dim, int page_size, int max_blocks_per_seq, int dtype,
                 float scale, int window_left, float softcap, int chunk_tokens, void *workspace,
-                size_t workspace_bytes, void *stream)
+                size_t workspace_bytes, void *stream, bool kv_e4m3 = false, const float *descale_k = nullptr,
+                const float *descale_v = nullptr)
 {
     if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 ||
         max_blocks_per_seq <= 0 || chunk_tokens < 0 || !variant_ok(window_left, softcap))
         return ATTN_ERR_SHAPE;
     if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
     if (!head_dim_ok(head_dim) || dtype != ATTN_BF16 ||
-        n_q_heads / n_kv_heads > attn::kDecodeMaxGroup)
+        n_q_heads / n_kv_heads > attn::kDecodeMaxGroup || (kv_e4m3 && head_dim == 256))
         return ATTN_ERR_UNSUPPORTED;
     // paged blocks of 16 tokens must not straddle pages
     if (block_table && page_size % attn::kDecodeTokenQuantum != 0) return ATTN_ERR_UNSUPPORTED;
@@ -126,7 +127,8 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
     if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
         !aligned16(workspace) || (lse_or_null && !aligned16(lse_or_null)) ||
-        (append && (!aligned16(k_new) || !aligned16(v_new))))
+        (append && (!aligned16(k_new) || !aligned16(v_new))) ||
+        (reinterpret_cast<uintptr_t>(descale_k) & 3u) != 0 || (reinterpret_cast<uintptr_t>(descale_v) & 3u) != 0)
         return ATTN_ERR_ALIGN;
     const long long cap = (long long)max_blocks_per_seq * page_size;
     const long long max_chunks = (cap + chunk - 1) / chunk;
@@ -148,6 +150,9 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
     p.v_new = v_new;
     p.window = window_left;
     p.softcap = softcap;
+    p.kv_e4m3 = kv_e4m3;
+    p.descale_k = descale_k;
+    p.descale_v = descale_v;
     p.o_parts = static_cast<float *>(workspace);
     p.lse_parts = p.o_parts + rows * (size_t)max_chunks * head_dim;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -277,6 +282,17 @@ int attn_decode_ext(const void *q, const void *k_new_or_null, const void *v_new_
     return decode_impl(k_new_or_null || v_new_or_null, q, k_new_or_null, v_new_or_null, k_cache, v_cache,
                        block_table, seq_lens, o, lse_or_null, batch, n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale,
                        window_left, softcap, chunk_tokens, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache, const float *descale_k_or_null,
+                    const float *descale_v_or_null, const int32_t *block_table, const int32_t *seq_lens, void *o,
+                    float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,
+                    int max_blocks_per_seq, float scale, int chunk_tokens, void *workspace, size_t workspace_bytes,
+                    void *stream)
+{
+    return decode_impl(false, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, o, lse_or_null, batch,
+                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, ATTN_BF16, scale, -1, 0.f,
+                       chunk_tokens, workspace, workspace_bytes, stream, true, descale_k_or_null, descale_v_or_null);
 }
 
 int attn_lse_combine(const float *o_parts, const float *lse_parts, const int32_t *n_splits_or_null,

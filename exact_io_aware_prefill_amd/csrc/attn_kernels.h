@@ -61,6 +61,10 @@ struct DecodeParams {
     // and logit soft-cap (0: none), as for prefill
     int window = -1;
     float softcap = 0.f;
+    // E4M3 cache (k_cache, v_cache hold one byte per element), with per-(sequence,
+    // KV head) descales [B, Hkv] (NULL: 1); plain decode only, head_dim 64 or 128
+    bool kv_e4m3 = false;
+    const float *descale_k = nullptr, *descale_v = nullptr;
 };
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 

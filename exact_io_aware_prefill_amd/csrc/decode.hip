@@ -84,6 +84,8 @@ struct SplitArgs {
     // in base-2 units, with cap_log2 = cap * log2(e) and cap_k = 2 log2(e) scale / cap
     int window;
     float cap_log2, cap_k;
+    // FP8 cache only: descale factors [B, Hkv] of K and V (NULL: 1)
+    const float *dk, *dv;
 };
 
 // Tokens the query attends for sequence b, and the index of the appended token
@@ -142,12 +144,33 @@ struct Geo {
     static_assert(VI % VP == 0, "whole permutation periods per step");
 };
 
-// Registers of one step: K as score A operands [block][k-step], V rows as loaded.
-template <int D>
-struct StepRegs {
-    uint4 k[2][D / 32];
-    uint4 v[Geo<D>::VI];
+// Load geometry of the cache: bf16 rows of 2D bytes, or E4M3 rows of D bytes.
+template <int D, bool KV8>
+struct KvGeo {
+    static constexpr int RB = KV8 ? D : 2 * D;    // bytes of one token row of one head
+    static constexpr int NC = RB / 16;            // 16-byte chunks per row
+    static constexpr int RPI = 64 / NC;           // V rows covered by one load instruction
+    static constexpr int VI = kStep / RPI;        // V load instructions per step
+    static constexpr int VIB = VI / 2;            // ... per 16-token block
+    static constexpr int KL = KV8 ? D / 64 : D / 32;  // 16-byte K loads per lane per block
 };
+
+// Registers of one step: K as loaded [block][load], V rows as loaded.
+template <int D, bool KV8>
+struct StepRegs {
+    uint4 k[2][KvGeo<D, KV8>::KL];
+    uint4 v[KvGeo<D, KV8>::VI];
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Four E4M3 bytes -> four bf16 (exact: every E4M3 value is a bf16 value).
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w)
+{
+    const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.f, false);
+    const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.f, true);
+    return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
 
 // Per-lane constants of the loads.
 struct LaneOffsets {
@@ -156,12 +179,12 @@ struct LaneOffsets {
     int l16, vtok;
 };
 
-template <int D>
-__device__ __forceinline__ void issue_step(const SplitArgs &a, StepRegs<D> &s, const char *kbase,
+template <int D, bool KV8>
+__device__ __forceinline__ void issue_step(const SplitArgs &a, StepRegs<D, KV8> &s, const char *kbase,
                                            const char *vbase, int b, int tb, int t_end, uint32_t rstride,
                                            const LaneOffsets &lo)
 {
-    using Gm = Geo<D>;
+    using Gm = KvGeo<D, KV8>;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
         const int t0 = tb + 16 * blk;
@@ -172,7 +195,7 @@ __device__ __forceinline__ void issue_step(const SplitArgs &a, StepRegs<D> &s, c
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0 * Gm::RB, nrec);
         const uint32_t ko = (t0 + lo.l16 < t_end) ? lo.k : kOutOfRange;
 #pragma unroll
-        for (int st = 0; st < D / 32; ++st) s.k[blk][st] = bload16(rk, ko + 64u * st, 0);
+        for (int st = 0; st < Gm::KL; ++st) s.k[blk][st] = bload16(rk, ko + 64u * st, 0);
 #pragma unroll
         for (int i = 0; i < Gm::VIB; ++i) {
             const int tok = Gm::RPI * i + lo.vtok;  // token within the block
@@ -197,12 +220,18 @@ __device__ __forceinline__ float soft_cap_log2(float raw, float cap_log2, float 
     return fmaf(-2.f * cap_log2, r, cap_log2);
 }
 
-template <int D, bool EXT>
-__device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<D> &s, char *slab,
+// KV8: the cache holds E4M3 codes.  A lane's K bytes 16G + 64j .. +15 (dims
+// 64j + 16G ..) become the bf16 operands of k-steps 2j and 2j+1, so its query
+// fragments take the same dims (see the kernel); V rows are converted to bf16 on
+// their way into the slab, as two 16-byte chunks per loaded chunk.
+template <int D, bool EXT, bool KV8>
+__device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<D, KV8> &s, char *slab,
                                              const bf16x8_t *qf, f32x4_t *acc, float &m, float &l, int tb,
-                                             int t_lo, int t_end, int G, const uint32_t *vstore, uint32_t vread)
+                                             int t_lo, int t_end, int G, const uint32_t *vstore, uint32_t vread,
+                                             float scale_log2)
 {
     using Gm = Geo<D>;
+    using Lg = KvGeo<D, KV8>;
     // scores of the two 16-token blocks
     f32x4_t st[2];
 #pragma unroll
@@ -210,14 +239,36 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
 #pragma unroll
         for (int i = 0; i < 4; ++i) st[blk][i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-            st[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(s.k[blk][ks]), qf[ks], st[blk], 0, 0, 0);
+        for (int ks = 0; ks < D / 32; ++ks) {
+            bf16x8_t kf;
+            if constexpr (KV8) {
+                const uint4 w = s.k[blk][ks >> 1];
+                const uint2 a0 = e4m3x4_to_bf16((ks & 1) ? w.z : w.x);
+                const uint2 a1 = e4m3x4_to_bf16((ks & 1) ? w.w : w.y);
+                kf = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+            } else {
+                kf = as_bf16x8(s.k[blk][ks]);
+            }
+            st[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], st[blk], 0, 0, 0);
+        }
     }
     // V rows into the wave's slab.  LDS executes one wave's accesses in order, so
     // these stores land after the previous step's transpose reads of the slab.
+    if constexpr (KV8) {
 #pragma unroll
-    for (int i = 0; i < Gm::VI; ++i)
-        *reinterpret_cast<uint4 *>(slab + vstore[i % Gm::VP] + (i - i % Gm::VP) * Gm::RPI * Gm::RB) = s.v[i];
+        for (int i = 0; i < Lg::VI; ++i) {
+            const uint4 w = s.v[i];
+            const uint2 b0 = e4m3x4_to_bf16(w.x), b1 = e4m3x4_to_bf16(w.y);
+            const uint2 b2 = e4m3x4_to_bf16(w.z), b3 = e4m3x4_to_bf16(w.w);
+            char *row = slab + i * Lg::RPI * Gm::RB;
+            *reinterpret_cast<uint4 *>(row + vstore[0]) = make_uint4(b0.x, b0.y, b1.x, b1.y);
+            *reinterpret_cast<uint4 *>(row + vstore[1]) = make_uint4(b2.x, b2.y, b3.x, b3.y);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < Gm::VI; ++i)
+            *reinterpret_cast<uint4 *>(slab + vstore[i % Gm::VP] + (i - i % Gm::VP) * Gm::RPI * Gm::RB) = s.v[i];
+    }
 
     // online softmax over this step (lane: query l16, tokens 4G+i of each block)
     const bool tail = tb + kStep > t_end || (EXT && tb < t_lo);
@@ -228,7 +279,7 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float xv = capped ? soft_cap_log2(st[blk][i], a.cap_log2, a.cap_k) : st[blk][i] * a.scale_log2;
+            float xv = capped ? soft_cap_log2(st[blk][i], a.cap_log2, a.cap_k) : st[blk][i] * scale_log2;
             const int tok = tb + 16 * blk + 4 * G + i;
             if (tail && (tok >= t_end || (EXT && tok < t_lo))) xv = -INFINITY;
             x[4 * blk + i] = xv;
@@ -265,12 +316,15 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
     }
 }
 
-// APPEND selects the in-place append variant, EXT the window / soft-cap variant
-// (separate instantiations, so the plain decode keeps its register budget).
-template <int D, bool APPEND, bool EXT>
+// APPEND selects the in-place append variant, EXT the window / soft-cap variant,
+// KV8 an E4M3 cache (separate instantiations, so the plain decode keeps its
+// register budget).
+template <int D, bool APPEND, bool EXT, bool KV8 = false>
 __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(SplitArgs a)
 {
     using Gm = Geo<D>;
+    using Lg = KvGeo<D, KV8>;
+    static_assert(!KV8 || (!APPEND && !EXT), "the E4M3 cache has the plain decode only");
     constexpr int kWaves = split_waves<D>();
     // one slab per wave; reused at the end for the eight waves' [16][D] float outputs
     static_assert(Gm::SLAB == 16 * D * 4, "slab must hold a wave's 16 x D float output");
@@ -295,35 +349,52 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, G = lane >> 4;
     const int g = a.group;
-    const uint32_t rstride = (uint32_t)a.Hkv * Gm::RB;  // bytes between consecutive tokens of one head
+    const uint32_t rstride = (uint32_t)a.Hkv * Lg::RB;  // bytes between consecutive tokens of one head
 
-    // query fragments (B operand of S^T = K Q^T); rows >= g are zero padding
+    // query fragments (B operand of S^T = K Q^T); rows >= g are zero padding.
+    // k-step s holds dims 32s + 8G .. +7, or with the E4M3 cache dims
+    // 64(s >> 1) + 16G + 8(s & 1) .. +7, the dims of the lane's converted K bytes.
     bf16x8_t qf[D / 32];
     {
         const uint16_t *qrow = a.q + ((size_t)b * a.Hq + (size_t)hk * g + l16) * D;
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) {
             uint4 u = make_uint4(0, 0, 0, 0);
-            if (l16 < g) u = *reinterpret_cast<const uint4 *>(qrow + 32 * s + 8 * G);
+            const int d0 = KV8 ? 64 * (s >> 1) + 16 * G + 8 * (s & 1) : 32 * s + 8 * G;
+            if (l16 < g) u = *reinterpret_cast<const uint4 *>(qrow + d0);
             qf[s] = as_bf16x8(u);
         }
     }
+    // effective scale (the E4M3 cache folds its K descale in) and the V descale
+    const float dkv = (KV8 && a.dk) ? a.dk[(size_t)b * a.Hkv + hk] : 1.f;
+    const float dvv = (KV8 && a.dv) ? a.dv[(size_t)b * a.Hkv + hk] : 1.f;
+    const float sl2 = a.scale_log2 * dkv;
 
     LaneOffsets lo;
     lo.l16 = l16;
-    lo.vtok = lane / Gm::NC;
-    const int vchunk = lane % Gm::NC;
+    lo.vtok = lane / Lg::NC;
+    const int vchunk = lane % Lg::NC;
     lo.k = (uint32_t)l16 * rstride + 16u * G;
     lo.v = (uint32_t)lo.vtok * rstride + 16u * vchunk;
     char *slab = slabs + wave * Gm::SLAB;
     // slab byte offsets of this lane's V row stores by load instruction modulo
     // VP (instruction i covers rows i*RPI..; the slot permutation repeats every
     // 8 rows, i.e. every two instructions for D = 128, four for D = 256)
-    uint32_t vstore[Gm::VP];
+    uint32_t vstore[Gm::VP > 2 ? Gm::VP : 2];
+    if constexpr (KV8) {
+        // a loaded chunk (16 dims) becomes bf16 chunks 2 vchunk and 2 vchunk + 1 of
+        // slab row lo.vtok + RPI i; the permutation repeats every 8 rows and RPI is
+        // a multiple of 8, so the offsets hold for every load instruction
+        static_assert(Lg::RPI % 8 == 0, "one permutation period per load instruction");
 #pragma unroll
-    for (int par = 0; par < Gm::VP; ++par) {
-        const int r = Gm::RPI * par + lo.vtok;
-        vstore[par] = (uint32_t)(r * Gm::RB + 16 * (vchunk ^ slab_swz<D>(r)));
+        for (int e = 0; e < 2; ++e)
+            vstore[e] = (uint32_t)(lo.vtok * Gm::RB + 16 * ((2 * vchunk + e) ^ slab_swz<D>(lo.vtok)));
+    } else {
+#pragma unroll
+        for (int par = 0; par < Gm::VP; ++par) {
+            const int r = Gm::RPI * par + lo.vtok;
+            vstore[par] = (uint32_t)(r * Gm::RB + 16 * (vchunk ^ slab_swz<D>(r)));
+        }
     }
     // transpose reads: group G, lane 4r+q reads 8 bytes of slab row 4G+r, dims
     // 16nb + 4q..4q+3; the slot permutation only touches bits 5+ of the offset,
@@ -331,8 +402,8 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
     const int vrow = 4 * G + (l16 >> 2), vq = l16 & 3;
     const uint32_t vread = (uint32_t)(vrow * Gm::RB + 16 * ((vq >> 1) ^ slab_swz<D>(vrow)) + 8 * (vq & 1));
 
-    const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)hk * Gm::RB;
-    const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)hk * Gm::RB;
+    const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)hk * Lg::RB;
+    const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)hk * Lg::RB;
 
     f32x4_t acc[D / 16];
 #pragma unroll
@@ -363,16 +434,39 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
     }
     // with a window, skip this wave's steps that end before it starts
     if (EXT && tb + kStep <= t_lo) tb += ((t_lo - tb - kStep) / stride + 1) * stride;
-    StepRegs<D> r0, r1;
-    issue_step<D>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
-    while (tb < t_end) {
-        issue_step<D>(a, r1, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-        consume_step<D, EXT>(a, r0, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread);
-        tb += stride;
-        if (tb >= t_end) break;
-        issue_step<D>(a, r0, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-        consume_step<D, EXT>(a, r1, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread);
-        tb += stride;
+    if constexpr (!KV8) {
+        StepRegs<D, KV8> r0, r1;
+        issue_step<D, KV8>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
+        while (tb < t_end) {
+            issue_step<D, KV8>(a, r1, kbase, vbase, b, tb + stride, t_end, rstride, lo);
+            consume_step<D, EXT, KV8>(a, r0, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2);
+            tb += stride;
+            if (tb >= t_end) break;
+            issue_step<D, KV8>(a, r0, kbase, vbase, b, tb + stride, t_end, rstride, lo);
+            consume_step<D, EXT, KV8>(a, r1, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2);
+            tb += stride;
+        }
+    } else {
+        // A ring of NS register sets, NS - 1 steps issued ahead.  An E4M3 step is
+        // half the bytes of a bf16 one, yet three or four steps in flight measured
+        // slower than two (32k cache: 13.9 -> 14.5 / 14.7 us), so NS stays 2.
+        constexpr int NS = 2;
+        StepRegs<D, KV8> r[NS];
+#pragma unroll
+        for (int j = 0; j < NS - 1; ++j) issue_step<D, KV8>(a, r[j], kbase, vbase, b, tb + j * stride, t_end, rstride, lo);
+        bool more = tb < t_end;
+        while (more) {
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                if (more) {
+                    issue_step<D, KV8>(a, r[(j + NS - 1) % NS], kbase, vbase, b, tb + (NS - 1) * stride, t_end,
+                                       rstride, lo);
+                    consume_step<D, EXT, KV8>(a, r[j], slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2);
+                    tb += stride;
+                    more = tb < t_end;
+                }
+            }
+        }
     }
 
     // ---- merge the eight wave states (combine rule) ------------------------------
@@ -402,7 +496,7 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
             Lsum += e[w] * ml[1][w][l16];
         }
         const size_t row = (size_t)b * a.Hq + (size_t)hk * g + l16;
-        const float inv = 1.f / Lsum;  // Lsum >= 1: the row's largest term is exp2(0)
+        const float inv = dvv / Lsum;  // Lsum >= 1: the row's largest term is exp2(0)
 #pragma unroll
         for (int nb = wave; nb < D / 16; nb += kWaves) {
             f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
@@ -574,6 +668,8 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     a.lse_parts = p.lse_parts;
     a.k_new = static_cast<const uint16_t *>(p.k_new);
     a.v_new = static_cast<const uint16_t *>(p.v_new);
+    a.dk = p.descale_k;
+    a.dv = p.descale_v;
     a.Hq = p.Hq;
     a.Hkv = p.Hkv;
     a.group = p.Hq / p.Hkv;
@@ -593,6 +689,12 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     auto kernel = [&](auto dconst) {
         constexpr int DD = decltype(dconst)::value;
         constexpr int kThreads = split_waves<DD>() * 64;
+        if constexpr (DD != 256) {
+            if (p.kv_e4m3) {
+                hipLaunchKernelGGL((decode_split_kernel<DD, false, false, true>), grid, dim3(kThreads), 0, stream, a);
+                return;
+            }
+        }
         if (append && ext)
             hipLaunchKernelGGL((decode_split_kernel<DD, true, true>), grid, dim3(kThreads), 0, stream, a);
         else if (append)

@@ -199,6 +199,56 @@ def decode_paged_inputs(seed: int, B: int, Hq: int, Hkv: int, d: int, page_size:
                         page_size, max_blocks, 1.0 / math.sqrt(d), dtype)
 
 
+@dataclass
+class Fp8DecodeInputs:
+    q: torch.Tensor                      # [B, Hq, d] bf16
+    k_cache8: torch.Tensor               # E4M3 codes, layout as DecodeInputs
+    v_cache8: torch.Tensor
+    descale_k: torch.Tensor              # [B, Hkv] float32
+    descale_v: torch.Tensor
+    block_table: Optional[torch.Tensor]
+    seq_lens: torch.Tensor
+    page_size: int
+    max_blocks: int
+    scale: float
+
+
+def decode_fp8_inputs(seed: int, B: int, Hq: int, Hkv: int, d: int, lengths, capacity: int, paged: bool,
+                      page_size: int = 16) -> Fp8DecodeInputs:
+    """The float32 draws of decode_paged_inputs / decode_contiguous_inputs (q kept in
+    bf16), with each sequence's cache rows quantised to E4M3 per KV head: the
+    sequence's largest magnitude of that head maps to 448 (PyTorch's conversion)."""
+    if paged:
+        x = decode_paged_inputs(seed, B, Hq, Hkv, d, page_size, 1, capacity, dtype=F32, lengths=lengths)
+    else:
+        x = decode_contiguous_inputs(seed, B, Hq, Hkv, capacity, d, dtype=F32, page_size=page_size,
+                                     seq_lens=lengths)
+    kc, vc = x.k_cache.clone(), x.v_cache.clone()
+    dk = torch.ones(B, Hkv); dv = torch.ones(B, Hkv)
+    k8 = torch.zeros(kc.shape, dtype=torch.float8_e4m3fn)
+    v8 = torch.zeros(vc.shape, dtype=torch.float8_e4m3fn)
+    for b in range(B):
+        L = int(x.seq_lens[b])
+        if paged:
+            pages = x.block_table[b, :-(-L // page_size)].long() if L > 0 else torch.zeros(0, dtype=torch.long)
+            rows_k, rows_v = kc[pages], vc[pages]            # [np, P, Hkv, d]
+        else:
+            rows_k, rows_v = kc[b:b + 1, :max(L, 1)], vc[b:b + 1, :max(L, 1)]
+        for h in range(Hkv):
+            for src, ds in ((rows_k, dk), (rows_v, dv)):
+                amax = float(src[..., h, :].abs().max()) if src.numel() else 0.0
+                ds[b, h] = max(amax, 1e-12) / 448.0
+        for h in range(Hkv):
+            if paged:
+                k8[pages, :, h] = (kc[pages, :, h] / dk[b, h]).to(torch.float8_e4m3fn)
+                v8[pages, :, h] = (vc[pages, :, h] / dv[b, h]).to(torch.float8_e4m3fn)
+            else:
+                k8[b, :, h] = (kc[b, :, h] / dk[b, h]).clamp(-448, 448).to(torch.float8_e4m3fn)
+                v8[b, :, h] = (vc[b, :, h] / dv[b, h]).clamp(-448, 448).to(torch.float8_e4m3fn)
+    return Fp8DecodeInputs(x.q.to(torch.bfloat16), k8, v8, dk.float(), dv.float(), x.block_table, x.seq_lens,
+                           x.page_size, x.max_blocks, x.scale)
+
+
 def decode_new_rows(seed: int, B: int, Hkv: int, d: int, dtype: str = BF16):
     """The appended token's key and value rows [B, Hkv, d] (draw order: K, then V)."""
     rng = np.random.default_rng(seed)

@@ -26,6 +26,7 @@
  *   - attn_prefill_fp8: the prefill on 8-bit (E4M3) inputs with descale
  *     factors, the FP8 direction the page names for FlashAttention-3 (section
  *     "The bottleneck it attacks");
+ *   - attn_decode_fp8: the decode over an FP8 (E4M3) KV cache;
  *   - attn_lse_combine: that reduction on its own -- the combine rule for
  *     independent partials, a softmax over the partials' log-sum-exps
  *     (section "The online softmax, with every symbol defined" and the
@@ -55,7 +56,7 @@
  *     n_kv_heads) (consecutive query heads share a KV head).
  *   - Head sizes 64, 128 and 256 (256 being the largest the page's section
  *     "Interaction with post-trained models" names) on every entry point except
- *     attn_prefill_fp8 (64 and 128).
+ *     attn_prefill_fp8 and attn_decode_fp8 (64 and 128).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -251,6 +252,24 @@ int attn_decode_ext(const void *q, const void *k_new_or_null, const void *v_new_
                     float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,
                     int max_blocks_per_seq, int dtype, float scale, int window_left, float softcap,
                     int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_fp8 -- attn_decode over an FP8 KV cache: k_cache and v_cache hold
+ * E4M3 codes (one byte per element, same layouts as attn_decode), the values being
+ * descale_k * k8 and descale_v * v8 with one factor per (sequence, KV head)
+ * ([batch, n_kv_heads] float32 on the device, 4-byte aligned; NULL means 1).  The
+ * decode split of the pofe.ai page's section "Decode: a different bottleneck" reads
+ * half the bytes per token of a bf16 cache.  q and o are bfloat16 as in
+ * attn_decode.  The codes convert to bf16 exactly; the products and the combine
+ * are those of attn_decode, with descale_k folded into the score scale and
+ * descale_v into the output.  head_dim 64 or 128 (else ATTN_ERR_UNSUPPORTED); no
+ * append, window or soft-cap.  Workspace, chunking and limits as attn_decode.
+ */
+int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache, const float *descale_k_or_null,
+                    const float *descale_v_or_null, const int32_t *block_table, const int32_t *seq_lens, void *o,
+                    float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,
+                    int max_blocks_per_seq, float scale, int chunk_tokens, void *workspace, size_t workspace_bytes,
+                    void *stream);
 
 /*
  * attn_decode_chunk_tokens -- the chunk size attn_decode uses for these

@@ -300,3 +300,31 @@ def prefill_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale
     k = k * dk[:, :, None, None]
     v = v * dv[:, :, None, None]
     return prefill(q, k, v, causal, scale, row_step=row_step)
+
+
+def decode_fp8(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, scale: float,
+               page_size: int, max_blocks: int):
+    """Decode over an E4M3 cache: sequence b reads descale_k[b, hk] * decode(k8) and
+    descale_v[b, hk] * decode(v8) for KV head hk (None = 1), then the plain decode."""
+    k, v = e4m3_decode(k_cache8), e4m3_decode(v_cache8)
+    qq = _f64(q)
+    B, Hkv = qq.shape[0], k.shape[-2]
+
+    def ds(x):
+        return np.ones((B, Hkv)) if x is None else _f64(x).reshape(B, Hkv)
+    dk, dv = ds(descale_k), ds(descale_v)
+    sl = _i32(seq_lens)
+    bt = None if block_table is None else _i32(block_table)
+    o = np.empty(qq.shape)
+    lse = np.empty(qq.shape[:2])
+    for b in range(B):
+        if bt is None:  # contiguous [B, S, Hkv, d]: this sequence's rows only
+            kb = k[b:b + 1] * dk[b][None, None, :, None]
+            vb = v[b:b + 1] * dv[b][None, None, :, None]
+            ob, lb = decode(qq[b:b + 1], kb, vb, None, sl[b:b + 1], scale, page_size, max_blocks)
+        else:  # paged pool [pages, P, Hkv, d] through this sequence's table row
+            kb = k * dk[b][None, None, :, None]
+            vb = v * dv[b][None, None, :, None]
+            ob, lb = decode(qq[b:b + 1], kb, vb, bt[b:b + 1], sl[b:b + 1], scale, page_size, max_blocks)
+        o[b], lse[b] = ob[0], lb[0]
+    return o, lse

@@ -231,6 +231,29 @@ def test_decode_ext_argument_errors(kw, code):
     assert decode_ext(**kw) == code
 
 
+def decode_fp8(q=FAKE, kc=FAKE, vc=FAKE, dk=0, dv=0, bt=FAKE, sl=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, d=128,
+               P_=16, maxb=8, chunk=0, ws=FAKE, wsb=1 << 30):
+    return attn.lib.attn_decode_fp8(P(q), P(kc), P(vc), P(dk), P(dv), P(bt), P(sl), P(o), P(lse), B, Hq, Hkv, d, P_,
+                                    maxb, 0.1, chunk, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), attn.ATTN_ERR_NULL),
+    (dict(kc=0), attn.ATTN_ERR_NULL),
+    (dict(B=-1), attn.ATTN_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
+    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),      # E4M3 cache: head sizes 64 and 128
+    (dict(d=80), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(P_=8), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(ws=0), attn.ATTN_ERR_WORKSPACE),
+    (dict(dk=FAKE + 2), attn.ATTN_ERR_ALIGN),      # descales are float arrays: 4-byte aligned
+    (dict(vc=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(B=0, q=0, kc=0, vc=0, bt=0, sl=0, o=0, ws=0), attn.ATTN_OK),
+])
+def test_decode_fp8_argument_errors(kw, code):
+    assert decode_fp8(**kw) == code
+
+
 def test_decode_contiguous_accepts_any_page_size_for_capacity():
     # page_size only fixes capacity when block_table is NULL; with a NULL workspace the
     # host check stops at ERR_WORKSPACE, i.e. after the page-size checks passed

@@ -142,3 +142,38 @@ def test_fp8_prefill_16k_sampled_rows(attn):
     rows = np.arange(0, N, step)
     check_fp8("fp8 16k (sampled)", o[:, :, rows], lse[:, :, rows], ro[:, :, rows], rl[:, :, rows],
               row_bounds(x, rows))
+
+
+# ------------------------------------------------------------------ decode over an E4M3 cache
+DEC_LENS = [1, 15, 16, 17, 100, 511, 513, 1000]
+
+
+@pytest.mark.parametrize("g", [1, 4, 16])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("chunk", [16, 256, 0])
+def test_fp8_cache_decode(attn, g, d, paged, chunk):
+    """The E4M3 codes convert to bf16 exactly and the descales fold into the score
+    scale and the output, so the bf16 decode's bars apply (2e-2 on O, 1e-3 on LSE)."""
+    say("case: fp8-cache decode g=%d d=%d paged=%s chunk=%d" % (g, d, paged, chunk))
+    x = W.decode_fp8_inputs(3300 + g + d + chunk, len(DEC_LENS), g * 2, 2, d, DEC_LENS, 1024, paged)
+    o, lse = attn.decode_fp8(dev(x.q), dev(x.k_cache8), dev(x.v_cache8), dev(x.block_table), dev(x.seq_lens),
+                             x.page_size, x.max_blocks, dev(x.descale_k), dev(x.descale_v), x.scale, chunk)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_fp8(x.q, x.k_cache8, x.v_cache8, x.descale_k, x.descale_v, x.block_table, x.seq_lens,
+                               x.scale, x.page_size, x.max_blocks)
+    from gpu_common import BF16_TOL, check
+    check("fp8-cache decode g=%d d=%d paged=%d chunk=%d" % (g, d, paged, chunk), o, lse, ro, rl, BF16_TOL)
+
+
+def test_fp8_cache_decode_32k(attn):
+    """The 32k-token decode (28 query / 4 KV heads, 64 chunks of 512) over an E4M3 cache."""
+    say("case: fp8-cache decode 32k")
+    x = W.decode_fp8_inputs(4, 1, 28, 4, 128, [32768], 32768, False)
+    o, lse = attn.decode_fp8(dev(x.q), dev(x.k_cache8), dev(x.v_cache8), None, dev(x.seq_lens), x.page_size,
+                             x.max_blocks, dev(x.descale_k), dev(x.descale_v), x.scale, 512)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_fp8(x.q, x.k_cache8, x.v_cache8, x.descale_k, x.descale_v, None, x.seq_lens, x.scale,
+                               x.page_size, x.max_blocks)
+    from gpu_common import BF16_TOL, check
+    check("fp8-cache decode 32k", o, lse, ro, rl, BF16_TOL)

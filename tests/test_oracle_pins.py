@@ -692,3 +692,50 @@ def test_fp8_prefill_descale_invariants():
     # the changed group equals the same call with the scale doubled for that sequence
     o5, lse5 = oracle.prefill_fp8(q8[1:], k8[1:], v8[1:], dq[1:], dk[1:], dv[1:], True, 0.5)
     assert np.max(np.abs(o5[0, 0:g] - o4[1, 0:g])) < 1e-12
+
+
+def test_fp8_decode_worked_example_and_invariants():
+    """Decode over an E4M3 cache: the worked example (codes by hand, as for the FP8
+    prefill) gives the printed 1.1381 for the last token; doubling descale_k while
+    halving scale changes nothing; descale_v scales O; one sequence's descales touch
+    only that sequence; decode of token L-1 equals FP8 prefill row L-1, bitwise."""
+    d = 16
+    q = np.zeros((1, 1, d)); q[0, 0, 0] = 1.0
+    k8 = np.zeros((1, 4, 1, d), np.uint8); v8 = np.zeros_like(k8)
+    k8[0, :, 0, 0] = [0x40, 0x38, 0x48, 0x44]
+    v8[0, :, 0, 0] = [0x38, 0x00, 0x40, 0xb8]
+    o, lse = oracle.decode_fp8(q, k8, v8, None, None, None, np.array([4], np.int32), 1.0, 4, 1)
+    assert round(o[0, 0, 0], 4) == 1.1381
+    e = math.e
+    assert abs(lse[0, 0] - math.log(e**2 + e + e**4 + e**3)) < 1e-12
+
+    rng = np.random.default_rng(71)
+    B, Hq, Hkv, S, d = 3, 4, 2, 48, 16
+    codes = lambda shape: (rng.integers(0, 256, size=shape).astype(np.uint8) & 0x3e) | (
+        rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+    qq = rng.standard_normal((B, Hq, d))
+    kc, vc = codes((B, S, Hkv, d)), codes((B, S, Hkv, d))
+    sl = np.array([1, 30, 48], np.int32)
+    dk = rng.uniform(0.5, 2, (B, Hkv)); dv = rng.uniform(0.5, 2, (B, Hkv))
+    o, lse = oracle.decode_fp8(qq, kc, vc, dk, dv, None, sl, 0.3, 16, 3)
+    o2, lse2 = oracle.decode_fp8(qq, kc, vc, 2 * dk, dv, None, sl, 0.15, 16, 3)
+    assert np.max(np.abs(o2 - o)) < 1e-12 and np.max(np.abs(lse2 - lse)) < 1e-12
+    o3, lse3 = oracle.decode_fp8(qq, kc, vc, dk, 3 * dv, None, sl, 0.3, 16, 3)
+    assert np.max(np.abs(o3 - 3 * o)) < 1e-12 and np.max(np.abs(lse3 - lse)) < 1e-12
+    dv4 = dv.copy(); dv4[2] *= 5
+    o4, _ = oracle.decode_fp8(qq, kc, vc, dk, dv4, None, sl, 0.3, 16, 3)
+    assert np.array_equal(o4[:2], o[:2]) and not np.allclose(o4[2], o[2])
+    # token L-1 of sequence 2 against the FP8 prefill of the same rows (query at row L-1)
+    L = 48
+    q8 = np.zeros((1, Hq, L, d), np.uint8)
+    qp = np.zeros((1, Hq, L, d)); qp[0, :, L - 1] = qq[2]
+    # the prefill takes E4M3 queries: compare on a query that is exact in E4M3
+    qx = oracle.e4m3_decode(codes((Hq, d)))
+    q8[0, :, L - 1] = 0  # placeholder rows; only row L-1 is compared
+    qcodes = torch.from_numpy(qx).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    q8[0, :, L - 1] = qcodes
+    kp = kc[2].transpose(1, 0, 2)[None].copy(); vp = vc[2].transpose(1, 0, 2)[None].copy()
+    op, lp = oracle.prefill_fp8(q8, kp, vp, None, dk[2:3], dv[2:3], True, 0.3)
+    od, ld = oracle.decode_fp8(qx[None], kc[2:3], vc[2:3], dk[2:3], dv[2:3], None, np.array([L], np.int32),
+                               0.3, 16, 3)
+    assert np.array_equal(op[0, :, L - 1], od[0]) and np.array_equal(lp[0, :, L - 1], ld[0])
