@@ -32,11 +32,11 @@ CSRC = os.path.join(ROOT, "exact_io_aware_prefill_amd", "csrc")
 # valid while the kernel source they were taken on is unchanged (sha256 recorded)
 TRAFFIC = {
     "prefill": {"file": os.path.join(ROOT, "profiles", "prefill_bf16_n16384_traffic.json"),
-                "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel"},
+                "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel<128, false>"},
     "decode": {"file": os.path.join(ROOT, "profiles", "decode_split_s32768_traffic.json"),
-               "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel"},
+               "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel<128, false, false, false>"},
     "fp8": {"file": os.path.join(ROOT, "profiles", "prefill_fp8_n16384_traffic.json"),
-            "src": os.path.join(CSRC, "prefill_fp8.hip"), "kernel": "prefill_fp8_kernel"},
+            "src": os.path.join(CSRC, "prefill_fp8.hip"), "kernel": "prefill_fp8_kernel<128>"},
 }
 COPY_BYTES = 1 << 30  # reference dispatch for the counters: a 1 GiB device-to-device copy
 N_KV_COPIES = 8
