@@ -41,12 +41,15 @@
 //     score registers.
 //   * The exponentials of tile t use the running max from before the tile, so
 //     they do not wait for the tile's own row max.  If a lane's probability sum
-//     for the tile exceeds 256 (so some probability may exceed 2^8), or the row
-//     has no reference yet, a rare path raises the max to the true running max,
+//     for the tile exceeds 256 (so some probability may exceed 2^8), or (window
+//     variant) the row has no reference yet, a rare path raises the max to the
+//     true running max,
 //     rescales l and O by c and recomputes the tile's probabilities.  Any
 //     reference value gives the same O = acc/l and LSE = m + ln l; the bound
-//     keeps every probability <= 256 in float32.  Exponentials run in base 2
-//     with scale*log2(e) folded into one FMA.
+//     keeps every probability <= 256 in float32.  The plain kernel takes its
+//     first reference from the first tile's true row max.  Exponentials run in
+//     base 2 with scale*log2(e) folded into one FMA; the reference is kept in
+//     those units.
 //   * Work order: workgroup ids walk (sequence, KV head, query tile, query head)
 //     with the query head fastest, so the query heads that share a KV head run
 //     at the same time and read the same key/value tiles.  Query tiles are
@@ -364,10 +367,12 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[bb][db][i] = 0.f;
-    float m[kBlocks], l[kBlocks];  // reference max of raw scores / this lane's share of the sum
+    // mb: the reference max of the scores in base-2 units (raw max * scale * log2 e);
+    // l: this lane's share of the row sum
+    float mb[kBlocks], l[kBlocks];
 #pragma unroll
     for (int bb = 0; bb < kBlocks; ++bb) {
-        m[bb] = -INFINITY;
+        mb[bb] = -INFINITY;
         l[bb] = 0.f;
     }
     const float sl2 = a.scale_log2;
@@ -402,7 +407,45 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
     wait_loads();
     __syncthreads();
     f32x16_t S[kBlocks][kKB];
+    // diagonal / ragged tile: mask keys past the row (causal) or past N; with a
+    // window also keys before row - window
+    auto mask_tile = [&](int k0) {
+        const bool win = EXT && a.window >= 0 && k0 < wrow0 + kBlocks * 32 - 1 - a.window;
+        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > N || win) {
+#pragma unroll
+            for (int bb = 0; bb < kBlocks; ++bb) {
+                const int qrow = wrow0 + 32 * bb + l32;
+                const int lim = (a.causal ? min(qrow, N - 1) : N - 1) - (k0 + 4 * hh);
+                const int low = win ? qrow - a.window - (k0 + 4 * hh) : INT_MIN;
+#pragma unroll
+                for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int e = 32 * kb + 8 * (i >> 2) + (i & 3);
+                        if (e > lim || (EXT && e < low)) S[bb][kb][i] = -INFINITY;
+                    }
+            }
+        }
+    };
+    // the row max of the visible keys of scores S, both half-waves combined
+    auto row_max = [&](int bb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[bb][kb][i]);
+        return fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
+    };
     qk_tile<D>(S, KB0, qf, kad);
+    if (!EXT) {
+        // The plain kernel starts from the first tile's true max: every row sees key
+        // 0 (causal) or all keys < N, so it is finite, and the steps need no check
+        // for a missing reference.  (The variant's soft-cap and window act at the
+        // start of each step, so it keeps the check.)
+        mask_tile(kbeg);
+#pragma unroll
+        for (int bb = 0; bb < kBlocks; ++bb) mb[bb] = row_max(bb) * sl2;
+    }
     bf16x8_t P0[kBlocks][kKS], P1[kBlocks][kKS];
 #pragma unroll
     for (int bb = 0; bb < kBlocks; ++bb)
@@ -428,34 +471,17 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
 #pragma unroll
                     for (int i = 0; i < 16; ++i) S[bb][kb][i] = soft_cap(S[bb][kb][i], a.cap_raw, a.cap_k);
         }
-        // diagonal / ragged tile: mask keys past the row (causal) or past N; with a
-        // window also keys before row - window
-        const bool win = EXT && a.window >= 0 && k0 < wrow0 + kBlocks * 32 - 1 - a.window;
-        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > N || win) {
-#pragma unroll
-            for (int bb = 0; bb < kBlocks; ++bb) {
-                const int qrow = wrow0 + 32 * bb + l32;
-                const int lim = (a.causal ? min(qrow, N - 1) : N - 1) - (k0 + 4 * hh);
-                const int low = win ? qrow - a.window - (k0 + 4 * hh) : INT_MIN;
-#pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int e = 32 * kb + 8 * (i >> 2) + (i & 3);
-                        if (e > lim || (EXT && e < low)) S[bb][kb][i] = -INFINITY;
-                    }
-            }
-        }
+        mask_tile(k0);
         // ---- matrix cores: PV(t-1); vector ALUs: probabilities of tile t against
-        // the reference max from before the tile (the first tile, with no
-        // reference yet, always takes the rare path)
+        // the reference max from before the tile (the variant's first tile, with no
+        // reference yet, takes the rare path)
         // raised wave priority while this block issues: the arbiter then favours the
         // wave whose products and softmax interleave, over waves in their QK part
         __builtin_amdgcn_s_setprio(1);
         pv_tile<D>(acc, Vp, Pp, vad);
         float rs[kBlocks];
 #pragma unroll
-        for (int bb = 0; bb < kBlocks; ++bb) rs[bb] = softmax_tile(S[bb], sl2, m[bb] * sl2, Pc[bb]);
+        for (int bb = 0; bb < kBlocks; ++bb) rs[bb] = softmax_tile(S[bb], sl2, mb[bb], Pc[bb]);
         // Instruction order of this block: the V operand reads run two products
         // ahead, and the softmax's VALU work is spread between the products so
         // the matrix cores and the vector ALUs overlap inside the wave.
@@ -470,7 +496,7 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
         __builtin_amdgcn_s_setprio(0);
         // ---- rare: some probability may exceed 2^8 (or a row has no reference yet):
         // raise the reference to the true running max, rescale, redo the tile
-        bool redo = m[0] == -INFINITY;
+        bool redo = EXT && mb[0] == -INFINITY;
 #pragma unroll
         for (int bb = 0; bb < kBlocks; ++bb) redo = redo || rs[bb] > kMaxLaneSum;
         if (__builtin_amdgcn_ballot_w64(redo)) {
@@ -482,25 +508,19 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
                 for (int jj = 0; jj < kKS; ++jj) asm volatile("" ::"v"(Pc[bb][jj]));
 #pragma unroll
             for (int bb = 0; bb < kBlocks; ++bb) {
-                float mx = -INFINITY;
-#pragma unroll
-                for (int kb = 0; kb < kKB; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[bb][kb][i]);
-                mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
-                const float m_new = fmaxf(m[bb], mx);
-                // 0 while m = -inf.  Only the variant can meet a row with no visible key
-                // yet (m_new = -inf); its state stays (m, l, acc) = (-inf, 0, 0), and a
-                // reference of 0 gives the masked scores probability 0.
-                const bool none = EXT && m_new == -INFINITY;
-                const float c = none ? 1.f : __builtin_amdgcn_exp2f((m[bb] - m_new) * sl2);
+                const float mb_new = fmaxf(mb[bb], row_max(bb) * sl2);
+                // c = 0 while mb = -inf.  Only the variant can meet a row with no visible
+                // key yet (mb_new = -inf); its state stays (mb, l, acc) = (-inf, 0, 0),
+                // and a reference of 0 gives the masked scores probability 0.
+                const bool none = EXT && mb_new == -INFINITY;
+                const float c = none ? 1.f : __builtin_amdgcn_exp2f(mb[bb] - mb_new);
                 l[bb] *= c;
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) acc[bb][db][i] *= c;
-                m[bb] = m_new;
-                rs[bb] = softmax_tile(S[bb], sl2, none ? 0.f : m[bb] * sl2, Pc[bb]);
+                mb[bb] = mb_new;
+                rs[bb] = softmax_tile(S[bb], sl2, none ? 0.f : mb[bb], Pc[bb]);
             }
         }
 #pragma unroll
@@ -554,7 +574,7 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
                     *reinterpret_cast<uint2 *>(orow + d0) = pk;
                 }
             }
-            if (hh == 0) a.lse[lse_off + qrow] = m[bb] * a.scale + log2f(lt) * kLn2;
+            if (hh == 0) a.lse[lse_off + qrow] = (mb[bb] + log2f(lt)) * kLn2;  // mb * ln 2 = max * |scale|
         }
     }
 }
