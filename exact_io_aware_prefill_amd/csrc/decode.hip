@@ -45,6 +45,10 @@
 //     first live chunk), waves skip their steps that end before it, and the one
 //     step that straddles its start is masked.  Soft-capping maps each score s to
 //     cap * tanh(s / cap) before the masking.
+//   * Another instantiation reads an E4M3 (8-bit float) cache: half the bytes per
+//     token, the quantity decode is bound by.  The codes convert exactly to bf16
+//     (K in registers, V on its way into the slab), and the per-(sequence, KV
+//     head) descales fold into the score scale and the output.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

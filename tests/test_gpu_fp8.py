@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from exact_io_aware_prefill_amd import workloads as W
-from gpu_common import dev, say
+from gpu_common import BF16_TOL, check, dev, say
 
 pytestmark = pytest.mark.gpu
 LSE_TOL = 1e-3
@@ -162,7 +162,6 @@ def test_fp8_cache_decode(attn, g, d, paged, chunk):
     torch.cuda.synchronize()
     ro, rl = oracle.decode_fp8(x.q, x.k_cache8, x.v_cache8, x.descale_k, x.descale_v, x.block_table, x.seq_lens,
                                x.scale, x.page_size, x.max_blocks)
-    from gpu_common import BF16_TOL, check
     check("fp8-cache decode g=%d d=%d paged=%d chunk=%d" % (g, d, paged, chunk), o, lse, ro, rl, BF16_TOL)
 
 
@@ -175,5 +174,27 @@ def test_fp8_cache_decode_32k(attn):
     torch.cuda.synchronize()
     ro, rl = oracle.decode_fp8(x.q, x.k_cache8, x.v_cache8, x.descale_k, x.descale_v, None, x.seq_lens, x.scale,
                                x.page_size, x.max_blocks)
-    from gpu_common import BF16_TOL, check
     check("fp8-cache decode 32k", o, lse, ro, rl, BF16_TOL)
+
+
+def test_fp8_cache_decode_matches_bf16_decode_of_the_same_values(attn):
+    """With NULL descales the E4M3 codes are the values themselves, each exactly a bf16
+    value, so the bf16 decode over the same cache widened to bf16 sums the same terms
+    (in another order): LSE agrees to 1e-3 and O to bf16 rounding of values up to 448.
+    Both are also held to the oracle, which reads NULL descales as 1."""
+    say("case: fp8-cache decode vs bf16 decode, no descales")
+    x = W.decode_fp8_inputs(3400, len(DEC_LENS), 8, 2, 128, DEC_LENS, 1024, True)
+    scale = 1.0 / (float(x.k_cache8.float().std()) * math.sqrt(128))  # scores stay O(1)
+    q, k8, v8 = dev(x.q), dev(x.k_cache8), dev(x.v_cache8)
+    bt, sl = dev(x.block_table), dev(x.seq_lens)
+    o8, l8 = attn.decode_fp8(q, k8, v8, bt, sl, x.page_size, x.max_blocks, None, None, scale, 64)
+    o, lse = attn.decode(q, k8.to(torch.bfloat16), v8.to(torch.bfloat16), bt, sl, x.page_size, x.max_blocks,
+                         scale, 64)
+    torch.cuda.synchronize()
+    o_tol = 448.0 * 2.0 ** -7
+    assert float((l8 - lse).abs().max()) <= 1e-3
+    assert float((o8.float() - o.float()).abs().max()) <= o_tol
+    ro, rl = oracle.decode_fp8(x.q, x.k_cache8, x.v_cache8, None, None, x.block_table, x.seq_lens, scale,
+                               x.page_size, x.max_blocks)
+    assert np.max(np.abs(l8.cpu().numpy() - rl)) <= 1e-3
+    assert np.max(np.abs(o8.float().cpu().numpy() - ro)) <= o_tol
