@@ -516,10 +516,13 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
 
 // ---------------------------------------------------------------------------
 // Combine: one workgroup of 256 threads per row (sequence x query head).  Thread
-// (sg, c) accumulates float4 column c over splits sg, sg + SG, ...; the first
-// batch of partial loads is issued before the row's Lambda is reduced, so the
-// whole row is requested at once for up to 8*SG splits.  Each wave reduces the
-// row's log-sum-exps itself (no barrier); the SG partial sums meet in LDS.
+// (sg, c) accumulates float4 column c over splits sg, sg + SG, ...  The first
+// batch of loads (partials and log-sum-exps of up to 8*SG splits) is issued
+// before the row's split count is known: the loads stay inside the row's
+// max_splits slots, and splits outside [first, ns) get weight 0 once the count
+// arrives, so the count's load and the partials' loads are in flight together.
+// Each wave reduces the row's log-sum-exps itself (no barrier); the SG partial
+// sums meet in LDS.
 // ---------------------------------------------------------------------------
 constexpr int kCombineThreads = 256;
 
@@ -546,6 +549,26 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
     const size_t row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int col = tid % C4, sg = tid / C4;
+    // descriptors over the row's max_splits slots (loads past them return zero);
+    // split k is slot k of the row
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<const char *>(a.o_parts + row * a.max_splits * D),
+                                                (uint32_t)a.max_splits * D * 4u);
+    const __amdgpu_buffer_rsrc_t rl =
+        make_rsrc(reinterpret_cast<const char *>(a.lse_parts + row * a.max_splits), (uint32_t)a.max_splits * 4u);
+    auto load_lam = [&](int k) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4u * (uint32_t)k, 0, 0));
+    };
+    // first batch, issued ahead of the split count
+    f32x4_t v[U];
+    float lk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int k = sg + SG * u;
+        v[u] = __builtin_bit_cast(f32x4_t, bload16(ro, (uint32_t)k * (D * 4) + 16u * col, 0));
+        lk[u] = load_lam(k);
+    }
+    float x0 = load_lam(lane);  // the log-sum-exp pass's first 64 splits
+
     int ns, first = 0;
     if (a.seq_lens) {
         const int sl = a.seq_lens[row / a.Hq];
@@ -559,25 +582,10 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
     }
     ns = max(0, min(ns, a.max_splits));
     first = min(first, ns);
-    // from here on, split k means split first + k of the row
-    const float *lam = a.lse_parts + row * a.max_splits + first;
-    ns -= first;
-    // descriptors over the row's ns live partials: loads past them return zero,
-    // so every load is unconditional and all of them can be in flight together
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(
-        reinterpret_cast<const char *>(a.o_parts + (row * a.max_splits + first) * D), (uint32_t)ns * D * 4u);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(reinterpret_cast<const char *>(lam), (uint32_t)ns * 4u);
-    auto load_part = [&](int k, f32x4_t &vk, float &lk) {
-        vk = __builtin_bit_cast(f32x4_t, bload16(ro, (uint32_t)k * (D * 4) + 16u * col, 0));
-        const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4u * k, 0, 0));
-        lk = (k < ns) ? x : -INFINITY;
-    };
-
-    // first batch of partials, in flight while Lambda is reduced
-    f32x4_t v[U];
-    float lk[U];
+    auto live = [&](int k) { return k >= first && k < ns; };
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_part(sg + SG * u, v[u], lk[u]);
+    for (int u = 0; u < U; ++u) lk[u] = live(sg + SG * u) ? lk[u] : -INFINITY;
+
     // Lambda = mx + ln z, z = sum_k exp(lambda_k - mx): every wave reduces the
     // row on its own, one pass with a running (max, sum) per lane, then a
     // butterfly merge of the lanes' pairs by the same rule
@@ -585,11 +593,11 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
     float mx = -INFINITY, z = 0.f;
     for (int p = 0; p < npass; ++p) {
         const int k = lane + 64 * p;
-        const float x = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4u * k, 0, 0));
-        if (k < ns && x > mx) {
+        const float x = p == 0 ? x0 : load_lam(k);
+        if (live(k) && x > mx) {
             z = z * expf(mx - x) + 1.f;
             mx = x;
-        } else if (k < ns && x != -INFINITY) {
+        } else if (live(k) && x != -INFINITY) {
             z += expf(x - mx);
         }
     }
@@ -605,7 +613,8 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (!empty) {
-        // a split with lambda = -inf has weight 0 and contributes nothing
+        // a split with lambda = -inf (dead, or empty) has weight 0 and contributes
+        // nothing; its partial, possibly stale, is never read into the sum
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const float w = expf(lk[u] - Lam);
@@ -613,10 +622,14 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
         }
         for (int k0 = sg + SG * U; k0 < ns; k0 += SG * U) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) load_part(k0 + SG * u, v[u], lk[u]);
+            for (int u = 0; u < U; ++u) {
+                const int k = k0 + SG * u;
+                v[u] = __builtin_bit_cast(f32x4_t, bload16(ro, (uint32_t)k * (D * 4) + 16u * col, 0));
+                lk[u] = load_lam(k);
+            }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const float w = expf(lk[u] - Lam);
+                const float w = expf((live(k0 + SG * u) ? lk[u] : -INFINITY) - Lam);
                 if (w != 0.f) acc += w * v[u];
             }
         }
