@@ -526,6 +526,41 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
 // ---------------------------------------------------------------------------
 constexpr int kCombineThreads = 256;
 
+// Cross-lane moves within a row of 16 lanes (DPP): quad_perm [1,0,3,2] and
+// [2,3,0,1], half-row mirror (lane i <-> 7 - i) and row mirror (i <-> 15 - i).
+// Applied in that order to a commutative reduction, each leaves every lane of a
+// group of 2, 4, 8, then 16 lanes holding the group's result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op)
+{
+    x = op(x, dpp_move<0xB1>(x));
+    x = op(x, dpp_move<0x4E>(x));
+    x = op(x, dpp_move<0x141>(x));
+    x = op(x, dpp_move<0x140>(x));
+    // the four rows' results, read from lanes 0, 16, 32, 48
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
+    return op(op(r0, r1), op(r2, r3));
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+    return wave_reduce(x, [](float u, float v) { return fmaxf(u, v); });
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+    return wave_reduce(x, [](float u, float v) { return u + v; });
+}
+
 struct CombineArgs {
     const float *o_parts, *lse_parts;
     const int32_t *n_splits;  // explicit per-row split counts, or NULL
@@ -586,29 +621,27 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
 #pragma unroll
     for (int u = 0; u < U; ++u) lk[u] = live(sg + SG * u) ? lk[u] : -INFINITY;
 
-    // Lambda = mx + ln z, z = sum_k exp(lambda_k - mx): every wave reduces the
-    // row on its own, one pass with a running (max, sum) per lane, then a
-    // butterfly merge of the lanes' pairs by the same rule
+    // Lambda = mx + ln z, z = sum_k exp(lambda_k - mx), mx the largest live lambda:
+    // every wave reduces the row on its own, a max pass, then one exponential per
+    // lane and pass and a sum (lane reductions in registers, no LDS round trips)
     const int npass = (ns + 63) / 64;
-    float mx = -INFINITY, z = 0.f;
+    float mx = -INFINITY;
     for (int p = 0; p < npass; ++p) {
         const int k = lane + 64 * p;
         const float x = p == 0 ? x0 : load_lam(k);
-        if (live(k) && x > mx) {
-            z = z * expf(mx - x) + 1.f;
-            mx = x;
-        } else if (live(k) && x != -INFINITY) {
-            z += expf(x - mx);
-        }
+        if (live(k)) mx = fmaxf(mx, x);
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float om = __shfl_xor(mx, off), oz = __shfl_xor(z, off);
-        const float nm = fmaxf(mx, om);
-        if (nm != -INFINITY) z = z * expf(mx - nm) + oz * expf(om - nm);
-        mx = nm;
-    }
+    mx = wave_max(mx);
     const bool empty = (mx == -INFINITY);
+    float z = 0.f;
+    if (!empty) {
+        for (int p = 0; p < npass; ++p) {
+            const int k = lane + 64 * p;
+            const float x = p == 0 ? x0 : load_lam(k);
+            if (live(k)) z += expf(x - mx);  // lambda = -inf adds 0
+        }
+        z = wave_sum(z);
+    }
     const float Lam = empty ? -INFINITY : mx + logf(z);
 
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
