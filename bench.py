@@ -148,6 +148,33 @@ def cpu_baseline(x, target_s: float):
                       "N=16384 causal prefill (%.1f GFLOP, %.1f s wall)" % (step, sample_flop(step) / 1e9, dt)}
 
 
+def host_cpu() -> str:
+    """The host's CPU model name, as the kernel reports it (empty if unknown)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
+def cpu_baseline_decode(dx, nbytes: int):
+    """The fp64 oracle, as it stands, on the whole 32k-token decode (one call)."""
+    import oracle
+    q, kc, vc = oracle._f64(dx.q), oracle._f64(dx.k_cache), oracle._f64(dx.v_cache)
+    calls, t0 = 0, time.perf_counter()
+    while calls < 3 or time.perf_counter() - t0 < 2.0:  # repeated to about 2 s of wall time
+        oracle.decode(q, kc, vc, dx.block_table, dx.seq_lens, dx.scale, dx.page_size, dx.max_blocks)
+        calls += 1
+    dt = (time.perf_counter() - t0) / calls
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "fp64 plain-definition oracle on the whole decode (all 28 heads, 32768 cached tokens; "
+                      "the cache converted to float64 beforehand), %d calls, %.1f ms each, bytes counted as "
+                      "the bf16 cache's" % (calls, dt * 1e3)}
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -350,6 +377,9 @@ def main():
         out["fp8_decode"] = fp8_dec
     if do_p and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(px, args.cpu_seconds)
+        out["cpu_baseline"]["host_cpu"] = host_cpu()
+    if do_d and not args.no_cpu_baseline:
+        out["decode"]["cpu_baseline"] = cpu_baseline_decode(dx, decode_bytes)
     print(json.dumps(out), flush=True)
 
 
