@@ -131,9 +131,18 @@ __device__ __forceinline__ long long token_index(const SplitArgs &a, int b, int 
 }
 
 // slot permutation of the V slab rows (see the header comment; D = 256 rows are
-// two bank lines and use the D = 128 permutation)
-template <int D>
-__device__ __forceinline__ int slab_swz(int r) { return D >= 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+// two bank lines and use the D = 128 permutation).  The E4M3 cache stores each
+// loaded 16-byte chunk as two bf16 chunks, one store instruction for the even
+// slots and one for the odd; its permutation also flips the low slot bit on odd
+// bank lines (row r for D = 128, row pair r / 2 for D = 64), so the two rows of
+// bank lines a store pass writes land on disjoint banks.  The flip keeps the
+// permutation's 8-row period, and the transpose reads stay conflict-free.
+template <int D, bool KV8 = false>
+__device__ __forceinline__ int slab_swz(int r)
+{
+    const int base = D >= 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+    return KV8 ? base + (D >= 128 ? (r & 1) : ((r >> 1) & 1)) : base;
+}
 
 template <int D>
 struct Geo {
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
         static_assert(Lg::RPI % 8 == 0, "one permutation period per load instruction");
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-            vstore[e] = (uint32_t)(lo.vtok * Gm::RB + 16 * ((2 * vchunk + e) ^ slab_swz<D>(lo.vtok)));
+            vstore[e] = (uint32_t)(lo.vtok * Gm::RB + 16 * ((2 * vchunk + e) ^ slab_swz<D, true>(lo.vtok)));
     } else {
 #pragma unroll
         for (int par = 0; par < Gm::VP; ++par) {
@@ -401,10 +410,11 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
         }
     }
     // transpose reads: group G, lane 4r+q reads 8 bytes of slab row 4G+r, dims
-    // 16nb + 4q..4q+3; the slot permutation only touches bits 5+ of the offset,
-    // so d-block nb is a XOR by 32nb
+    // 16nb + 4q..4q+3, i.e. chunk 2nb + (q >> 1); the permutation's bits above its
+    // lowest move whole 32-byte chunk pairs and its lowest bit (E4M3 cache) only
+    // swaps the two chunks of a pair, so d-block nb is a XOR by 32nb
     const int vrow = 4 * G + (l16 >> 2), vq = l16 & 3;
-    const uint32_t vread = (uint32_t)(vrow * Gm::RB + 16 * ((vq >> 1) ^ slab_swz<D>(vrow)) + 8 * (vq & 1));
+    const uint32_t vread = (uint32_t)(vrow * Gm::RB + 16 * ((vq >> 1) ^ slab_swz<D, KV8>(vrow)) + 8 * (vq & 1));
 
     const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)hk * Lg::RB;
     const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)hk * Lg::RB;
