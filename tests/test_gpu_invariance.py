@@ -124,3 +124,26 @@ def test_decode_row_matches_prefill_row(attn):
                         torch.tensor([i + 1], dtype=torch.int32), 16, 1008 // 16, x.scale, 256)
         assert (o.float() - po[:, :, i].float()).abs().max().item() <= BF16_TOL["o"]
         assert (lse - pl[:, :, i]).abs().max().item() <= BF16_TOL["lse"]
+
+
+def test_launches_follow_the_callers_stream(attn):
+    """Prefill and decode launched on a side stream (default priority) that first
+    waits for the inputs: the same results as on the current stream, bit for bit,
+    once that stream is synchronised."""
+    say("case: calls on a side stream")
+    x = W.prefill_inputs(71, 1, 8, 2, 700, 128, W.BF16)
+    y = W.decode_paged_inputs(72, 3, 8, 2, 128, 16, 1, 900, lengths=[900, 17, 512])
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    args = (dev(y.q), dev(y.k_cache), dev(y.v_cache), dev(y.block_table), dev(y.seq_lens), y.page_size,
+            y.max_blocks, y.scale, 64)
+    o0, l0 = attn.prefill(q, k, v, True, x.scale)
+    d0, m0 = attn.decode(*args)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o1, l1 = attn.prefill(q, k, v, True, x.scale, stream=side)
+        d1, m1 = attn.decode(*args, stream=side)
+    side.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert torch.equal(d0, d1) and torch.equal(m0, m1)
