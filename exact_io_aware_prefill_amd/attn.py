@@ -30,10 +30,9 @@ ATTN_ERR_HIP = -7
 ATTN_F32 = 0
 ATTN_BF16 = 1
 
-EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_ext", "attn_prefill_fp8", "attn_decode",
-           "attn_decode_append",
-           "attn_decode_ext", "attn_decode_fp8", "attn_decode_chunk_tokens", "attn_decode_workspace_bytes", "attn_lse_combine",
-           "attn_status_string")
+EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_ext", "attn_prefill_fp8", "attn_prefill_fp8_varlen",
+           "attn_decode", "attn_decode_append", "attn_decode_ext", "attn_decode_fp8", "attn_decode_chunk_tokens",
+           "attn_decode_workspace_bytes", "attn_lse_combine", "attn_status_string")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -46,6 +45,9 @@ lib.attn_prefill_ext.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
 lib.attn_prefill_ext.restype = _I
 lib.attn_prefill_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _P]
 lib.attn_prefill_fp8.restype = _I
+lib.attn_prefill_fp8_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                        ctypes.c_float, _P]
+lib.attn_prefill_fp8_varlen.restype = _I
 lib.attn_decode_ext.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                                 ctypes.c_float, _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode_ext.restype = _I
@@ -148,6 +150,18 @@ def attn_prefill_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal
                               _ptr(descale_v), B, N, Hq, k8.shape[1], d, int(bool(causal)), float(scale),
                               _stream(stream))
     _check(rc, "attn_prefill_fp8")
+
+
+def attn_prefill_fp8_varlen(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen: int,
+                            causal: bool, scale: float, stream=None) -> None:
+    """Packed batch: q8 [T, Hq, d], k8, v8 [T, Hkv, d] E4M3 codes; o [T, Hq, d] bf16; lse [Hq, T]
+    float32; descale_* [B, Hkv] float32 or None; cu_seqlens [B+1] int32 on the GPU."""
+    T, Hq, d = q8.shape
+    B = cu_seqlens.numel() - 1
+    rc = lib.attn_prefill_fp8_varlen(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), _ptr(descale_q),
+                                     _ptr(descale_k), _ptr(descale_v), _ptr(cu_seqlens), B, int(max_seqlen), T, Hq,
+                                     k8.shape[1], d, int(bool(causal)), float(scale), _stream(stream))
+    _check(rc, "attn_prefill_fp8_varlen")
 
 
 def attn_decode_chunk_tokens(batch: int, n_kv_heads: int, page_size: int, max_blocks_per_seq: int,
@@ -288,6 +302,16 @@ def prefill_fp8(q8, k8, v8, descale_q=None, descale_k=None, descale_v=None, caus
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
     attn_prefill_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, d ** -0.5 if scale is None else scale,
                      stream)
+    return o, lse
+
+
+def prefill_fp8_varlen(q8, k8, v8, cu_seqlens, max_seqlen: int, descale_q=None, descale_k=None, descale_v=None,
+                       causal: bool = True, scale: float | None = None, stream=None):
+    T, Hq, d = q8.shape
+    o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=q8.device)
+    attn_prefill_fp8_varlen(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen, causal,
+                            d ** -0.5 if scale is None else scale, stream)
     return o, lse
 
 

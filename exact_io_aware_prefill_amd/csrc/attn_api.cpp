@@ -205,33 +205,65 @@ int attn_prefill_ext(const void *q, const void *k, const void *v, void *o, float
                         stream);
 }
 
-int attn_prefill_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
-                     const float *descale_q_or_null, const float *descale_k_or_null,
-                     const float *descale_v_or_null, int batch, int seqlen, int n_q_heads, int n_kv_heads,
-                     int head_dim, int causal, float scale, void *stream)
+namespace {
+
+// Shared body of the FP8 prefill entry points: padded layout (seqlen = N) or,
+// with `packed`, the packed layout described by cu_seqlens (seqlen = the
+// longest sequence).
+int prefill_fp8_impl(bool packed, const void *q, const void *k, const void *v, void *o, float *lse,
+                     const float *descale_q, const float *descale_k, const float *descale_v,
+                     const int32_t *cu_seqlens, int batch, int seqlen, int total_tokens, int n_q_heads,
+                     int n_kv_heads, int head_dim, int causal, float scale, void *stream)
 {
-    if (batch < 0 || seqlen < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0) return ATTN_ERR_SHAPE;
+    if (batch < 0 || seqlen < 0 || (packed && total_tokens < 0) || n_q_heads <= 0 || n_kv_heads <= 0 ||
+        head_dim <= 0)
+        return ATTN_ERR_SHAPE;
     if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
     if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
-    if (batch == 0 || seqlen == 0) return ATTN_OK;
-    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
+    if (batch == 0 || seqlen == 0 || (packed && total_tokens == 0)) return ATTN_OK;
+    if (!q || !k || !v || !o || !lse || (packed && !cu_seqlens)) return ATTN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||
-        (reinterpret_cast<uintptr_t>(descale_q_or_null) & 3u) != 0 ||
-        (reinterpret_cast<uintptr_t>(descale_k_or_null) & 3u) != 0 ||
-        (reinterpret_cast<uintptr_t>(descale_v_or_null) & 3u) != 0)
+        (reinterpret_cast<uintptr_t>(descale_q) & 3u) != 0 || (reinterpret_cast<uintptr_t>(descale_k) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(descale_v) & 3u) != 0 || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0)
         return ATTN_ERR_ALIGN;
-    // one head's rows (seqlen rounded up to a 128-row tile) are addressed with 32-bit offsets
+    // one head's rows of one sequence (seqlen rounded up to a 128-row tile) are
+    // addressed with 32-bit offsets; a packed row holds every head
+    const long long row_bytes = packed ? (long long)n_q_heads * head_dim : head_dim;
     if ((long long)batch * n_q_heads * ((seqlen + 127) / 128) > INT_MAX ||
-        ((long long)seqlen + 127) * head_dim > 0xffffffffLL)
+        ((long long)seqlen + 127) * row_bytes > 0xffffffffLL)
         return ATTN_ERR_UNSUPPORTED;
     attn::PrefillFp8Params p;
     p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
-    p.descale_q = descale_q_or_null; p.descale_k = descale_k_or_null; p.descale_v = descale_v_or_null;
+    p.descale_q = descale_q; p.descale_k = descale_k; p.descale_v = descale_v;
+    p.cu_seqlens = packed ? cu_seqlens : nullptr;
+    p.total = packed ? total_tokens : 0;
     p.B = batch; p.N = seqlen; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
     p.causal = causal ? 1 : 0;
     p.scale = scale;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return run([&] { return attn::launch_prefill_fp8(p, s); });
+}
+
+}  // namespace
+
+int attn_prefill_fp8(const void *q, const void *k, const void *v, void *o, float *lse,
+                     const float *descale_q_or_null, const float *descale_k_or_null,
+                     const float *descale_v_or_null, int batch, int seqlen, int n_q_heads, int n_kv_heads,
+                     int head_dim, int causal, float scale, void *stream)
+{
+    return prefill_fp8_impl(false, q, k, v, o, lse, descale_q_or_null, descale_k_or_null, descale_v_or_null,
+                            nullptr, batch, seqlen, 0, n_q_heads, n_kv_heads, head_dim, causal, scale, stream);
+}
+
+int attn_prefill_fp8_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                            const float *descale_q_or_null, const float *descale_k_or_null,
+                            const float *descale_v_or_null, const int32_t *cu_seqlens, int batch,
+                            int max_seqlen, int total_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+                            int causal, float scale, void *stream)
+{
+    return prefill_fp8_impl(true, q, k, v, o, lse, descale_q_or_null, descale_k_or_null, descale_v_or_null,
+                            cu_seqlens, batch, max_seqlen, total_tokens, n_q_heads, n_kv_heads, head_dim, causal,
+                            scale, stream);
 }
 
 int attn_decode_chunk_tokens(int batch, int n_kv_heads, int page_size, int max_blocks_per_seq,

@@ -32,10 +32,12 @@ hipError_t launch_prefill_f32(const PrefillParams &p, hipStream_t stream);
 
 // Tiled prefill on FP8 (E4M3) inputs, bf16 output (prefill_fp8.hip).
 struct PrefillFp8Params {
-    const void *q, *k, *v;  // [B, Hq | Hkv, N, head_dim] E4M3 codes
-    void *o;                // [B, Hq, N, head_dim] bf16
-    float *lse;             // [B, Hq, N]
+    const void *q, *k, *v;  // E4M3 codes: [B, Hq | Hkv, N, head_dim], or packed [T, Hq | Hkv, head_dim]
+    void *o;                // bf16, q's layout
+    float *lse;             // [B, Hq, N], or packed [Hq, T]
     const float *descale_q, *descale_k, *descale_v;  // [B, Hkv] or NULL (1)
+    const int32_t *cu_seqlens;  // packed layout (N = the longest sequence), or NULL
+    int total;                  // packed: T
     int B, N, Hq, Hkv, head_dim, causal;
     float scale;
 };

@@ -68,12 +68,21 @@ constexpr float kMaxLaneSum = 256.f;      // a lane's tile sum above this redoes
 constexpr uint32_t kBufferFlags = 0x00020000u;
 constexpr int kUnitScale = 127;           // E8M0 block scale 2^0
 
+// Two layouts, as in the bf16 kernel.  Padded: q, o [B, Hq, N, D], k, v
+// [B, Hkv, N, D], lse [B, Hq, N] (cu_seqlens NULL).  Packed: sequence b owns
+// tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 of q, o [T, Hq, D], k, v [T, Hkv, D]
+// and lse [Hq, T].  Strides are in elements (bytes of the codes, bf16 of o).
 struct Args {
-    const uint8_t *q, *k, *v;  // [B, Hq | Hkv, N, D] E4M3 codes
-    uint16_t *o;               // [B, Hq, N, D] bf16
-    float *lse;                // [B, Hq, N]
+    const uint8_t *q, *k, *v;  // E4M3 codes
+    uint16_t *o;               // bf16
+    float *lse;
     const float *dq, *dk, *dv; // [B, Hkv] descales, or NULL (1)
+    const int32_t *cu_seqlens; // packed layout, or NULL
     int B, N, Hq, Hkv, group, causal, n_qtiles;
+    int T;                     // packed: total tokens
+    long long q_head, q_row;   // strides of q and o
+    long long kv_head, kv_row; // strides of k and v
+    long long lse_head;        // stride of lse between heads (rows are adjacent)
     float scale;
 };
 
@@ -102,24 +111,27 @@ struct TileLoader {
     static constexpr int PER_WAVE = INSTR / kWaves;
     static_assert(INSTR % kWaves == 0, "tile instructions split evenly over the waves");
     static_assert(RPI * kWaves == 32 || PER_WAVE == 1, "a lane's rows are 32 apart");
-    uint32_t voff;
+    uint32_t voff;  // per-lane byte offset from the first row an instruction fills
+    uint32_t rowb;  // bytes between consecutive key rows in memory
 
     template <typename Swz>
-    __device__ __forceinline__ void init(int wave, int lane, Swz swz)
+    __device__ __forceinline__ void init(int wave, int lane, uint32_t row_bytes, Swz swz)
     {
         const int u = wave * 64 + lane;
         const int r = u / NC, pos = u % NC;
-        voff = (uint32_t)(lane / NC) * D + 16u * (uint32_t)(pos ^ swz(r));
+        rowb = row_bytes;
+        voff = (uint32_t)(lane / NC) * row_bytes + 16u * (uint32_t)(pos ^ swz(r));
     }
     // rows past n read as zero: each instruction's descriptor ends at row n
+    // ((n - row0) * rowb < 2^32: the launcher bounds a head's padded rows)
     __device__ __forceinline__ void load(const uint8_t *head, int n, int k0, int wave, uint8_t *dst) const
     {
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int ins = wave + i * kWaves;
             const int row0 = k0 + ins * RPI;
-            const uint32_t rec = __builtin_amdgcn_readfirstlane((uint32_t)max(n - row0, 0) * (uint32_t)D);
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (long long)row0 * D, rec);
+            const uint32_t rec = __builtin_amdgcn_readfirstlane((uint32_t)max(n - row0, 0) * rowb);
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(head + (long long)row0 * rowb, rec);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)(dst + ins * 1024), 16, voff, 0, 0, 0);
         }
     }
@@ -198,7 +210,9 @@ __device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[2], float sl2,
     return rs0 + rs1;
 }
 
-template <int D>
+// PACKED selects the packed layout (a separate instantiation, so the padded one
+// keeps its row strides as compile-time constants).
+template <int D, bool PACKED>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
 {
     constexpr int NT = kWaves * 64;
@@ -222,7 +236,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     const int h = hk * a.group + j;
     const int qtile = (r & 1) ? (r >> 1) : a.n_qtiles - 1 - (r >> 1);
     const int q0 = qtile * kBM;
-    const int N = a.N;
+    // this sequence's first token and length
+    long long tok0;
+    int N;
+    if (PACKED) {
+        // offsets outside [0, T] or a length above the launch's maximum are
+        // clamped, so nothing outside the packed tensors is touched
+        const int s0 = min(max(a.cu_seqlens[b], 0), a.T);
+        const int s1 = min(max(a.cu_seqlens[b + 1], s0), a.T);
+        tok0 = s0;
+        N = min(s1 - s0, a.N);
+    } else {
+        tok0 = (long long)b * a.N;
+        N = a.N;
+    }
+    if (q0 >= N) return;  // whole workgroup: no query row of this tile exists
 
     // effective scale of the raw 8-bit dot products, and the output factor
     const float dq = a.dq ? a.dq[b * a.Hkv + hk] : 1.f;
@@ -233,8 +261,12 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     const float aeff = fmaxf(fabsf(eff), 1e-30f);
     const float sl2 = aeff * kLog2e;
 
-    const long long qo = ((long long)b * a.Hq + h) * N * D;
-    const long long kvo = ((long long)b * a.Hkv + hk) * N * D;
+    // element offsets of this (sequence, head): packed rows are token-major
+    const long long qo = PACKED ? tok0 * a.Hq * D + (long long)h * a.q_head : ((long long)b * a.Hq + h) * a.q_head;
+    const long long kvo = PACKED ? tok0 * a.Hkv * D + (long long)hk * a.kv_head : ((long long)b * a.Hkv + hk) * a.kv_head;
+    const long long lse_off = PACKED ? (long long)h * a.lse_head + tok0 : ((long long)b * a.Hq + h) * a.lse_head;
+    const long long q_row = PACKED ? a.q_row : D;        // elements between query rows
+    const uint32_t kv_rowb = PACKED ? (uint32_t)a.kv_row : D;  // bytes between key rows
     const uint8_t *const kh = a.k + kvo;
     const uint8_t *const vh = a.v + kvo;
     const int wrow0 = q0 + wave * 32;
@@ -242,8 +274,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     // Q fragments: lane (query l32, half hh) holds dims 64 ds + 32 hh .. + 31
     i32x8_t qf[D / 64];
     {
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qo, (uint32_t)N * D);
-        const uint32_t qrow_off = (uint32_t)(wrow0 + l32) * D + 32u * hh;
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + qo, (uint32_t)min((long long)N * q_row, 0xFFFFFFFFLL));
+        const uint32_t qrow_off = (uint32_t)((long long)(wrow0 + l32) * q_row) + 32u * hh;
         const int flip = negate ? (int)0x80808080u : 0;
 #pragma unroll
         for (int ds = 0; ds < D / 64; ++ds) {
@@ -268,8 +300,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     const int xlane = (lane ^ 32) << 2;
 
     TileLoader<D> kld, vld;
-    kld.init(wave, lane, [](int rr) { return k_swz<D>(rr); });
-    vld.init(wave, lane, [](int rr) { return v_swz<D>(rr); });
+    kld.init(wave, lane, kv_rowb, [](int rr) { return k_swz<D>(rr); });
+    vld.init(wave, lane, kv_rowb, [](int rr) { return v_swz<D>(rr); });
     const uint32_t kad0 = (uint32_t)(l32 * D + 16 * ((2 * hh) ^ k_swz<D>(l32)));
     const uint32_t kad1 = (uint32_t)(l32 * D + 16 * ((2 * hh + 1) ^ k_swz<D>(l32)));
     uint32_t vad;
@@ -365,7 +397,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     const float lt = l + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, l)));
     if (qrow < N) {
         const float f = dv / lt;
-        uint16_t *orow = a.o + qo + (long long)qrow * D;
+        uint16_t *orow = a.o + qo + (long long)qrow * q_row;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -379,7 +411,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
                 pk.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
                 *reinterpret_cast<uint2 *>(orow + d0) = pk;
             }
-        if (hh == 0) a.lse[((long long)b * a.Hq + h) * N + qrow] = m * aeff + log2f(lt) * kLn2;
+        if (hh == 0) a.lse[lse_off + qrow] = m * aeff + log2f(lt) * kLn2;
     }
 }
 
@@ -399,17 +431,34 @@ hipError_t launch_prefill_fp8(const PrefillFp8Params &p, hipStream_t stream)
     a.B = p.B; a.N = p.N; a.Hq = p.Hq; a.Hkv = p.Hkv; a.group = p.Hq / p.Hkv;
     a.causal = p.causal;
     a.scale = p.scale;
+    a.cu_seqlens = p.cu_seqlens;
+    a.T = p.total;
+    const long long D = p.head_dim;
+    if (p.cu_seqlens) {  // packed [T, H, D]
+        a.q_head = D; a.q_row = (long long)p.Hq * D;
+        a.kv_head = D; a.kv_row = (long long)p.Hkv * D;
+        a.lse_head = p.total;
+    } else {  // padded [B, H, N, D]
+        a.q_head = (long long)p.N * D; a.q_row = D;
+        a.kv_head = (long long)p.N * D; a.kv_row = D;
+        a.lse_head = p.N;
+    }
     a.n_qtiles = (p.N + kBM - 1) / kBM;
     const long long items = (long long)a.n_qtiles * p.B * p.Hq;
     if (items == 0) return hipSuccess;
     if (items > 0x7fffffffLL) return hipErrorInvalidValue;
-    // one head's rows, including the padded last query tile, are addressed with 32-bit offsets
-    if ((long long)a.n_qtiles * kBM * p.head_dim > 0xffffffffLL) return hipErrorInvalidValue;
+    // one head's rows of one sequence, including the padded last query tile, are
+    // addressed with 32-bit offsets (q rows are the widest)
+    if ((long long)a.n_qtiles * kBM * a.q_row > 0xffffffffLL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)items), block(kWaves * 64);
-    if (p.head_dim == 128)
-        hipLaunchKernelGGL(prefill_fp8_kernel<128>, grid, block, 0, stream, a);
+    if (p.head_dim == 128 && p.cu_seqlens)
+        hipLaunchKernelGGL((prefill_fp8_kernel<128, true>), grid, block, 0, stream, a);
+    else if (p.head_dim == 128)
+        hipLaunchKernelGGL((prefill_fp8_kernel<128, false>), grid, block, 0, stream, a);
+    else if (p.cu_seqlens)
+        hipLaunchKernelGGL((prefill_fp8_kernel<64, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL(prefill_fp8_kernel<64>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((prefill_fp8_kernel<64, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

@@ -129,6 +129,48 @@ def prefill_fp8_inputs(seed: int, B: int, Hq: int, Hkv: int, N: int, d: int, cau
                             dv.float(), causal, 1.0 / math.sqrt(d) if scale is None else scale)
 
 
+@dataclass
+class Fp8PackedPrefillInputs:
+    q8: torch.Tensor  # [T, Hq, d] E4M3 codes
+    k8: torch.Tensor  # [T, Hkv, d]
+    v8: torch.Tensor
+    descale_q: torch.Tensor  # [B, Hkv] float32
+    descale_k: torch.Tensor
+    descale_v: torch.Tensor
+    cu_seqlens: torch.Tensor  # [B + 1] int32
+    max_seqlen: int
+    causal: bool
+    scale: float
+
+
+def prefill_fp8_packed_inputs(seed: int, lens, Hq: int, Hkv: int, d: int, causal: bool = True,
+                              scale: Optional[float] = None) -> Fp8PackedPrefillInputs:
+    """The float32 draws of prefill_packed_inputs, quantised to E4M3 with one descale
+    per (sequence, KV head): the largest magnitude of the sequence's rows of that KV
+    head (and, for Q, of its query heads) maps to 448."""
+    x = prefill_packed_inputs(seed, lens, Hq, Hkv, d, F32, causal, scale)
+    lens = [int(n) for n in lens]
+    B, g = len(lens), Hq // Hkv
+    cu = x.cu_seqlens.tolist()
+    dq, dk, dv = torch.ones(B, Hkv), torch.ones(B, Hkv), torch.ones(B, Hkv)
+    q8 = torch.zeros(x.q.shape, dtype=torch.float8_e4m3fn)
+    k8 = torch.zeros(x.k.shape, dtype=torch.float8_e4m3fn)
+    v8 = torch.zeros(x.v.shape, dtype=torch.float8_e4m3fn)
+    for b in range(B):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 <= s0:
+            continue
+        qs = x.q[s0:s1].reshape(s1 - s0, Hkv, g, d)  # the query heads of one KV head are adjacent
+        dq[b] = torch.clamp(qs.abs().amax(dim=(0, 2, 3)), min=1e-12) / 448.0
+        dk[b] = torch.clamp(x.k[s0:s1].abs().amax(dim=(0, 2)), min=1e-12) / 448.0
+        dv[b] = torch.clamp(x.v[s0:s1].abs().amax(dim=(0, 2)), min=1e-12) / 448.0
+        q8[s0:s1] = (qs / dq[b][None, :, None, None]).reshape(s1 - s0, Hq, d).to(torch.float8_e4m3fn)
+        k8[s0:s1] = (x.k[s0:s1] / dk[b][None, :, None]).to(torch.float8_e4m3fn)
+        v8[s0:s1] = (x.v[s0:s1] / dv[b][None, :, None]).to(torch.float8_e4m3fn)
+    return Fp8PackedPrefillInputs(q8, k8, v8, dq.float(), dk.float(), dv.float(), x.cu_seqlens, x.max_seqlen,
+                                  causal, x.scale)
+
+
 def worked_example_inputs(d: int = 64) -> PrefillInputs:
     """The pofe.ai worked example (section "A worked example by hand": scores
     (2, 1, 4, 3), scalar values (1, 0, 2, -1)) embedded in a 4-token causal

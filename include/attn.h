@@ -26,6 +26,7 @@
  *   - attn_prefill_fp8: the prefill on 8-bit (E4M3) inputs with descale
  *     factors, the FP8 direction the page names for FlashAttention-3 (section
  *     "The bottleneck it attacks");
+ *   - attn_prefill_fp8_varlen: the FP8 prefill over a packed batch;
  *   - attn_decode_fp8: the decode over an FP8 (E4M3) KV cache;
  *   - attn_lse_combine: that reduction on its own -- the combine rule for
  *     independent partials, a softmax over the partials' log-sum-exps
@@ -56,7 +57,8 @@
  *     n_kv_heads) (consecutive query heads share a KV head).
  *   - Head sizes 64, 128 and 256 (256 being the largest the page's section
  *     "Interaction with post-trained models" names) on every entry point except
- *     attn_prefill_fp8 and attn_decode_fp8 (64 and 128).
+ *     the FP8 ones (attn_prefill_fp8, attn_prefill_fp8_varlen, attn_decode_fp8:
+ *     64 and 128).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -174,6 +176,32 @@ int attn_prefill_fp8(const void *q, const void *k, const void *v, void *o, float
                      const float *descale_q_or_null, const float *descale_k_or_null,
                      const float *descale_v_or_null, int batch, int seqlen, int n_q_heads, int n_kv_heads,
                      int head_dim, int causal, float scale, void *stream);
+
+/*
+ * attn_prefill_fp8_varlen -- attn_prefill_fp8 over a packed batch of sequences
+ * (the layout of attn_prefill_varlen).  The pofe.ai page's section
+ * "Interaction with post-trained models" discusses both FP8 attention and the
+ * variable-length interface engines use to batch prompts without padding.
+ * Sequence b owns tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 and attends only
+ * to itself.
+ *
+ *   q     [total_tokens, n_q_heads,  head_dim]  E4M3 codes
+ *   k, v  [total_tokens, n_kv_heads, head_dim]  E4M3 codes
+ *   o     [total_tokens, n_q_heads,  head_dim]  bfloat16 (written)
+ *   lse   [n_q_heads, total_tokens] float32 (written)
+ *   descale_q/k/v_or_null [batch, n_kv_heads] float32, one factor per (sequence,
+ *         KV head); NULL means 1.
+ *   cu_seqlens, max_seqlen: as attn_prefill_varlen (offsets outside
+ *         [0, total_tokens] or lengths above max_seqlen are clamped).
+ *   head_dim in {64, 128}; arithmetic as attn_prefill_fp8.
+ *   (max_seqlen + 127) * n_q_heads * head_dim >= 2^32 is ATTN_ERR_UNSUPPORTED;
+ *   batch, max_seqlen or total_tokens of 0 does nothing.
+ */
+int attn_prefill_fp8_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
+                            const float *descale_q_or_null, const float *descale_k_or_null,
+                            const float *descale_v_or_null, const int32_t *cu_seqlens, int batch,
+                            int max_seqlen, int total_tokens, int n_q_heads, int n_kv_heads, int head_dim,
+                            int causal, float scale, void *stream);
 
 /*
  * attn_decode -- one new query token per sequence against a KV cache, by

@@ -302,6 +302,29 @@ def prefill_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale
     return prefill(q, k, v, causal, scale, row_step=row_step)
 
 
+def prefill_fp8_varlen(q8, k8, v8, descale_q, descale_k, descale_v, cu_seqlens, causal: bool, scale: float):
+    """FP8 inputs in the packed layout: q8 [T, Hq, d], k8, v8 [T, Hkv, d] E4M3 codes;
+    sequence b (tokens cu_seqlens[b] .. cu_seqlens[b+1]-1) reads its own descales
+    descale_*[b, hk] (None = 1) for KV head hk and the query heads that share it.
+    The dequantised packed tensors then go through prefill_varlen above.  Returns
+    (o [T, Hq, d], lse [Hq, T]) in float64."""
+    q, k, v = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
+    cu = _i32(cu_seqlens)
+    B = cu.shape[0] - 1
+    Hq, Hkv = q.shape[1], k.shape[1]
+    g = Hq // Hkv
+
+    def ds(x):
+        return np.ones((B, Hkv)) if x is None else _f64(x).reshape(B, Hkv)
+    dq, dk, dv = ds(descale_q), ds(descale_k), ds(descale_v)
+    for b in range(B):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        q[s0:s1] *= np.repeat(dq[b], g)[None, :, None]
+        k[s0:s1] *= dk[b][None, :, None]
+        v[s0:s1] *= dv[b][None, :, None]
+    return prefill_varlen(q, k, v, cu, causal, scale)
+
+
 def decode_fp8(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, scale: float,
                page_size: int, max_blocks: int):
     """Decode over an E4M3 cache: sequence b reads descale_k[b, hk] * decode(k8) and

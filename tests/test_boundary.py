@@ -156,6 +156,30 @@ def test_prefill_fp8_argument_errors(kw, code):
     assert prefill_fp8(**kw) == code
 
 
+def prefill_fp8_varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dq=0, dk=0, dv=0, cu=FAKE, B=2, N=16, T=20, Hq=4,
+                       Hkv=2, d=128, causal=1):
+    return attn.lib.attn_prefill_fp8_varlen(P(q), P(k), P(v), P(o), P(lse), P(dq), P(dk), P(dv), P(cu), B, N, T, Hq,
+                                            Hkv, d, causal, 0.1, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu=0), attn.ATTN_ERR_NULL),
+    (dict(q=0), attn.ATTN_ERR_NULL),
+    (dict(cu=FAKE + 2), attn.ATTN_ERR_ALIGN),      # cu_seqlens is int32: 4-byte aligned
+    (dict(cu=FAKE + 4, q=0), attn.ATTN_ERR_NULL),  # 4-byte aligned offsets are fine; NULL q is not
+    (dict(v=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(T=-1), attn.ATTN_ERR_SHAPE),
+    (dict(B=-1), attn.ATTN_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
+    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(N=1 << 24, Hq=32), attn.ATTN_ERR_UNSUPPORTED),  # a packed row holds all heads: 32-bit offsets
+    (dict(T=0, q=0, k=0, v=0, o=0, lse=0, cu=0), attn.ATTN_OK),
+    (dict(N=0, q=0, k=0, v=0, o=0, lse=0, cu=0), attn.ATTN_OK),
+])
+def test_prefill_fp8_varlen_argument_errors(kw, code):
+    assert prefill_fp8_varlen(**kw) == code
+
+
 def decode(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, d=128, P_=16,
            maxb=8, dtype=1, chunk=0, ws=FAKE, wsb=1 << 30):
     return attn.lib.attn_decode(P(q), P(kc), P(vc), P(bt), P(sl), P(o), P(lse), B, Hq, Hkv, d, P_,

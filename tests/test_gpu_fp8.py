@@ -198,3 +198,63 @@ def test_fp8_cache_decode_matches_bf16_decode_of_the_same_values(attn):
                                x.page_size, x.max_blocks)
     assert np.max(np.abs(l8.cpu().numpy() - rl)) <= 1e-3
     assert np.max(np.abs(o8.float().cpu().numpy() - ro)) <= o_tol
+
+
+# ------------------------------------------------------------------ packed (variable-length) FP8 prefill
+def packed_row_bounds(x):
+    """row_bounds for each sequence of a packed batch, assembled as [T, Hq]."""
+    cu = x.cu_seqlens.tolist()
+    Hq = x.q8.shape[1]
+    out = np.zeros((x.q8.shape[0], Hq))
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 == s0:
+            continue
+        seq = W.Fp8PrefillInputs(x.q8[s0:s1].permute(1, 0, 2)[None], x.k8[s0:s1].permute(1, 0, 2)[None],
+                                 x.v8[s0:s1].permute(1, 0, 2)[None], x.descale_q[b:b + 1], x.descale_k[b:b + 1],
+                                 x.descale_v[b:b + 1], x.causal, x.scale)
+        out[s0:s1] = row_bounds(seq)[0].T
+    return out
+
+
+def run_packed(attn, x):
+    o, lse = attn.prefill_fp8_varlen(dev(x.q8), dev(x.k8), dev(x.v8), dev(x.cu_seqlens), x.max_seqlen,
+                                     dev(x.descale_q), dev(x.descale_k), dev(x.descale_v), x.causal, x.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_prefill_varlen_ragged(attn, d, causal):
+    lens = [1, 7, 0, 128, 129, 300, 64]
+    say("case: fp8 varlen d=%d causal=%s lens=%s" % (d, causal, lens))
+    x = W.prefill_fp8_packed_inputs(3500 + d, lens, 8, 2, d, causal=causal)
+    o, lse = run_packed(attn, x)
+    ro, rl = oracle.prefill_fp8_varlen(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, x.cu_seqlens,
+                                       causal, x.scale)
+    check_fp8("fp8 varlen d=%d causal=%d" % (d, causal), o, lse, ro, rl, packed_row_bounds(x))
+
+
+def test_fp8_prefill_varlen_long_mix(attn):
+    """Four prompts of 3000, 1, 2048 and 777 tokens, 8 query / 2 KV heads, d = 128."""
+    lens = [3000, 1, 2048, 777]
+    say("case: fp8 varlen long mix %s" % lens)
+    x = W.prefill_fp8_packed_inputs(3600, lens, 8, 2, 128)
+    o, lse = run_packed(attn, x)
+    ro, rl = oracle.prefill_fp8_varlen(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, x.cu_seqlens,
+                                       True, x.scale)
+    check_fp8("fp8 varlen long mix", o, lse, ro, rl, packed_row_bounds(x))
+
+
+def test_fp8_prefill_varlen_one_sequence_equals_padded(attn):
+    """One packed sequence runs the padded kernel's arithmetic: bit for bit equal."""
+    say("case: fp8 varlen one sequence = padded")
+    N = 333
+    x = W.prefill_fp8_packed_inputs(3700, [N], 8, 2, 128)
+    o, lse = run_packed(attn, x)
+    op, lp = attn.prefill_fp8(dev(x.q8.permute(1, 0, 2)[None]), dev(x.k8.permute(1, 0, 2)[None]),
+                              dev(x.v8.permute(1, 0, 2)[None]), dev(x.descale_q), dev(x.descale_k),
+                              dev(x.descale_v), True, x.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, op[0].permute(1, 0, 2)) and torch.equal(lse, lp[0])

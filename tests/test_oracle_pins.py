@@ -21,6 +21,7 @@ import torch
 import torch.nn.functional as F
 
 import oracle
+from exact_io_aware_prefill_amd import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")
 E = math.e
@@ -692,6 +693,45 @@ def test_fp8_prefill_descale_invariants():
     # the changed group equals the same call with the scale doubled for that sequence
     o5, lse5 = oracle.prefill_fp8(q8[1:], k8[1:], v8[1:], dq[1:], dk[1:], dv[1:], True, 0.5)
     assert np.max(np.abs(o5[0, 0:g] - o4[1, 0:g])) < 1e-12
+
+
+def test_fp8_varlen_oracle_is_the_padded_fp8_oracle_per_sequence():
+    """The packed FP8 oracle against the (pinned) padded one on each sequence alone
+    with that sequence's descale row; an empty sequence owns no rows; another
+    sequence's codes do not reach a sequence; descale_v[b] scales sequence b's
+    output only, and descale_q * descale_k is all the scores see."""
+    lens = [5, 0, 70, 33]
+    x = W.prefill_fp8_packed_inputs(41, lens, 6, 2, 64, scale=0.3)
+    args = (x.descale_q, x.descale_k, x.descale_v, x.cu_seqlens, True, x.scale)
+    o, lse = oracle.prefill_fp8_varlen(x.q8, x.k8, x.v8, *args)
+    cu = x.cu_seqlens.tolist()
+    for b in range(len(lens)):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 == s0:
+            continue
+        sl = lambda t: t[s0:s1].permute(1, 0, 2)[None]  # noqa: E731
+        ro, rl = oracle.prefill_fp8(sl(x.q8), sl(x.k8), sl(x.v8), x.descale_q[b:b + 1], x.descale_k[b:b + 1],
+                                    x.descale_v[b:b + 1], True, x.scale)
+        assert np.abs(ro[0].transpose(1, 0, 2) - o[s0:s1]).max() <= 1e-12
+        assert np.abs(rl[0] - lse[:, s0:s1]).max() <= 1e-12
+    assert not np.isnan(o).any() and not np.isnan(lse).any()  # the empty sequence leaves no row unwritten
+    # isolation: new codes for sequence 0 leave sequences 2 and 3 unchanged
+    q2 = x.q8.clone()
+    q2[:5] = torch.flip(q2[:5], dims=[0])
+    k2 = x.k8.clone()
+    k2[:5] = torch.flip(k2[:5], dims=[0])
+    o2, l2 = oracle.prefill_fp8_varlen(q2, k2, x.v8, *args)
+    assert np.array_equal(o2[5:], o[5:]) and np.array_equal(l2[:, 5:], lse[:, 5:])
+    # descale_v[2] x 2: sequence 2's output doubles, the rest is unchanged
+    dv = x.descale_v.clone()
+    dv[2] *= 2
+    o3, l3 = oracle.prefill_fp8_varlen(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, dv, x.cu_seqlens, True, x.scale)
+    assert np.abs(o3[5:75] - 2 * o[5:75]).max() <= 1e-12
+    assert np.array_equal(o3[75:], o[75:]) and np.array_equal(o3[:5], o[:5]) and np.array_equal(l3, lse)
+    # descale_q x 4 with descale_k / 4: the same scores
+    o4, l4 = oracle.prefill_fp8_varlen(x.q8, x.k8, x.v8, x.descale_q * 4, x.descale_k / 4, x.descale_v,
+                                       x.cu_seqlens, True, x.scale)
+    assert np.abs(o4 - o).max() <= 1e-12 and np.abs(l4 - lse).max() <= 1e-12
 
 
 def test_fp8_decode_worked_example_and_invariants():
