@@ -12,7 +12,7 @@
 //
 // gfx950 mapping
 //   * workgroup = 4 waves x 32 query rows (128 rows); key/value tile = 32 keys.
-//     The kernel fits in 166 VGPRs (d = 128) so three workgroups (three waves
+//     The kernel fits in 167 VGPRs (d = 128) so three workgroups (three waves
 //     per SIMD) are resident per compute unit: the operand reads from LDS are
 //     the limiter, and the other waves' matrix work covers each wave's LDS
 //     latency.  d = 256 runs two waves per SIMD.
@@ -482,11 +482,11 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
         float rs[kBlocks];
 #pragma unroll
         for (int bb = 0; bb < kBlocks; ++bb) rs[bb] = softmax_tile(S[bb], sl2, mb[bb], Pc[bb]);
-        // Instruction order of this block: the V operand reads run two products
+        // Instruction order of this block: the V operand reads run three products
         // ahead, and the softmax's VALU work is spread between the products so
         // the matrix cores and the vector ALUs overlap inside the wave.
         // (masks: 0x008 MFMA, 0x100 LDS read, 0x002 VALU)
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
         for (int i = 0; i < kKS * (D / 32) * kBlocks; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -528,8 +528,9 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
         // ---- matrix cores: QK(t+1) into the freed score registers
         if (t + 1 < ntiles) {
             qk_tile<D>(S, Kn, qf, kad);
-            // K operand reads two products ahead
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            // the first four K operand reads issue before the first product, so three
+            // stay in flight behind the one each product consumes
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
             for (int i = 0; i < (D / 16) * kKB * kBlocks; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
