@@ -57,6 +57,14 @@ def parse():
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write profiles/*_traffic.json from two rocprofv3 counter runs, then exit")
     ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="time the fp64 oracle on every workload (host CPU only, no GPU) and print one JSON line")
+    ap.add_argument("--oracle-configs", default="c1,c2,c3-8192,c3-16384,c3-30720,c4,c5",
+                    help="workloads timed by --oracle-table")
+    ap.add_argument("--oracle-threads", type=int, default=0,
+                    help="OpenMP threads of the oracle in --oracle-table (0: the runtime's default)")
+    ap.add_argument("--oracle-budget", type=float, default=10.0,
+                    help="approximate seconds of oracle work per sampled workload in --oracle-table")
     return ap.parse_args()
 
 
@@ -175,8 +183,79 @@ def cpu_baseline_decode(dx, nbytes: int):
                       "the bf16 cache's" % (calls, dt * 1e3)}
 
 
+def _timed(fn, min_s: float = 1.0, min_calls: int = 1):
+    """Mean wall time of fn() over repeated calls lasting at least min_s."""
+    calls, t0 = 0, time.perf_counter()
+    while calls < min_calls or time.perf_counter() - t0 < min_s:
+        fn()
+        calls += 1
+    return (time.perf_counter() - t0) / calls, calls
+
+
+def oracle_table(configs, budget_s: float, threads: int = 0):
+    """The fp64 oracle, as it stands, timed on each workload with the inputs already
+    converted to float64 (generation and conversion excluded).  Prefill workloads whose
+    full run would exceed the budget are timed on every k-th query row of all heads, and
+    the full-run time is scaled from that sample by the algorithmic work (the oracle's
+    cost per row grows with the row's visible keys, as the work does)."""
+    import numpy as np
+    import oracle
+    from exact_io_aware_prefill_amd import workloads as W
+
+    if threads > 0:
+        oracle.set_num_threads(threads)
+    rows = {}
+    for c in configs:
+        t_setup = time.perf_counter()
+        if c in ("c1", "c2") or c.startswith("c3-"):
+            cfg = W.PREFILL_SMALL_F32 if c == "c1" else W.PREFILL_2K if c == "c2" else W.prefill_long(int(c[3:]))
+            x = W.make_prefill(cfg)
+            q, k, v = oracle._f64(x.q), oracle._f64(x.k), oracle._f64(x.v)
+            B, Hq, N, d = q.shape
+            full_flop = 2.0 * B * Hq * d * N * N
+
+            def flop_of(step):
+                r = np.arange(0, N, step, dtype=np.float64)
+                return 4.0 * d * float((r + 1).sum()) * B * Hq
+
+            step = 1
+            if full_flop > 2e10:  # calibrate on a sparse sample, then size the sample to the budget
+                probe = max(1, N // 64)
+                t0 = time.perf_counter()
+                oracle.prefill(q, k, v, True, x.scale, row_step=probe)
+                rate = flop_of(probe) / max(time.perf_counter() - t0, 1e-6)
+                step = max(1, int(np.ceil(full_flop / (rate * budget_s))))
+            dt, calls = _timed(lambda: oracle.prefill(q, k, v, True, x.scale, row_step=step),
+                               min_s=0.5 if step == 1 else 0.0)
+            full_s = dt * full_flop / flop_of(step) if step > 1 else dt
+            rows[c] = {"workload": cfg["name"], "seconds_full": full_s,
+                       "value": full_flop / full_s / 1e12, "unit": "TFLOP/s",
+                       "sample": "all rows" if step == 1 else "every %d-th query row of all %d heads (%.1f s), "
+                                 "scaled to the full run by work" % (step, Hq, dt),
+                       "calls": calls}
+        elif c in ("c4", "c5"):
+            dx = W.make_decode_32k() if c == "c4" else W.make_decode_paged()
+            qd, kc, vc = oracle._f64(dx.q), oracle._f64(dx.k_cache), oracle._f64(dx.v_cache)
+            lens = dx.seq_lens.numpy().astype(np.int64)
+            Hkv, d = kc.shape[2], kc.shape[3]
+            nbytes = float(lens.sum()) * Hkv * d * 2 * 2  # K and V rows attended, as bf16
+            dt, calls = _timed(lambda: oracle.decode(qd, kc, vc, dx.block_table, dx.seq_lens, dx.scale,
+                                                     dx.page_size, dx.max_blocks), min_s=1.0)
+            rows[c] = {"workload": (W.DECODE_32K if c == "c4" else W.DECODE_PAGED)["name"], "seconds_full": dt,
+                       "value": nbytes / dt / 1e9, "unit": "GB/s (bf16 K/V bytes attended)", "sample": "whole call",
+                       "calls": calls}
+        else:
+            raise SystemExit("unknown workload %r" % c)
+        rows[c]["elapsed_s"] = round(time.perf_counter() - t_setup, 1)  # generation, conversion and timing
+        print("oracle %s: %s" % (c, json.dumps(rows[c])), file=sys.stderr, flush=True)
+    return {"threads": oracle.num_threads(), "host_cpu": host_cpu(), "workloads": rows}
+
+
 def main():
     args = parse()
+    if args.oracle_table:
+        print(json.dumps(oracle_table(args.oracle_configs.split(","), args.oracle_budget, args.oracle_threads)), flush=True)
+        return
     if args.write_traffic:
         write_traffic(args.write_traffic[0], args.write_traffic[1], args.traffic_command)
         return

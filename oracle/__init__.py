@@ -62,12 +62,13 @@ def _load():
         lib.oracle_lse_combine.argtypes = [P, P, P, i, i, i, P, P]
         lib.oracle_online_trace.argtypes = [P, P, i, i, P, P, P, P, P, P]
         lib.oracle_num_threads.argtypes = []
+        lib.oracle_set_num_threads.argtypes = [i]
         lib.oracle_e4m3_decode.argtypes = [P, P, ctypes.c_int64]
         lib.oracle_e4m3_decode.restype = ctypes.c_int
         for f in (lib.oracle_prefill, lib.oracle_prefill_ext, lib.oracle_decode_ext,
                   lib.oracle_prefill_tiled, lib.oracle_decode,
                   lib.oracle_split_decode, lib.oracle_lse_combine, lib.oracle_online_trace,
-                  lib.oracle_num_threads):
+                  lib.oracle_num_threads, lib.oracle_set_num_threads):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -92,6 +93,11 @@ def _p(a):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Use n OpenMP threads from now on (n > 0); returns the count in effect."""
+    return int(_load().oracle_set_num_threads(int(n)))
 
 
 def prefill(q, k, v, causal: bool, scale: float, row_step: int = 1, window: int = -1, softcap: float = 0.0):

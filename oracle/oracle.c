@@ -517,6 +517,14 @@ int oracle_e4m3_decode(const uint8_t *in, double *out, int64_t n)
     return 0;
 }
 
+/* Set the number of OpenMP threads the oracle's parallel loops use (n > 0), e.g. one
+ * for a single-core timing; returns the count now in effect. */
+int oracle_set_num_threads(int n)
+{
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -779,3 +779,24 @@ def test_fp8_decode_worked_example_and_invariants():
     od, ld = oracle.decode_fp8(qx[None], kc[2:3], vc[2:3], dk[2:3], dv[2:3], None, np.array([L], np.int32),
                                0.3, 16, 3)
     assert np.array_equal(op[0, :, L - 1], od[0]) and np.array_equal(lp[0, :, L - 1], ld[0])
+
+
+def test_oracle_result_does_not_depend_on_its_thread_count():
+    """The oracle's threads split rows and heads, never one row's sums, so its results
+    are bitwise the same on one thread as on all of them (the single-core timing
+    therefore measures the same computation)."""
+    x = W.prefill_inputs(21, 1, 4, 2, 97, 64, W.BF16)
+    y = W.decode_paged_inputs(22, 3, 4, 2, 64, 16, 1, 300, lengths=[300, 17, 129])
+    n0 = oracle.num_threads()
+    try:
+        outs = []
+        for n in (1, max(2, n0)):
+            assert oracle.set_num_threads(n) == n
+            o, l = oracle.prefill(x.q, x.k, x.v, True, x.scale)
+            od, ld = oracle.decode(y.q, y.k_cache, y.v_cache, y.block_table, y.seq_lens, y.scale,
+                                   y.page_size, y.max_blocks)
+            outs.append((o, l, od, ld))
+    finally:
+        oracle.set_num_threads(n0)
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
