@@ -50,13 +50,15 @@
 //     first reference from the first tile's true row max.  Exponentials run in
 //     base 2 with scale*log2(e) folded into one FMA; the reference is kept in
 //     those units.
-//   * Work order: workgroup ids walk (sequence, KV head, query tile, query head)
-//     with the query head fastest, so the query heads that share a KV head run
-//     at the same time and read the same key/value tiles.  Query tiles are
-//     taken in zig-zag order (last, first, second last, second, ...) so the
-//     longest tiles start first and the causal work stays balanced over time.
-//     (Remapping ids so that each XCD gets a contiguous slice of this list, to
-//     keep a KV head's tiles in one XCD's L2, measured 2% slower.)
+//   * Work order: longest first.  Workgroup ids walk (query tile descending,
+//     sequence, KV head, query head) with the query head fastest: every head's
+//     last (longest, under the causal mask) tile is dispatched before any
+//     shorter one, and the query heads that share a KV head run side by side
+//     and read the same key/value tiles.  Greedy dispatch of a longest-first
+//     list leaves the least idle time at the end of the launch; it measured
+//     3-5% faster at 16k-30k prompts and 8-11% at 8k than walking each KV head's
+//     tiles in turn in zig-zag order.  (Also giving each KV head its own XCDs,
+//     so its tiles stay in one L2, changed nothing.)
 //   * A second instantiation adds a sliding window (row i sees keys i - w .. i;
 //     the tile loop starts at the first tile of row q0's window and tiles that
 //     reach below a row's window are masked as the diagonal is) and logit
@@ -310,14 +312,14 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // ---- work item: (b, kv head, zig-zag q tile, q head), query head fastest ----
+    // ---- work item: (q tile descending, b, kv head, q head), query head fastest ----
     const int item = blockIdx.x;
     const int j = item % a.group;
-    const int r = (item / a.group) % a.n_qtiles;
-    const int bg = item / (a.group * a.n_qtiles);
+    const int bg = (item / a.group) % (a.B * a.Hkv);
+    const int r = item / (a.group * a.B * a.Hkv);
     const int b = bg / a.Hkv, hk = bg % a.Hkv;
     const int h = hk * a.group + j;
-    const int qtile = (r & 1) ? (r >> 1) : a.n_qtiles - 1 - (r >> 1);
+    const int qtile = a.n_qtiles - 1 - r;
     const int q0 = qtile * kBM;
     // this sequence's first token and length
     long long tok0;
