@@ -32,7 +32,7 @@ ATTN_BF16 = 1
 
 EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_ext", "attn_prefill_fp8", "attn_prefill_fp8_varlen",
            "attn_decode", "attn_decode_append", "attn_decode_ext", "attn_decode_fp8", "attn_decode_chunk_tokens",
-           "attn_decode_workspace_bytes", "attn_lse_combine", "attn_status_string")
+           "attn_decode_workspace_bytes", "attn_lse_combine", "attn_decode_check_tables", "attn_status_string")
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -60,6 +60,8 @@ lib.attn_decode.restype = _I
 lib.attn_decode_append.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                                    _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode_append.restype = _I
+lib.attn_decode_check_tables.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P, _P]
+lib.attn_decode_check_tables.restype = _I
 lib.attn_decode_chunk_tokens.argtypes = [_I, _I, _I, _I, _I]
 lib.attn_decode_chunk_tokens.restype = _I
 lib.attn_decode_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I, _I]
@@ -263,6 +265,17 @@ def attn_lse_combine(o_parts, lse_parts, n_splits, o, lse, stream=None) -> None:
                               _dtype_code(o), _ptr(lse), _stream(stream))
     _check(rc, "attn_lse_combine")
 
+
+
+def attn_decode_check_tables(block_table, seq_lens, page_size: int, max_blocks_per_seq: int, num_blocks: int,
+                             appended: bool, bad_out, stream=None) -> None:
+    """block_table [B, max_blocks] int32 or None; seq_lens [B] int32; bad_out: a one-element
+    int32 device tensor, overwritten with the number of out-of-range lengths and used table
+    entries (read it after synchronising)."""
+    rc = lib.attn_decode_check_tables(_ptr(block_table), _ptr(seq_lens), int(seq_lens.shape[0]), int(page_size),
+                                      int(max_blocks_per_seq), int(num_blocks), 1 if appended else 0, _ptr(bad_out),
+                                      _stream(stream))
+    _check(rc, "attn_decode_check_tables")
 
 # ---- conveniences that allocate outputs with PyTorch (allocation only) ----------
 def _plain(window_left, softcap) -> bool:

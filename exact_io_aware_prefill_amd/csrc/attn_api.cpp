@@ -163,6 +163,30 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
 
 extern "C" {
 
+int attn_decode_check_tables(const int32_t *block_table_or_null, const int32_t *seq_lens, int batch,
+                             int page_size, int max_blocks_per_seq, int num_blocks, int appended, int32_t *bad_out,
+                             void *stream)
+{
+    if (batch < 0 || page_size <= 0 || max_blocks_per_seq <= 0 || (block_table_or_null && num_blocks < 0) ||
+        (appended != 0 && appended != 1))
+        return ATTN_ERR_SHAPE;
+    if ((!seq_lens && batch > 0) || !bad_out) return ATTN_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(seq_lens) & 3u) != 0 || (reinterpret_cast<uintptr_t>(bad_out) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(block_table_or_null) & 3u) != 0)
+        return ATTN_ERR_ALIGN;
+    attn::TableCheckParams p;
+    p.block_table = block_table_or_null;
+    p.seq_lens = seq_lens;
+    p.B = batch;
+    p.page_size = page_size;
+    p.max_blocks = max_blocks_per_seq;
+    p.num_blocks = num_blocks;
+    p.appended = appended;
+    p.bad_out = bad_out;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return run([&] { return attn::launch_check_tables(p, s); });
+}
+
 const char *attn_status_string(int status)
 {
     switch (status) {

@@ -81,6 +81,15 @@ struct CombineParams {
 };
 hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream);
 
+// Device-side check of a decode's block table and lengths (decode.hip).
+struct TableCheckParams {
+    const int32_t *block_table;  // [B, max_blocks], or NULL (contiguous cache: lengths only)
+    const int32_t *seq_lens;     // [B]
+    int B, page_size, max_blocks, num_blocks;
+    int appended;                // 1: lengths exclude a token appended in place
+    int32_t *bad_out;            // one int32, overwritten
+};
+hipError_t launch_check_tables(const TableCheckParams &p, hipStream_t stream);
 // Decode tiling constants the host front end needs for validation/sizing.
 constexpr int kDecodeMaxGroup = 16;  // largest supported n_q_heads / n_kv_heads
 constexpr int kDecodeTokenQuantum = 16;  // chunk sizes are multiples of this

@@ -791,6 +791,54 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     return launch_combine_d(p.head_dim, c, rows, stream);
 }
 
+namespace {
+
+// Table check: one workgroup walks every sequence's length and every table slot a
+// decode of that length reads, counting entries outside their valid range, and
+// thread 0 stores the total.  One workgroup and one plain store: no atomics and
+// no memory that must start at zero, so the result is deterministic.
+constexpr int kCheckThreads = 1024;
+
+__global__ __launch_bounds__(kCheckThreads) void check_tables_kernel(TableCheckParams p)
+{
+    __shared__ unsigned partial[kCheckThreads / 64];
+    const long long cap = (long long)p.max_blocks * p.page_size;
+    unsigned bad = 0;
+    for (int b = threadIdx.x; b < p.B; b += kCheckThreads) {
+        const long long need = (long long)p.seq_lens[b] + p.appended;
+        if (p.seq_lens[b] < 0 || need > cap) ++bad;
+    }
+    if (p.block_table) {
+        const long long slots = (long long)p.B * p.max_blocks;
+        for (long long i = threadIdx.x; i < slots; i += kCheckThreads) {
+            const int b = (int)(i / p.max_blocks), j = (int)(i % p.max_blocks);
+            // tokens a decode reads from this sequence, clamped into [0, capacity]
+            const long long used = min(max((long long)p.seq_lens[b] + p.appended, 0LL), cap);
+            if ((long long)j * p.page_size < used) {
+                const int e = p.block_table[i];
+                if (e < 0 || e >= p.num_blocks) ++bad;
+            }
+        }
+    }
+    // wave sums by shuffles, then the waves' sums through LDS
+    for (int off = 32; off > 0; off >>= 1) bad += __shfl_down(bad, off, 64);
+    if ((threadIdx.x & 63) == 0) partial[threadIdx.x >> 6] = bad;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned long long t = 0;
+        for (int w = 0; w < kCheckThreads / 64; ++w) t += partial[w];
+        *p.bad_out = (int32_t)min(t, (unsigned long long)INT32_MAX);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_check_tables(const TableCheckParams &p, hipStream_t stream)
+{
+    hipLaunchKernelGGL(check_tables_kernel, dim3(1), dim3(kCheckThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream)
 {
     CombineArgs c;

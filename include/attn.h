@@ -332,6 +332,38 @@ int attn_lse_combine(const float *o_parts, const float *lse_parts,
                      const int32_t *n_splits_or_null, int rows, int max_splits, int head_dim,
                      void *o, int o_dtype, float *lse_or_null, void *stream);
 
+/*
+ * attn_decode_check_tables -- count, on the device, the entries of a decode's
+ * block table and lengths that would send attn_decode (or attn_decode_append)
+ * outside the cache.  The page's section "Minimal implementation" defines the
+ * paged cache (num_blocks, block_size, kv_heads, head_dim), the block table
+ * (batch, max_blocks) int32 and the per-sequence lengths; the decode kernels read
+ * these device arrays without checking them, since the host cannot see them.
+ * Callers that build tables from untrusted or changing state can run this first
+ * (a debug mode), synchronise, and read the count.
+ *
+ *   block_table_or_null [batch, max_blocks_per_seq] int32, or NULL for a
+ *               contiguous cache (only the lengths are checked)
+ *   seq_lens    [batch] int32: the lengths attn_decode would be given
+ *   num_blocks  pages in the cache pool (entries must lie in [0, num_blocks))
+ *   appended    0: lengths count the attended tokens (attn_decode); 1: lengths
+ *               count the cached tokens before an in-place append
+ *               (attn_decode_append), so one more token must fit
+ *   bad_out     one int32 on the device, overwritten with the count: each
+ *               sequence with length < 0 or length + appended > max_blocks_per_seq
+ *               * page_size counts once, and each table slot j with j * page_size
+ *               < min(length + appended, capacity) holding an entry outside [0,
+ *               num_blocks) counts once (slots past a sequence's length are never
+ *               read and are not checked); saturates at INT32_MAX.
+ *   All pointers are device pointers, 4-byte aligned (else ATTN_ERR_ALIGN);
+ *   bad_out may not be NULL, nor seq_lens unless batch is 0 (which writes 0).  Asynchronous on
+ *   `stream`; one workgroup reads each length and table entry once; no memory
+ *   other than *bad_out is written.
+ */
+int attn_decode_check_tables(const int32_t *block_table_or_null, const int32_t *seq_lens, int batch,
+                             int page_size, int max_blocks_per_seq, int num_blocks, int appended,
+                             int32_t *bad_out, void *stream);
+
 /* attn_status_string -- static, human-readable text for a status code. */
 const char *attn_status_string(int status);
 

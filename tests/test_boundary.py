@@ -316,3 +316,24 @@ def combine(op=FAKE, lp=FAKE, ns=0, rows=4, S=3, d=128, o=FAKE, odt=1, lse=0):
 ])
 def test_combine_argument_errors(kw, code):
     assert combine(**kw) == code
+
+
+def check_tables(bt=FAKE, sl=FAKE, B=4, page=16, mb=8, nb=32, app=0, out=FAKE):
+    return attn.lib.attn_decode_check_tables(P(bt), P(sl), B, page, mb, nb, app, P(out), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sl=0), attn.ATTN_ERR_NULL),
+    (dict(out=0), attn.ATTN_ERR_NULL),
+    (dict(B=0, out=0), attn.ATTN_ERR_NULL),
+    (dict(B=-1), attn.ATTN_ERR_SHAPE),
+    (dict(page=0), attn.ATTN_ERR_SHAPE),
+    (dict(mb=0), attn.ATTN_ERR_SHAPE),
+    (dict(nb=-1), attn.ATTN_ERR_SHAPE),
+    (dict(app=2), attn.ATTN_ERR_SHAPE),
+    (dict(out=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    (dict(sl=FAKE + 1), attn.ATTN_ERR_ALIGN),
+    (dict(bt=FAKE + 2), attn.ATTN_ERR_ALIGN),
+])
+def test_check_tables_argument_errors(kw, code):
+    assert check_tables(**kw) == code
