@@ -31,6 +31,7 @@ ATTN_F32 = 0
 ATTN_BF16 = 1
 
 EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_ext", "attn_prefill_fp8", "attn_prefill_fp8_varlen",
+           "attn_prefill_fp8_ext",
            "attn_decode", "attn_decode_append", "attn_decode_ext", "attn_decode_fp8", "attn_decode_chunk_tokens",
            "attn_decode_workspace_bytes", "attn_lse_combine", "attn_decode_check_tables", "attn_status_string")
 
@@ -48,6 +49,9 @@ lib.attn_prefill_fp8.restype = _I
 lib.attn_prefill_fp8_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                         ctypes.c_float, _P]
 lib.attn_prefill_fp8_varlen.restype = _I
+lib.attn_prefill_fp8_ext.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
+                                     ctypes.c_float, _P]
+lib.attn_prefill_fp8_ext.restype = _I
 lib.attn_decode_ext.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                                 ctypes.c_float, _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode_ext.restype = _I
@@ -164,6 +168,22 @@ def attn_prefill_fp8_varlen(q8, k8, v8, o, lse, descale_q, descale_k, descale_v,
                                      _ptr(descale_k), _ptr(descale_v), _ptr(cu_seqlens), B, int(max_seqlen), T, Hq,
                                      k8.shape[1], d, int(bool(causal)), float(scale), _stream(stream))
     _check(rc, "attn_prefill_fp8_varlen")
+
+
+def attn_prefill_fp8_ext(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen: int,
+                         causal: bool, scale: float, window_left: int, softcap: float, stream=None) -> None:
+    """attn_prefill_fp8 (cu_seqlens None: padded [B, H, N, d]) or attn_prefill_fp8_varlen (packed
+    [T, H, d] with cu_seqlens) with a sliding window (-1: none) and a logit soft-cap (0: none)."""
+    if cu_seqlens is None:
+        B, Hq, N, d = q8.shape
+        Hkv, T, seq = k8.shape[1], 0, N
+    else:
+        T, Hq, d = q8.shape
+        B, Hkv, seq = cu_seqlens.numel() - 1, k8.shape[1], int(max_seqlen)
+    rc = lib.attn_prefill_fp8_ext(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(o), _ptr(lse), _ptr(descale_q), _ptr(descale_k),
+                                  _ptr(descale_v), _ptr(cu_seqlens), B, seq, T, Hq, Hkv, d, int(bool(causal)),
+                                  float(scale), int(window_left), float(softcap), _stream(stream))
+    _check(rc, "attn_prefill_fp8_ext")
 
 
 def attn_decode_chunk_tokens(batch: int, n_kv_heads: int, page_size: int, max_blocks_per_seq: int,
@@ -309,22 +329,32 @@ def prefill_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, sc
 
 
 def prefill_fp8(q8, k8, v8, descale_q=None, descale_k=None, descale_v=None, causal: bool = True,
-                scale: float | None = None, stream=None):
+                scale: float | None = None, stream=None, window_left: int = -1, softcap: float = 0.0):
     B, Hq, N, d = q8.shape
     o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
-    attn_prefill_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, d ** -0.5 if scale is None else scale,
-                     stream)
+    scale = d ** -0.5 if scale is None else scale
+    if _plain(window_left, softcap):
+        attn_prefill_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, scale, stream)
+    else:
+        attn_prefill_fp8_ext(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, None, N, causal, scale, window_left,
+                             softcap, stream)
     return o, lse
 
 
 def prefill_fp8_varlen(q8, k8, v8, cu_seqlens, max_seqlen: int, descale_q=None, descale_k=None, descale_v=None,
-                       causal: bool = True, scale: float | None = None, stream=None):
+                       causal: bool = True, scale: float | None = None, stream=None, window_left: int = -1,
+                       softcap: float = 0.0):
     T, Hq, d = q8.shape
     o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=q8.device)
-    attn_prefill_fp8_varlen(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen, causal,
-                            d ** -0.5 if scale is None else scale, stream)
+    scale = d ** -0.5 if scale is None else scale
+    if _plain(window_left, softcap):
+        attn_prefill_fp8_varlen(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen, causal,
+                                scale, stream)
+    else:
+        attn_prefill_fp8_ext(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen, causal,
+                             scale, window_left, softcap, stream)
     return o, lse
 
 

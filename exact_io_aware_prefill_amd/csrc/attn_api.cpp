@@ -237,10 +237,11 @@ namespace {
 int prefill_fp8_impl(bool packed, const void *q, const void *k, const void *v, void *o, float *lse,
                      const float *descale_q, const float *descale_k, const float *descale_v,
                      const int32_t *cu_seqlens, int batch, int seqlen, int total_tokens, int n_q_heads,
-                     int n_kv_heads, int head_dim, int causal, float scale, void *stream)
+                     int n_kv_heads, int head_dim, int causal, float scale, int window_left, float softcap,
+                     void *stream)
 {
     if (batch < 0 || seqlen < 0 || (packed && total_tokens < 0) || n_q_heads <= 0 || n_kv_heads <= 0 ||
-        head_dim <= 0)
+        head_dim <= 0 || !variant_ok(window_left, softcap))
         return ATTN_ERR_SHAPE;
     if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
     if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
@@ -264,6 +265,8 @@ int prefill_fp8_impl(bool packed, const void *q, const void *k, const void *v, v
     p.B = batch; p.N = seqlen; p.Hq = n_q_heads; p.Hkv = n_kv_heads; p.head_dim = head_dim;
     p.causal = causal ? 1 : 0;
     p.scale = scale;
+    p.window = window_left;
+    p.softcap = softcap;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return run([&] { return attn::launch_prefill_fp8(p, s); });
 }
@@ -276,7 +279,8 @@ int attn_prefill_fp8(const void *q, const void *k, const void *v, void *o, float
                      int head_dim, int causal, float scale, void *stream)
 {
     return prefill_fp8_impl(false, q, k, v, o, lse, descale_q_or_null, descale_k_or_null, descale_v_or_null,
-                            nullptr, batch, seqlen, 0, n_q_heads, n_kv_heads, head_dim, causal, scale, stream);
+                            nullptr, batch, seqlen, 0, n_q_heads, n_kv_heads, head_dim, causal, scale, -1, 0.f,
+                            stream);
 }
 
 int attn_prefill_fp8_varlen(const void *q, const void *k, const void *v, void *o, float *lse,
@@ -287,7 +291,18 @@ int attn_prefill_fp8_varlen(const void *q, const void *k, const void *v, void *o
 {
     return prefill_fp8_impl(true, q, k, v, o, lse, descale_q_or_null, descale_k_or_null, descale_v_or_null,
                             cu_seqlens, batch, max_seqlen, total_tokens, n_q_heads, n_kv_heads, head_dim, causal,
-                            scale, stream);
+                            scale, -1, 0.f, stream);
+}
+
+int attn_prefill_fp8_ext(const void *q, const void *k, const void *v, void *o, float *lse,
+                         const float *descale_q_or_null, const float *descale_k_or_null,
+                         const float *descale_v_or_null, const int32_t *cu_seqlens_or_null, int batch, int seqlen,
+                         int total_tokens, int n_q_heads, int n_kv_heads, int head_dim, int causal, float scale,
+                         int window_left, float softcap, void *stream)
+{
+    return prefill_fp8_impl(cu_seqlens_or_null != nullptr, q, k, v, o, lse, descale_q_or_null, descale_k_or_null,
+                            descale_v_or_null, cu_seqlens_or_null, batch, seqlen, total_tokens, n_q_heads,
+                            n_kv_heads, head_dim, causal, scale, window_left, softcap, stream);
 }
 
 int attn_decode_chunk_tokens(int batch, int n_kv_heads, int page_size, int max_blocks_per_seq,

@@ -40,6 +40,8 @@ struct PrefillFp8Params {
     int total;                  // packed: T
     int B, N, Hq, Hkv, head_dim, causal;
     float scale;
+    int window = -1;       // as PrefillParams
+    float softcap = 0.f;
 };
 hipError_t launch_prefill_fp8(const PrefillFp8Params &p, hipStream_t stream);
 

@@ -50,6 +50,7 @@
 //     XCDs so its 8-bit K/V tiles stay in their L2s (+2% more; the bf16 kernel,
 //     whose tiles are twice the bytes, timed the same either way).
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include <type_traits>
@@ -90,6 +91,10 @@ struct Args {
     long long kv_head, kv_row; // strides of k and v
     long long lse_head;        // stride of lse between heads (rows are adjacent)
     float scale;
+    // window / soft-cap instantiation only: row i sees keys >= i - window (-1: no
+    // limit); softcap > 0 caps each scaled score s at softcap * tanh(s / softcap)
+    int window;
+    float softcap;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
@@ -218,7 +223,17 @@ __device__ __forceinline__ float softmax_tile(const f32x16_t (&S)[2], float sl2,
 
 // PACKED selects the packed layout (a separate instantiation, so the padded one
 // keeps its row strides as compile-time constants).
-template <int D, bool PACKED>
+// Logit soft-cap of one raw score: cap * tanh(x / cap) with tanh(y) = 1 - 2 / (e^{2y} + 1)
+// (exact for y -> +-inf), cap_k = 2 log2(e) / cap.
+__device__ __forceinline__ float soft_cap(float x, float cap, float cap_k)
+{
+    const float r = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(x * cap_k) + 1.f);
+    return fmaf(-2.f * cap, r, cap);
+}
+
+// EXT selects the sliding-window / soft-cap instantiation (the plain ones keep
+// their instruction schedule).
+template <int D, bool PACKED, bool EXT>
 __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
 {
     constexpr int NT = kWaves * 64;
@@ -280,6 +295,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     const bool negate = eff < 0.f;  // s * eff = (-s) * |eff|: flip Q's sign bits
     const float aeff = fmaxf(fabsf(eff), 1e-30f);
     const float sl2 = aeff * kLog2e;
+    // soft-cap on raw scores x: x * aeff becomes softcap * tanh(x * aeff / softcap)
+    const float cap_raw = (EXT && a.softcap > 0.f) ? a.softcap / aeff : 0.f;
+    const float cap_k = cap_raw > 0.f ? 2.f * kLog2e / cap_raw : 0.f;
 
     // element offsets of this (sequence, head): packed rows are token-major
     const long long qo = PACKED ? tok0 * a.Hq * D + (long long)h * a.q_head : ((long long)b * a.Hq + h) * a.q_head;
@@ -332,7 +350,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     }
 
     const int kend = a.causal ? min(N, q0 + kBM) : N;
-    const int ntiles = (kend + kBlockN - 1) / kBlockN;
+    // with a window, the first tile holding a key of row q0's window
+    const int kbeg = (EXT && a.window >= 0) ? max(0, q0 - a.window) / kBlockN * kBlockN : 0;
+    const int ntiles = (kend - kbeg + kBlockN - 1) / kBlockN;  // >= 1: key q0 is visible to row q0
 
     // ---- prologue: V buffers start as zeros (tile -1 is multiplied by P = 0, and
     // rows past N must be finite)
@@ -340,8 +360,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
         reinterpret_cast<uint4 *>(VB0)[i] = make_uint4(0, 0, 0, 0);
         reinterpret_cast<uint4 *>(VB1)[i] = make_uint4(0, 0, 0, 0);
     }
-    kld.load(kh, N, 0, wave, KB0);
-    if (ntiles > 1) kld.load(kh, N, kBlockN, wave, KB1);
+    kld.load(kh, N, kbeg, wave, KB0);
+    if (ntiles > 1) kld.load(kh, N, kbeg + kBlockN, wave, KB1);
     wait_loads();
     __syncthreads();
     f32x16_t SA[2], SB[2];
@@ -358,17 +378,28 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
     // both products overlap the softmax of tile t)
     auto step = [&](f32x16_t (&S)[2], f32x16_t (&Sn)[2], i32x8_t &Pp, i32x8_t &Pc, int t, const uint8_t *Kn,
                     const uint8_t *Vp, uint8_t *Kw, uint8_t *Vw) {
-        const int k0 = t * kBlockN;
+        const int k0 = kbeg + t * kBlockN;
         if (t + 2 < ntiles) kld.load(kh, N, k0 + 2 * kBlockN, wave, Kw);
         vld.load(vh, N, k0, wave, Vw);
-        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > N) {
-            const int qrow = wrow0 + l32;
-            const int lim = (a.causal ? min(qrow, N - 1) : N - 1) - (k0 + 4 * hh);
+        if (EXT && cap_raw > 0.f) {  // soft-cap before masking, so masked scores stay -inf
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (32 * kb + 8 * (i >> 2) + (i & 3) > lim) S[kb][i] = -INFINITY;
+                for (int i = 0; i < 16; ++i) S[kb][i] = soft_cap(S[kb][i], cap_raw, cap_k);
+        }
+        // a tile reaching below some row's window start (wrow0 + 31 - window for the wave's last row)
+        const bool win = EXT && a.window >= 0 && k0 < wrow0 + 31 - a.window;
+        if ((a.causal && k0 + kBlockN - 1 > wrow0) || k0 + kBlockN > N || win) {
+            const int qrow = wrow0 + l32;
+            const int lim = (a.causal ? min(qrow, N - 1) : N - 1) - (k0 + 4 * hh);
+            const int low = win ? qrow - a.window - (k0 + 4 * hh) : INT_MIN;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int e = 32 * kb + 8 * (i >> 2) + (i & 3);
+                    if (e > lim || (EXT && e < low)) S[kb][i] = -INFINITY;
+                }
         }
         if (t + 1 < ntiles) qk_tile<D>(Sn, Kn, qf, kad0, kad1);
         pv_tile<D>(acc, Vp, Pp, vad);
@@ -389,14 +420,18 @@ __global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[kb][i]);
             mx = fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
             const float m_new = fmaxf(m, mx);
-            const float c = __builtin_amdgcn_exp2f((m - m_new) * sl2);  // 0 while m = -inf
+            // Only the window variant can meet a row with no visible key yet (m_new =
+            // -inf): its state stays (m, l, acc) = (-inf, 0, 0), and a reference of 0
+            // gives the masked scores probability 0.
+            const bool none = EXT && m_new == -INFINITY;
+            const float c = none ? 1.f : __builtin_amdgcn_exp2f((m - m_new) * sl2);  // 0 while m = -inf
             l *= c;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[db][i] *= c;
             m = m_new;
-            rs = softmax_tile(S, sl2, m * sl2, Pc);
+            rs = softmax_tile(S, sl2, none ? 0.f : m * sl2, Pc);
         }
         l += rs;
         wait_loads();
@@ -470,15 +505,33 @@ hipError_t launch_prefill_fp8(const PrefillFp8Params &p, hipStream_t stream)
     // one head's rows of one sequence, including the padded last query tile, are
     // addressed with 32-bit offsets (q rows are the widest)
     if ((long long)a.n_qtiles * kBM * a.q_row > 0xffffffffLL) return hipErrorInvalidValue;
+    // a window reaching back past the first key limits nothing
+    a.window = (p.window >= 0 && p.window < p.N) ? p.window : -1;
+    a.softcap = p.softcap > 0.f ? p.softcap : 0.f;
+    const bool ext = a.window >= 0 || a.softcap > 0.f;
     const dim3 grid((unsigned)items), block(kWaves * 64);
-    if (p.head_dim == 128 && p.cu_seqlens)
-        hipLaunchKernelGGL((prefill_fp8_kernel<128, true>), grid, block, 0, stream, a);
-    else if (p.head_dim == 128)
-        hipLaunchKernelGGL((prefill_fp8_kernel<128, false>), grid, block, 0, stream, a);
-    else if (p.cu_seqlens)
-        hipLaunchKernelGGL((prefill_fp8_kernel<64, true>), grid, block, 0, stream, a);
+    auto launch = [&](auto dconst, auto packed, auto extc) {
+        hipLaunchKernelGGL((prefill_fp8_kernel<decltype(dconst)::value, decltype(packed)::value, decltype(extc)::value>),
+                           grid, block, 0, stream, a);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    auto by_ext = [&](auto dconst, auto packed) {
+        if (ext)
+            launch(dconst, packed, T_());
+        else
+            launch(dconst, packed, F_());
+    };
+    auto by_packed = [&](auto dconst) {
+        if (p.cu_seqlens)
+            by_ext(dconst, T_());
+        else
+            by_ext(dconst, F_());
+    };
+    if (p.head_dim == 128)
+        by_packed(std::integral_constant<int, 128>());
     else
-        hipLaunchKernelGGL((prefill_fp8_kernel<64, false>), grid, block, 0, stream, a);
+        by_packed(std::integral_constant<int, 64>());
     return hipGetLastError();
 }
 

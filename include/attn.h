@@ -204,6 +204,31 @@ int attn_prefill_fp8_varlen(const void *q, const void *k, const void *v, void *o
                             int causal, float scale, void *stream);
 
 /*
+ * attn_prefill_fp8_ext -- attn_prefill_fp8 (cu_seqlens_or_null == NULL; seqlen is
+ * N, total_tokens ignored) or attn_prefill_fp8_varlen (cu_seqlens_or_null !=
+ * NULL; seqlen is max_seqlen) with the sliding window and the logit soft-cap of
+ * attn_prefill_ext, the two variants the pofe.ai page's section "Interaction
+ * with post-trained models" lists, on 8-bit inputs as that section's FP8
+ * paragraph describes.
+ *
+ *   window_left  -1: no window; >= 0: the query at position i also needs key
+ *                position j >= i - window_left; below -1 is ATTN_ERR_SHAPE.
+ *   softcap      0: none; > 0 (finite): each scaled score s = scale * dq * dk *
+ *                <q8, k8> becomes softcap * tanh(s / softcap) before masking and
+ *                the softmax (tanh(y) formed as 1 - 2 / (e^{2y} + 1) with the
+ *                hardware exponential and reciprocal); negative or non-finite is
+ *                ATTN_ERR_SHAPE.
+ *   With window_left = -1 and softcap = 0 the plain FP8 kernels run (the results
+ *   of attn_prefill_fp8 / attn_prefill_fp8_varlen, bit for bit).  Layouts,
+ *   descales, arithmetic, limits and errors as those two calls.
+ */
+int attn_prefill_fp8_ext(const void *q, const void *k, const void *v, void *o, float *lse,
+                         const float *descale_q_or_null, const float *descale_k_or_null,
+                         const float *descale_v_or_null, const int32_t *cu_seqlens_or_null, int batch, int seqlen,
+                         int total_tokens, int n_q_heads, int n_kv_heads, int head_dim, int causal, float scale,
+                         int window_left, float softcap, void *stream);
+
+/*
  * attn_decode -- one new query token per sequence against a KV cache, by
  * split-KV: the first seq_lens[b] tokens of sequence b are cut into chunks of
  * `chunk_tokens`; one workgroup per (sequence, KV head, chunk) computes the

@@ -286,14 +286,16 @@ def e4m3_decode(codes) -> np.ndarray:
     return out
 
 
-def prefill_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale: float, row_step: int = 1):
+def prefill_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale: float, row_step: int = 1,
+                window: int = -1, softcap: float = 0.0):
     """Attention on FP8 inputs: the plain prefill of the dequantised tensors.
 
     q8 [B, Hq, N, d], k8, v8 [B, Hkv, N, d] are E4M3 byte codes; descale_* are
     [B, Hkv] float factors (None = 1), shared by the query heads of one KV head:
     Q = descale_q[b, h / g] * decode(q8), K and V likewise.  The result is
     prefill(Q, K, V, causal, scale) in float64 -- what the method computes on the
-    dequantised inputs, with no rounding of the probabilities."""
+    dequantised inputs, with no rounding of the probabilities.  window / softcap are
+    those of prefill (the cap acts on the scaled score scale * <Q, K>)."""
     q, k, v = e4m3_decode(q8), e4m3_decode(k8), e4m3_decode(v8)
     B, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -305,10 +307,11 @@ def prefill_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal: bool, scale
     q = q * np.repeat(dq, g, axis=1)[:, :, None, None]
     k = k * dk[:, :, None, None]
     v = v * dv[:, :, None, None]
-    return prefill(q, k, v, causal, scale, row_step=row_step)
+    return prefill(q, k, v, causal, scale, row_step=row_step, window=window, softcap=softcap)
 
 
-def prefill_fp8_varlen(q8, k8, v8, descale_q, descale_k, descale_v, cu_seqlens, causal: bool, scale: float):
+def prefill_fp8_varlen(q8, k8, v8, descale_q, descale_k, descale_v, cu_seqlens, causal: bool, scale: float,
+                       window: int = -1, softcap: float = 0.0):
     """FP8 inputs in the packed layout: q8 [T, Hq, d], k8, v8 [T, Hkv, d] E4M3 codes;
     sequence b (tokens cu_seqlens[b] .. cu_seqlens[b+1]-1) reads its own descales
     descale_*[b, hk] (None = 1) for KV head hk and the query heads that share it.
@@ -328,7 +331,7 @@ def prefill_fp8_varlen(q8, k8, v8, descale_q, descale_k, descale_v, cu_seqlens, 
         q[s0:s1] *= np.repeat(dq[b], g)[None, :, None]
         k[s0:s1] *= dk[b][None, :, None]
         v[s0:s1] *= dv[b][None, :, None]
-    return prefill_varlen(q, k, v, cu, causal, scale)
+    return prefill_varlen(q, k, v, cu, causal, scale, window=window, softcap=softcap)
 
 
 def decode_fp8(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, scale: float,

@@ -337,3 +337,27 @@ def check_tables(bt=FAKE, sl=FAKE, B=4, page=16, mb=8, nb=32, app=0, out=FAKE):
 ])
 def test_check_tables_argument_errors(kw, code):
     assert check_tables(**kw) == code
+
+
+def prefill_fp8_ext(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dq=0, dk=0, dv=0, cu=0, B=2, N=16, T=0, Hq=4, Hkv=2,
+                    d=128, causal=1, window=8, cap=10.0):
+    return attn.lib.attn_prefill_fp8_ext(P(q), P(k), P(v), P(o), P(lse), P(dq), P(dk), P(dv), P(cu), B, N, T, Hq, Hkv,
+                                         d, causal, 0.1, window, cap, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-2), attn.ATTN_ERR_SHAPE),
+    (dict(cap=-1.0), attn.ATTN_ERR_SHAPE),
+    (dict(cap=float("nan")), attn.ATTN_ERR_SHAPE),
+    (dict(cap=float("inf")), attn.ATTN_ERR_SHAPE),
+    (dict(q=0), attn.ATTN_ERR_NULL),
+    (dict(cu=FAKE, T=20, q=0), attn.ATTN_ERR_NULL),   # packed form: same checks as the varlen call
+    (dict(cu=FAKE + 2, T=20), attn.ATTN_ERR_ALIGN),
+    (dict(o=MIS), attn.ATTN_ERR_ALIGN),
+    (dict(dk=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
+    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(B=0, q=0, k=0, v=0, o=0, lse=0), attn.ATTN_OK),
+])
+def test_prefill_fp8_ext_argument_errors(kw, code):
+    assert prefill_fp8_ext(**kw) == code

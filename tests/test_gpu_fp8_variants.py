@@ -1,0 +1,135 @@
+"""GPU parity of the FP8 (E4M3) prefill with a sliding window and logit soft-capping
+(attn_prefill_fp8_ext) against the fp64 oracle on the dequantised codes.  The error
+bar is the FP8 prefill's per-row bound (tests/test_gpu_fp8.py), taken over each
+row's visible keys (causal limit and window) and the capped scores: the kernel rounds
+each probability to E4M3 before the P*V product; the LSE keeps the 1e-3 bar."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_prefill_amd import workloads as W
+from gpu_common import dev, say
+from test_gpu_fp8 import check_fp8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def attn():
+    from exact_io_aware_prefill_amd import attn as a  # raises if libattn.so is missing
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return a
+
+
+def visible_scores(qv, kv, eff, causal, window, softcap, rows, N):
+    """Scaled (and capped) scores of the given rows with the invisible keys at -inf."""
+    s = (qv[rows] @ kv.T) * eff
+    if softcap > 0:
+        s = softcap * np.tanh(s / softcap)
+    j = np.arange(N)[None, :]
+    i = rows[:, None]
+    vis = np.ones_like(s, dtype=bool)
+    if causal:
+        vis &= j <= i
+    if window >= 0:
+        vis &= j >= i - window
+    return np.where(vis, s, -np.inf)
+
+
+def bound_rows(q, k, v, dq, dk, dv, scale, causal, window, softcap, rows, N, g):
+    """Per-row bound descale_v * max|v8| * (2^-4 + n 2^-10 / l) of each head (shape [Hq, rows])."""
+    Hq = q.shape[0]
+    out = np.zeros((Hq, len(rows)))
+    for h in range(Hq):
+        hk = h // g
+        s = visible_scores(q[h], k[hk], scale * dq[hk] * dk[hk], causal, window, softcap, rows, N)
+        n = np.isfinite(s).sum(axis=1)
+        mx = s.max(axis=1)
+        lsum = np.exp(s - mx[:, None]).sum(axis=1)
+        out[h] = np.abs(v[hk]).max() * dv[hk] * (2.0 ** -4 + n * 2.0 ** -10 / lsum)
+    return out
+
+
+def padded_bounds(x, window, softcap, rows=None):
+    q, k, v = (oracle.e4m3_decode(t) for t in (x.q8, x.k8, x.v8))
+    B, Hq, N, d = q.shape
+    g = Hq // k.shape[1]
+    rows = np.arange(N) if rows is None else rows
+    dq, dk, dv = (t.double().numpy() for t in (x.descale_q, x.descale_k, x.descale_v))
+    return np.stack([bound_rows(q[b], k[b], v[b], dq[b], dk[b], dv[b], x.scale, x.causal, window, softcap, rows, N, g)
+                     for b in range(B)])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("window,softcap", [(0, 0.0), (37, 0.0), (200, 0.0), (-1, 20.0), (64, 5.0)])
+def test_fp8_window_softcap_padded(attn, d, causal, window, softcap):
+    N = 333
+    say("case: fp8 ext N=%d d=%d causal=%s window=%d softcap=%g" % (N, d, causal, window, softcap))
+    x = W.prefill_fp8_inputs(4000 + d + window, 2, 8, 2, N, d, causal=causal)
+    o, lse = attn.prefill_fp8(dev(x.q8), dev(x.k8), dev(x.v8), dev(x.descale_q), dev(x.descale_k), dev(x.descale_v),
+                              causal, x.scale, window_left=window, softcap=softcap)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, causal, x.scale,
+                                window=window, softcap=softcap)
+    check_fp8("fp8 ext d=%d causal=%d w=%d cap=%g" % (d, causal, window, softcap), o, lse, ro, rl,
+              padded_bounds(x, window, softcap))
+
+
+def test_fp8_ext_without_options_is_the_plain_kernel(attn):
+    """window -1 and softcap 0 through the variant entry point run the plain kernel: bit for bit."""
+    x = W.prefill_fp8_inputs(4100, 1, 8, 2, 500, 128)
+    args = (dev(x.q8), dev(x.k8), dev(x.v8))
+    ds = (dev(x.descale_q), dev(x.descale_k), dev(x.descale_v))
+    o0, l0 = attn.prefill_fp8(*args, *ds, True, x.scale)
+    o1 = torch.empty_like(o0)
+    l1 = torch.empty_like(l0)
+    attn.attn_prefill_fp8_ext(*args, o1, l1, *ds, None, 500, True, x.scale, -1, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+def test_fp8_window_softcap_packed(attn):
+    """A packed batch of ragged prompts with a window of 100 and a cap of 30."""
+    lens = [1, 7, 0, 128, 129, 300, 64, 1000]
+    window, softcap = 100, 30.0
+    say("case: fp8 ext packed lens=%s window=%d softcap=%g" % (lens, window, softcap))
+    x = W.prefill_fp8_packed_inputs(4200, lens, 8, 2, 128)
+    cu = dev(x.cu_seqlens)
+    o, lse = attn.prefill_fp8_varlen(dev(x.q8), dev(x.k8), dev(x.v8), cu, max(lens), dev(x.descale_q),
+                                     dev(x.descale_k), dev(x.descale_v), True, x.scale, window_left=window,
+                                     softcap=softcap)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_fp8_varlen(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, x.cu_seqlens,
+                                       True, x.scale, window=window, softcap=softcap)
+    q, k, v = (oracle.e4m3_decode(t) for t in (x.q8, x.k8, x.v8))
+    dq, dk, dv = (t.double().numpy() for t in (x.descale_q, x.descale_k, x.descale_v))
+    cuh = x.cu_seqlens.numpy()
+    Hq, Hkv = q.shape[1], k.shape[1]
+    bound = np.zeros((Hq, q.shape[0]))
+    for b in range(len(lens)):
+        s0, s1 = int(cuh[b]), int(cuh[b + 1])
+        if s1 <= s0:
+            continue
+        bound[:, s0:s1] = bound_rows(q[s0:s1].transpose(1, 0, 2), k[s0:s1].transpose(1, 0, 2),
+                                     v[s0:s1].transpose(1, 0, 2), dq[b], dk[b], dv[b], x.scale, True, window, softcap,
+                                     np.arange(s1 - s0), s1 - s0, Hq // Hkv)
+    # packed layout: o [T, Hq, d], lse [Hq, T]; check_fp8 takes the bound per (head, token)
+    check_fp8("fp8 ext packed", o.permute(1, 0, 2), lse, ro.transpose(1, 0, 2), rl, bound)
+
+
+def test_fp8_window_softcap_long_sampled_rows(attn):
+    """N = 8192, 28 query / 4 KV heads, d = 128, window 4096, cap 30: every 97th row."""
+    N, step, window, softcap = 8192, 97, 4096, 30.0
+    say("case: fp8 ext N=%d window=%d cap=%g sampled every %d" % (N, window, softcap, step))
+    x = W.prefill_fp8_inputs(3, 1, 28, 4, N, 128)
+    o, lse = attn.prefill_fp8(dev(x.q8), dev(x.k8), dev(x.v8), dev(x.descale_q), dev(x.descale_k), dev(x.descale_v),
+                              True, x.scale, window_left=window, softcap=softcap)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, True, x.scale, row_step=step,
+                                window=window, softcap=softcap)
+    rows = np.arange(0, N, step)
+    check_fp8("fp8 ext 8k (sampled)", o[:, :, rows], lse[:, :, rows], ro[:, :, rows], rl[:, :, rows],
+              padded_bounds(x, window, softcap, rows))
