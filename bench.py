@@ -36,7 +36,7 @@ TRAFFIC = {
     "decode": {"file": os.path.join(ROOT, "profiles", "decode_split_s32768_traffic.json"),
                "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel<128, false, false, false>"},
     "fp8": {"file": os.path.join(ROOT, "profiles", "prefill_fp8_n16384_traffic.json"),
-            "src": os.path.join(CSRC, "prefill_fp8.hip"), "kernel": "prefill_fp8_kernel<128, false>"},
+            "src": os.path.join(CSRC, "prefill_fp8.hip"), "kernel": "prefill_fp8_kernel<128, false, false>"},
 }
 COPY_BYTES = 1 << 30  # reference dispatch for the counters: a 1 GiB device-to-device copy
 N_KV_COPIES = 8
@@ -368,7 +368,7 @@ def main():
                "config": {"workload": pcfg["name"].replace("bf16", "fp8e4m3"), "descales": "per (sequence, KV head)"},
                "roofline": {"bound": "mfma", "achieved": a8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                             "frac": a8 / PEAK_FP8_TFLOPS, "traffic": measured_traffic("fp8"),
-                            "kernel": "prefill_fp8_kernel<128, false>", "algorithmic_flop_per_launch": prefill_flop}}
+                            "kernel": "prefill_fp8_kernel<128, false, false>", "algorithmic_flop_per_launch": prefill_flop}}
 
     # Decode over an E4M3 copy of the same 32k cache (one byte per element), timed as
     # the bf16 decode: back-to-back calls rotating the copies, between two events

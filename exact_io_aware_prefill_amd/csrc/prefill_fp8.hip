@@ -47,8 +47,8 @@
 //     tile before any shorter one, the query heads of a KV head side by side
 //     (+9% at 16k prompts and +17% at 8k over per-KV-head zig-zag order).  When
 //     the (sequence, KV head) pairs divide the 8 XCDs, each pair gets its own
-//     XCDs so its 8-bit K/V tiles stay in their L2s (+2% more; the bf16 kernel,
-//     whose tiles are twice the bytes, timed the same either way).
+//     XCDs so its 8-bit K/V tiles stay in their L2s (+2% more here; the bf16
+//     kernel timed the same either way and keeps it for its traffic).
 #include <hip/hip_runtime.h>
 #include <limits.h>
 #include <stdint.h>
