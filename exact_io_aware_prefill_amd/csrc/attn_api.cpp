@@ -366,6 +366,18 @@ int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache, con
                        chunk_tokens, workspace, workspace_bytes, stream, true, descale_k_or_null, descale_v_or_null);
 }
 
+int attn_decode_fp8_ext(const void *q, const void *k_cache, const void *v_cache, const float *descale_k_or_null,
+                        const float *descale_v_or_null, const int32_t *block_table, const int32_t *seq_lens, void *o,
+                        float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,
+                        int max_blocks_per_seq, float scale, int window_left, float softcap, int chunk_tokens,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    return decode_impl(false, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, o, lse_or_null, batch,
+                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, ATTN_BF16, scale, window_left,
+                       softcap, chunk_tokens, workspace, workspace_bytes, stream, true, descale_k_or_null,
+                       descale_v_or_null);
+}
+
 int attn_lse_combine(const float *o_parts, const float *lse_parts, const int32_t *n_splits_or_null,
                      int rows, int max_splits, int head_dim, void *o, int o_dtype,
                      float *lse_or_null, void *stream)

@@ -241,7 +241,7 @@ template <int D, bool EXT, bool KV8>
 __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<D, KV8> &s, char *slab,
                                              const bf16x8_t *qf, f32x4_t *acc, float &m, float &l, int tb,
                                              int t_lo, int t_end, int G, const uint32_t *vstore, uint32_t vread,
-                                             float scale_log2)
+                                             float scale_log2, float cap_k)
 {
     using Gm = Geo<D>;
     using Lg = KvGeo<D, KV8>;
@@ -292,7 +292,7 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float xv = capped ? soft_cap_log2(st[blk][i], a.cap_log2, a.cap_k) : st[blk][i] * scale_log2;
+            float xv = capped ? soft_cap_log2(st[blk][i], a.cap_log2, cap_k) : st[blk][i] * scale_log2;
             const int tok = tb + 16 * blk + 4 * G + i;
             if (tail && (tok >= t_end || (EXT && tok < t_lo))) xv = -INFINITY;
             x[4 * blk + i] = xv;
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
 {
     using Gm = Geo<D>;
     using Lg = KvGeo<D, KV8>;
-    static_assert(!KV8 || (!APPEND && !EXT), "the E4M3 cache has the plain decode only");
+    static_assert(!KV8 || !APPEND, "the E4M3 cache has no in-place append");
     constexpr int kWaves = split_waves<D>();
     // one slab per wave; reused at the end for the eight waves' [16][D] float outputs
     static_assert(Gm::SLAB == 16 * D * 4, "slab must hold a wave's 16 x D float output");
@@ -382,6 +382,7 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
     const float dkv = (KV8 && a.dk) ? a.dk[(size_t)b * a.Hkv + hk] : 1.f;
     const float dvv = (KV8 && a.dv) ? a.dv[(size_t)b * a.Hkv + hk] : 1.f;
     const float sl2 = a.scale_log2 * dkv;
+    const float cap_k = a.cap_k * dkv;  // the cap acts on the scaled score raw * scale * descale_k
 
     LaneOffsets lo;
     lo.l16 = l16;
@@ -453,11 +454,11 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
         issue_step<D, KV8>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
         while (tb < t_end) {
             issue_step<D, KV8>(a, r1, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-            consume_step<D, EXT, KV8>(a, r0, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2);
+            consume_step<D, EXT, KV8>(a, r0, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
             tb += stride;
             if (tb >= t_end) break;
             issue_step<D, KV8>(a, r0, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-            consume_step<D, EXT, KV8>(a, r1, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2);
+            consume_step<D, EXT, KV8>(a, r1, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
             tb += stride;
         }
     } else {
@@ -475,7 +476,7 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
                 if (more) {
                     issue_step<D, KV8>(a, r[(j + NS - 1) % NS], kbase, vbase, b, tb + (NS - 1) * stride, t_end,
                                        rstride, lo);
-                    consume_step<D, EXT, KV8>(a, r[j], slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2);
+                    consume_step<D, EXT, KV8>(a, r[j], slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
                     tb += stride;
                     more = tb < t_end;
                 }
@@ -751,7 +752,10 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
         constexpr int kThreads = split_waves<DD>() * 64;
         if constexpr (DD != 256) {
             if (p.kv_e4m3) {
-                hipLaunchKernelGGL((decode_split_kernel<DD, false, false, true>), grid, dim3(kThreads), 0, stream, a);
+                if (ext)
+                    hipLaunchKernelGGL((decode_split_kernel<DD, false, true, true>), grid, dim3(kThreads), 0, stream, a);
+                else
+                    hipLaunchKernelGGL((decode_split_kernel<DD, false, false, true>), grid, dim3(kThreads), 0, stream, a);
                 return;
             }
         }

@@ -325,6 +325,23 @@ int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache, con
                     void *stream);
 
 /*
+ * attn_decode_fp8_ext -- attn_decode_fp8 with the sliding window and the logit
+ * soft-cap of attn_decode_ext (window_left: the query, token L-1, also needs
+ * token j >= L-1-window_left, -1 = none; softcap > 0 caps each scaled score
+ * s = scale * descale_k * <q, k8> at softcap * tanh(s / softcap), 0 = none; the
+ * variants of the pofe.ai page's section "Interaction with post-trained
+ * models").  With window_left = -1 and softcap = 0 the attn_decode_fp8 kernel
+ * runs (bit for bit).  Every other argument, the workspace, the limits and the
+ * errors are those of attn_decode_fp8; window_left below -1 or a negative or
+ * non-finite softcap is ATTN_ERR_SHAPE.
+ */
+int attn_decode_fp8_ext(const void *q, const void *k_cache, const void *v_cache, const float *descale_k_or_null,
+                        const float *descale_v_or_null, const int32_t *block_table, const int32_t *seq_lens, void *o,
+                        float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,
+                        int max_blocks_per_seq, float scale, int window_left, float softcap, int chunk_tokens,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * attn_decode_chunk_tokens -- the chunk size attn_decode uses for these
  * arguments (resolves chunk_tokens == 0), or a negative status.
  */

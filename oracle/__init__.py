@@ -335,9 +335,10 @@ def prefill_fp8_varlen(q8, k8, v8, descale_q, descale_k, descale_v, cu_seqlens, 
 
 
 def decode_fp8(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, scale: float,
-               page_size: int, max_blocks: int):
+               page_size: int, max_blocks: int, window: int = -1, softcap: float = 0.0):
     """Decode over an E4M3 cache: sequence b reads descale_k[b, hk] * decode(k8) and
-    descale_v[b, hk] * decode(v8) for KV head hk (None = 1), then the plain decode."""
+    descale_v[b, hk] * decode(v8) for KV head hk (None = 1), then the plain decode
+    (with decode's window and soft-cap, the cap acting on scale * <q, K>)."""
     k, v = e4m3_decode(k_cache8), e4m3_decode(v_cache8)
     qq = _f64(q)
     B, Hkv = qq.shape[0], k.shape[-2]
@@ -353,10 +354,11 @@ def decode_fp8(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_len
         if bt is None:  # contiguous [B, S, Hkv, d]: this sequence's rows only
             kb = k[b:b + 1] * dk[b][None, None, :, None]
             vb = v[b:b + 1] * dv[b][None, None, :, None]
-            ob, lb = decode(qq[b:b + 1], kb, vb, None, sl[b:b + 1], scale, page_size, max_blocks)
+            ob, lb = decode(qq[b:b + 1], kb, vb, None, sl[b:b + 1], scale, page_size, max_blocks, window, softcap)
         else:  # paged pool [pages, P, Hkv, d] through this sequence's table row
             kb = k * dk[b][None, None, :, None]
             vb = v * dv[b][None, None, :, None]
-            ob, lb = decode(qq[b:b + 1], kb, vb, bt[b:b + 1], sl[b:b + 1], scale, page_size, max_blocks)
+            ob, lb = decode(qq[b:b + 1], kb, vb, bt[b:b + 1], sl[b:b + 1], scale, page_size, max_blocks, window,
+                            softcap)
         o[b], lse[b] = ob[0], lb[0]
     return o, lse

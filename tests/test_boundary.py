@@ -361,3 +361,24 @@ def prefill_fp8_ext(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dq=0, dk=0, dv=0, 
 ])
 def test_prefill_fp8_ext_argument_errors(kw, code):
     assert prefill_fp8_ext(**kw) == code
+
+
+def decode_fp8_ext(q=FAKE, kc=FAKE, vc=FAKE, dk=0, dv=0, bt=FAKE, sl=FAKE, o=FAKE, lse=0, B=2, Hq=8, Hkv=2, d=128,
+                   page=16, mb=8, window=16, cap=10.0, chunk=0, ws=FAKE, wsb=1 << 30):
+    return attn.lib.attn_decode_fp8_ext(P(q), P(kc), P(vc), P(dk), P(dv), P(bt), P(sl), P(o), P(lse), B, Hq, Hkv, d,
+                                        page, mb, 0.1, window, cap, chunk, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-2), attn.ATTN_ERR_SHAPE),
+    (dict(cap=-0.5), attn.ATTN_ERR_SHAPE),
+    (dict(cap=float("inf")), attn.ATTN_ERR_SHAPE),
+    (dict(q=0), attn.ATTN_ERR_NULL),
+    (dict(ws=0), attn.ATTN_ERR_WORKSPACE),
+    (dict(wsb=16), attn.ATTN_ERR_WORKSPACE),
+    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(dk=FAKE + 2), attn.ATTN_ERR_ALIGN),
+    (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
+])
+def test_decode_fp8_ext_argument_errors(kw, code):
+    assert decode_fp8_ext(**kw) == code

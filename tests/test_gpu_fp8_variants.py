@@ -133,3 +133,39 @@ def test_fp8_window_softcap_long_sampled_rows(attn):
     rows = np.arange(0, N, step)
     check_fp8("fp8 ext 8k (sampled)", o[:, :, rows], lse[:, :, rows], ro[:, :, rows], rl[:, :, rows],
               padded_bounds(x, window, softcap, rows))
+
+
+# ------------------------------------------------------------------ decode over an E4M3 cache
+DEC_LENS = [1, 15, 16, 17, 100, 511, 513, 1000]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("window,softcap", [(0, 0.0), (40, 0.0), (300, 0.0), (-1, 15.0), (100, 5.0)])
+def test_fp8_cache_decode_window_softcap(attn, d, paged, window, softcap):
+    """The E4M3 codes convert to bf16 exactly and the descales fold into the scale (the
+    cap acts on the descaled score), so the bf16 decode's bars hold: 2e-2 on O, 1e-3 on LSE."""
+    from gpu_common import BF16_TOL, check
+    say("case: fp8-cache decode d=%d paged=%s window=%d softcap=%g" % (d, paged, window, softcap))
+    x = W.decode_fp8_inputs(4300 + d + window, len(DEC_LENS), 8, 2, d, DEC_LENS, 1024, paged)
+    o, lse = attn.decode_fp8(dev(x.q), dev(x.k_cache8), dev(x.v_cache8), dev(x.block_table), dev(x.seq_lens),
+                             x.page_size, x.max_blocks, dev(x.descale_k), dev(x.descale_v), x.scale, 64,
+                             window_left=window, softcap=softcap)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_fp8(x.q, x.k_cache8, x.v_cache8, x.descale_k, x.descale_v, x.block_table, x.seq_lens,
+                               x.scale, x.page_size, x.max_blocks, window=window, softcap=softcap)
+    check("fp8-cache decode d=%d paged=%d w=%d cap=%g" % (d, paged, window, softcap), o, lse, ro, rl, BF16_TOL)
+
+
+def test_fp8_cache_decode_ext_without_options_is_the_plain_kernel(attn):
+    x = W.decode_fp8_inputs(4400, len(DEC_LENS), 8, 2, 128, DEC_LENS, 1024, True)
+    args = (dev(x.q), dev(x.k_cache8), dev(x.v_cache8), dev(x.descale_k), dev(x.descale_v), dev(x.block_table),
+            dev(x.seq_lens))
+    o0, l0 = attn.decode_fp8(args[0], args[1], args[2], args[5], args[6], x.page_size, x.max_blocks, args[3],
+                             args[4], x.scale, 64)
+    ws = torch.empty(attn.attn_decode_workspace_bytes(len(DEC_LENS), 8, 2, 128, x.page_size, x.max_blocks, 64),
+                     dtype=torch.uint8, device="cuda")
+    o1, l1 = torch.empty_like(o0), torch.empty_like(l0)
+    attn.attn_decode_fp8_ext(*args, o1, l1, x.page_size, x.max_blocks, x.scale, -1, 0.0, 64, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
