@@ -805,9 +805,9 @@ constexpr int kCheckThreads = 1024;
 
 __global__ __launch_bounds__(kCheckThreads) void check_tables_kernel(TableCheckParams p)
 {
-    __shared__ unsigned partial[kCheckThreads / 64];
+    __shared__ unsigned long long partial[kCheckThreads / 64];
     const long long cap = (long long)p.max_blocks * p.page_size;
-    unsigned bad = 0;
+    unsigned long long bad = 0;  // 64-bit: a table may hold more than 2^32 entries
     for (int b = threadIdx.x; b < p.B; b += kCheckThreads) {
         const long long need = (long long)p.seq_lens[b] + p.appended;
         if (p.seq_lens[b] < 0 || need > cap) ++bad;
