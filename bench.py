@@ -150,7 +150,7 @@ def cpu_baseline(x, target_s: float):
     t0 = time.perf_counter()
     oracle.prefill(q, k, v, True, x.scale, row_step=step)
     dt = time.perf_counter() - t0
-    return {"value": sample_flop(step) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    return {"value": sample_flop(step) / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads_used(),
             "kind": "oracle",
             "sample": "fp64 plain-definition oracle on every %d-th query row of all 28 heads of the "
                       "N=16384 causal prefill (%.1f GFLOP, %.1f s wall)" % (step, sample_flop(step) / 1e9, dt)}
@@ -168,6 +168,15 @@ def host_cpu() -> str:
     return ""
 
 
+def host_info() -> dict:
+    """What the CPU baseline ran on: the CPU model, the logical CPUs the kernel
+    reports (nproc), the ones this process may run on (its affinity mask) and the
+    threads the oracle's parallel regions actually use."""
+    import oracle
+    return {"cpu_model": host_cpu(), "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "oracle_threads": oracle.threads_used()}
+
+
 def cpu_baseline_decode(dx, nbytes: int):
     """The fp64 oracle, as it stands, on the whole 32k-token decode (one call)."""
     import oracle
@@ -177,7 +186,7 @@ def cpu_baseline_decode(dx, nbytes: int):
         oracle.decode(q, kc, vc, dx.block_table, dx.seq_lens, dx.scale, dx.page_size, dx.max_blocks)
         calls += 1
     dt = (time.perf_counter() - t0) / calls
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": oracle.threads_used(), "kind": "oracle",
             "sample": "fp64 plain-definition oracle on the whole decode (all 28 heads, 32768 cached tokens; "
                       "the cache converted to float64 beforehand), %d calls, %.1f ms each, bytes counted as "
                       "the bf16 cache's" % (calls, dt * 1e3)}
@@ -248,7 +257,7 @@ def oracle_table(configs, budget_s: float, threads: int = 0):
             raise SystemExit("unknown workload %r" % c)
         rows[c]["elapsed_s"] = round(time.perf_counter() - t_setup, 1)  # generation, conversion and timing
         print("oracle %s: %s" % (c, json.dumps(rows[c])), file=sys.stderr, flush=True)
-    return {"threads": oracle.num_threads(), "host_cpu": host_cpu(), "workloads": rows}
+    return {"threads": oracle.threads_used(), "host": host_info(), "workloads": rows}
 
 
 def main():
@@ -456,7 +465,7 @@ def main():
         out["fp8_decode"] = fp8_dec
     if do_p and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(px, args.cpu_seconds)
-        out["cpu_baseline"]["host_cpu"] = host_cpu()
+        out["cpu_baseline"]["host"] = host_info()
     if do_d and not args.no_cpu_baseline:
         out["decode"]["cpu_baseline"] = cpu_baseline_decode(dx, decode_bytes)
     print(json.dumps(out), flush=True)

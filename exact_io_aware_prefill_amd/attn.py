@@ -8,6 +8,7 @@ the library has not been built (python -m exact_io_aware_prefill_amd.build).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -284,21 +285,22 @@ def attn_decode_fp8_ext(q, k_cache8, v_cache8, descale_k, descale_v, block_table
 def decode_fp8(q, k_cache8, v_cache8, block_table, seq_lens, page_size: int, max_blocks_per_seq: int,
                descale_k=None, descale_v=None, scale: float | None = None, chunk_tokens: int = 0, stream=None,
                workspace=None, window_left: int = -1, softcap: float = 0.0):
-    B, Hq, d = q.shape
-    Hkv = k_cache8.shape[-2]
-    need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    scale = d ** -0.5 if scale is None else scale
-    if _plain(window_left, softcap):
-        attn_decode_fp8(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, o, lse, page_size,
-                        max_blocks_per_seq, scale, chunk_tokens, workspace, stream)
-    else:
-        attn_decode_fp8_ext(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, o, lse, page_size,
-                            max_blocks_per_seq, scale, window_left, softcap, chunk_tokens, workspace, stream)
-    return o, lse
+    with _on(stream):
+        B, Hq, d = q.shape
+        Hkv = k_cache8.shape[-2]
+        need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        scale = d ** -0.5 if scale is None else scale
+        if _plain(window_left, softcap):
+            attn_decode_fp8(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, o, lse, page_size,
+                            max_blocks_per_seq, scale, chunk_tokens, workspace, stream)
+        else:
+            attn_decode_fp8_ext(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, o, lse, page_size,
+                                max_blocks_per_seq, scale, window_left, softcap, chunk_tokens, workspace, stream)
+        return o, lse
 
 
 def attn_lse_combine(o_parts, lse_parts, n_splits, o, lse, stream=None) -> None:
@@ -322,64 +324,80 @@ def attn_decode_check_tables(block_table, seq_lens, page_size: int, max_blocks_p
     _check(rc, "attn_decode_check_tables")
 
 # ---- conveniences that allocate outputs with PyTorch (allocation only) ----------
+# Outputs and the decode workspace are allocated on the stream the kernels run on,
+# so PyTorch's caching allocator orders any reuse of that memory (in particular of
+# the temporary workspace, released when the function returns) after the launch.
 def _plain(window_left, softcap) -> bool:
     return window_left == -1 and softcap == 0.0
 
 
+def _on(stream):
+    """Allocation context for a launch on `stream` (None: the current stream)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
+
+
 def prefill(q, k, v, causal: bool = True, scale: float | None = None, stream=None, window_left: int = -1,
             softcap: float = 0.0):
-    B, Hq, N, d = q.shape
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    scale = d ** -0.5 if scale is None else scale
-    if _plain(window_left, softcap):
-        attn_prefill(q, k, v, o, lse, causal, scale, stream)
-    else:
-        attn_prefill_ext(q, k, v, o, lse, None, N, causal, scale, window_left, softcap, stream)
-    return o, lse
+    with _on(stream):
+        B, Hq, N, d = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        scale = d ** -0.5 if scale is None else scale
+        if _plain(window_left, softcap):
+            attn_prefill(q, k, v, o, lse, causal, scale, stream)
+        else:
+            attn_prefill_ext(q, k, v, o, lse, None, N, causal, scale, window_left, softcap, stream)
+        return o, lse
 
 
 def prefill_varlen(q, k, v, cu_seqlens, max_seqlen: int, causal: bool = True, scale: float | None = None,
                    stream=None, window_left: int = -1, softcap: float = 0.0):
-    T, Hq, d = q.shape
-    o = torch.empty_like(q)
-    lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    scale = d ** -0.5 if scale is None else scale
-    if _plain(window_left, softcap):
-        attn_prefill_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, scale, stream)
-    else:
-        attn_prefill_ext(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, scale, window_left, softcap, stream)
-    return o, lse
+    with _on(stream):
+        T, Hq, d = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+        scale = d ** -0.5 if scale is None else scale
+        if _plain(window_left, softcap):
+            attn_prefill_varlen(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, scale, stream)
+        else:
+            attn_prefill_ext(q, k, v, o, lse, cu_seqlens, max_seqlen, causal, scale, window_left, softcap, stream)
+        return o, lse
 
 
 def prefill_fp8(q8, k8, v8, descale_q=None, descale_k=None, descale_v=None, causal: bool = True,
                 scale: float | None = None, stream=None, window_left: int = -1, softcap: float = 0.0):
-    B, Hq, N, d = q8.shape
-    o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device)
-    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
-    scale = d ** -0.5 if scale is None else scale
-    if _plain(window_left, softcap):
-        attn_prefill_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, scale, stream)
-    else:
-        attn_prefill_fp8_ext(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, None, N, causal, scale, window_left,
-                             softcap, stream)
-    return o, lse
+    with _on(stream):
+        B, Hq, N, d = q8.shape
+        o = torch.empty((B, Hq, N, d), dtype=torch.bfloat16, device=q8.device)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q8.device)
+        scale = d ** -0.5 if scale is None else scale
+        if _plain(window_left, softcap):
+            attn_prefill_fp8(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, causal, scale, stream)
+        else:
+            attn_prefill_fp8_ext(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, None, N, causal, scale, window_left,
+                                 softcap, stream)
+        return o, lse
 
 
 def prefill_fp8_varlen(q8, k8, v8, cu_seqlens, max_seqlen: int, descale_q=None, descale_k=None, descale_v=None,
                        causal: bool = True, scale: float | None = None, stream=None, window_left: int = -1,
                        softcap: float = 0.0):
-    T, Hq, d = q8.shape
-    o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=q8.device)
-    lse = torch.empty((Hq, T), dtype=torch.float32, device=q8.device)
-    scale = d ** -0.5 if scale is None else scale
-    if _plain(window_left, softcap):
-        attn_prefill_fp8_varlen(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen, causal,
-                                scale, stream)
-    else:
-        attn_prefill_fp8_ext(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen, causal,
-                             scale, window_left, softcap, stream)
-    return o, lse
+    with _on(stream):
+        T, Hq, d = q8.shape
+        o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=q8.device)
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q8.device)
+        scale = d ** -0.5 if scale is None else scale
+        if _plain(window_left, softcap):
+            attn_prefill_fp8_varlen(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen, causal,
+                                    scale, stream)
+        else:
+            attn_prefill_fp8_ext(q8, k8, v8, o, lse, descale_q, descale_k, descale_v, cu_seqlens, max_seqlen, causal,
+                                 scale, window_left, softcap, stream)
+        return o, lse
 
 
 def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, page_size: int,
@@ -387,38 +405,40 @@ def decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens,
                   workspace=None, window_left: int = -1, softcap: float = 0.0):
     """Decode step with the new token's k_new, v_new [B, Hkv, d] written into the caches
     in place at token cache_seqlens[b]; returns (o, lse) over cache_seqlens[b] + 1 tokens."""
-    B, Hq, d = q.shape
-    Hkv = k_cache.shape[-2]
-    need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    scale = d ** -0.5 if scale is None else scale
-    if _plain(window_left, softcap):
-        attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse, page_size,
-                           max_blocks_per_seq, scale, chunk_tokens, workspace, stream)
-    else:
-        attn_decode_ext(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse, page_size,
-                        max_blocks_per_seq, scale, window_left, softcap, chunk_tokens, workspace, stream)
-    return o, lse
+    with _on(stream):
+        B, Hq, d = q.shape
+        Hkv = k_cache.shape[-2]
+        need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        scale = d ** -0.5 if scale is None else scale
+        if _plain(window_left, softcap):
+            attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse, page_size,
+                               max_blocks_per_seq, scale, chunk_tokens, workspace, stream)
+        else:
+            attn_decode_ext(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse, page_size,
+                            max_blocks_per_seq, scale, window_left, softcap, chunk_tokens, workspace, stream)
+        return o, lse
 
 
 def decode(q, k_cache, v_cache, block_table, seq_lens, page_size: int, max_blocks_per_seq: int,
            scale: float | None = None, chunk_tokens: int = 0, stream=None, workspace=None, window_left: int = -1,
            softcap: float = 0.0):
-    B, Hq, d = q.shape
-    Hkv = k_cache.shape[-2]
-    need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    scale = d ** -0.5 if scale is None else scale
-    if _plain(window_left, softcap):
-        attn_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, page_size, max_blocks_per_seq, scale,
-                    chunk_tokens, workspace, stream)
-    else:
-        attn_decode_ext(q, None, None, k_cache, v_cache, block_table, seq_lens, o, lse, page_size,
-                        max_blocks_per_seq, scale, window_left, softcap, chunk_tokens, workspace, stream)
-    return o, lse
+    with _on(stream):
+        B, Hq, d = q.shape
+        Hkv = k_cache.shape[-2]
+        need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        scale = d ** -0.5 if scale is None else scale
+        if _plain(window_left, softcap):
+            attn_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, page_size, max_blocks_per_seq, scale,
+                        chunk_tokens, workspace, stream)
+        else:
+            attn_decode_ext(q, None, None, k_cache, v_cache, block_table, seq_lens, o, lse, page_size,
+                            max_blocks_per_seq, scale, window_left, softcap, chunk_tokens, workspace, stream)
+        return o, lse

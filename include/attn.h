@@ -349,9 +349,17 @@ int attn_decode_chunk_tokens(int batch, int n_kv_heads, int page_size, int max_b
                              int chunk_tokens);
 
 /*
- * attn_decode_workspace_bytes -- bytes of workspace attn_decode needs:
- * batch * n_q_heads * ceil(max_blocks_per_seq*page_size / chunk) * (head_dim + 1) * 4
- * (partials are float32), or 0 if the arguments are invalid.
+ * attn_decode_workspace_bytes -- bytes of device workspace the split-KV decode
+ * needs for its per-chunk partials: each chunk of a sequence's keys yields a
+ * normalised partial output and its log-sum-exp, which the separate combine then
+ * merges (pofe.ai page, section "Decode: a different bottleneck").  The size is
+ *   batch * n_q_heads * ceil(max_blocks_per_seq * page_size / chunk) * (head_dim + 1) * 4
+ * (partials are float32), where chunk is the chunk size attn_decode resolves for
+ * the same arguments (attn_decode_chunk_tokens); 0 if the arguments are invalid.
+ * The arguments are those of attn_decode that fix the chunk count: the capacity
+ * max_blocks_per_seq * page_size bounds every sequence's length, and n_kv_heads
+ * and page_size enter the automatic chunk choice (chunk_tokens == 0).  Pure host
+ * function: no HIP call, callable without a GPU.
  */
 size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int head_dim,
                                    int page_size, int max_blocks_per_seq, int chunk_tokens);

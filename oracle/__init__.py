@@ -63,12 +63,13 @@ def _load():
         lib.oracle_online_trace.argtypes = [P, P, i, i, P, P, P, P, P, P]
         lib.oracle_num_threads.argtypes = []
         lib.oracle_set_num_threads.argtypes = [i]
+        lib.oracle_threads_used.argtypes = []
         lib.oracle_e4m3_decode.argtypes = [P, P, ctypes.c_int64]
         lib.oracle_e4m3_decode.restype = ctypes.c_int
         for f in (lib.oracle_prefill, lib.oracle_prefill_ext, lib.oracle_decode_ext,
                   lib.oracle_prefill_tiled, lib.oracle_decode,
                   lib.oracle_split_decode, lib.oracle_lse_combine, lib.oracle_online_trace,
-                  lib.oracle_num_threads, lib.oracle_set_num_threads):
+                  lib.oracle_num_threads, lib.oracle_set_num_threads, lib.oracle_threads_used):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -93,6 +94,11 @@ def _p(a):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def threads_used() -> int:
+    """Threads one of the oracle's parallel regions actually runs with."""
+    return int(_load().oracle_threads_used())
 
 
 def set_num_threads(n: int) -> int:

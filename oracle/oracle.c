@@ -46,6 +46,22 @@
 #include <omp.h>
 #endif
 
+/* Threads of every parallel loop below: 0 = the OpenMP runtime's default.  The   */
+/* count is passed to each parallel region explicitly (num_threads clause), so a */
+/* request holds even where the process carries more than one OpenMP runtime     */
+/* (the calling thread's settings would then live in the other one).  Results do */
+/* not depend on it: every row or sequence is computed by one thread.            */
+static int g_threads = 0;
+
+static int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return g_threads > 0 ? g_threads : omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* The plain definition for one query row (two passes, no rescaling) over    */
 /* the keys j0 .. n-1.  Keys/values are rows of d doubles, `stride` doubles  */
@@ -106,7 +122,7 @@ int oracle_prefill_ext(const double *q, const double *k, const double *v,
     const int g = Hq / Hkv;
     const int64_t rows = (int64_t)B * Hq * N;
     int err = 0;
-#pragma omp parallel
+#pragma omp parallel num_threads(oracle_threads())
     {
         double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
         if (!s) {
@@ -183,7 +199,7 @@ int oracle_decode_ext(const double *q, const double *k_cache, const double *v_ca
     for (int b = 0; b < B; ++b)
         if (seq_lens[b] < 0 || seq_lens[b] > cap) return -1;
     int err = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(oracle_threads())
     for (int64_t bk = 0; bk < (int64_t)B * Hkv; ++bk) {
         const int b = (int)(bk / Hkv), hk = (int)(bk % Hkv);
         const int64_t len = seq_lens[b];
@@ -313,7 +329,7 @@ int oracle_prefill_tiled(const double *q, const double *k, const double *v,
     const int ntiles = (N + Br - 1) / Br;
     const int64_t work = (int64_t)B * Hq * ntiles;
     int err = 0;
-#pragma omp parallel
+#pragma omp parallel num_threads(oracle_threads())
     {
         row_state *st = (row_state *)malloc(sizeof(row_state) * (size_t)Br);
         double *ot = (double *)malloc(sizeof(double) * (size_t)Br * d);
@@ -431,7 +447,7 @@ int oracle_split_decode(const double *q, const double *k_cache, const double *v_
     for (int b = 0; b < B; ++b)
         if (seq_lens[b] < 0 || seq_lens[b] > cap) return -1;
     int err = 0;
-#pragma omp parallel for schedule(dynamic, 1)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(oracle_threads())
     for (int64_t bk = 0; bk < (int64_t)B * Hkv; ++bk) {
         const int b = (int)(bk / Hkv), hk = (int)(bk % Hkv);
         const int64_t len = seq_lens[b];
@@ -521,15 +537,26 @@ int oracle_e4m3_decode(const uint8_t *in, double *out, int64_t n)
  * for a single-core timing; returns the count now in effect. */
 int oracle_set_num_threads(int n)
 {
-    if (n > 0) omp_set_num_threads(n);
-    return omp_get_max_threads();
+    if (n > 0) g_threads = n;
+    return oracle_threads();
 }
 
 int oracle_num_threads(void)
 {
+    return oracle_threads();
+}
+
+/* Threads a parallel region of the oracle actually runs with (the runtime may */
+/* grant fewer than requested). */
+int oracle_threads_used(void)
+{
+    int used = 1;
 #ifdef _OPENMP
-    return omp_get_max_threads();
-#else
-    return 1;
+#pragma omp parallel num_threads(oracle_threads())
+    {
+#pragma omp single
+        used = omp_get_num_threads();
+    }
 #endif
+    return used;
 }

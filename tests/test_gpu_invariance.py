@@ -147,3 +147,31 @@ def test_launches_follow_the_callers_stream(attn):
     side.synchronize()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
     assert torch.equal(d0, d1) and torch.equal(m0, m1)
+
+
+def test_stream_argument_without_stream_context(attn):
+    """stream= names a side stream while the current stream stays the default one: the
+    outputs and the decode workspace are allocated on the side stream, so memory that
+    the current stream allocates and fills right after the calls (before any
+    synchronisation) cannot be the memory the kernels still use."""
+    say("case: stream= without a stream context")
+    x = W.prefill_inputs(73, 1, 8, 2, 700, 128, W.BF16)
+    y = W.decode_paged_inputs(74, 3, 8, 2, 128, 16, 1, 900, lengths=[900, 17, 512])
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    args = (dev(y.q), dev(y.k_cache), dev(y.v_cache), dev(y.block_table), dev(y.seq_lens), y.page_size,
+            y.max_blocks, y.scale, 64)
+    o0, l0 = attn.prefill(q, k, v, True, x.scale)
+    d0, m0 = attn.decode(*args)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        o1, l1 = attn.prefill(q, k, v, True, x.scale, stream=side)
+        d1, m1 = attn.decode(*args, stream=side)
+        # the current stream allocates and overwrites memory while the side stream runs
+        junk = [torch.full((1 << 20,), float("nan"), device="cuda") for _ in range(8)]
+        del junk
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert torch.equal(d0, d1) and torch.equal(m0, m1)

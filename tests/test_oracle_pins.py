@@ -792,6 +792,7 @@ def test_oracle_result_does_not_depend_on_its_thread_count():
         outs = []
         for n in (1, max(2, n0)):
             assert oracle.set_num_threads(n) == n
+            assert oracle.threads_used() == n  # the request holds in the parallel regions
             o, l = oracle.prefill(x.q, x.k, x.v, True, x.scale)
             od, ld = oracle.decode(y.q, y.k_cache, y.v_cache, y.block_table, y.seq_lens, y.scale,
                                    y.page_size, y.max_blocks)
