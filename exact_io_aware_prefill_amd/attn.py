@@ -28,12 +28,13 @@ ATTN_ERR_UNSUPPORTED = -4
 ATTN_ERR_WORKSPACE = -5
 ATTN_ERR_ALIGN = -6
 ATTN_ERR_HIP = -7
+ATTN_ERR_SCRATCH = -8
 ATTN_F32 = 0
 ATTN_BF16 = 1
 
 EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_ext", "attn_prefill_fp8", "attn_prefill_fp8_varlen",
            "attn_prefill_fp8_ext",
-           "attn_decode", "attn_decode_append", "attn_decode_ext", "attn_decode_fp8", "attn_decode_fp8_ext",
+           "attn_decode", "attn_decode_noalloc", "attn_decode_append", "attn_decode_ext", "attn_decode_fp8", "attn_decode_fp8_ext",
            "attn_decode_chunk_tokens",
            "attn_decode_workspace_bytes", "attn_lse_combine", "attn_decode_check_tables", "attn_status_string")
 
@@ -66,6 +67,8 @@ lib.attn_decode_fp8_ext.restype = _I
 lib.attn_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                             _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode.restype = _I
+lib.attn_decode_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P]
+lib.attn_decode_noalloc.restype = _I
 lib.attn_decode_append.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                                    _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode_append.restype = _I
@@ -218,6 +221,22 @@ def attn_decode(q, k_cache, v_cache, block_table, seq_lens, o, lse, page_size: i
                          0 if workspace is None else workspace.numel() * workspace.element_size(),
                          _stream(stream))
     _check(rc, "attn_decode")
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse, page_size: int,
+                        max_blocks_per_seq: int, scale: float, chunk_tokens: int, stream=None) -> None:
+    """attn_decode with the partials in the library's static per-GPU scratch
+    (ATTN_DECODE_NOALLOC_SCRATCH_BYTES) instead of a caller workspace: no device
+    memory is allocated.  Calls that overlap on one GPU race on that scratch."""
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[-2]
+    rc = lib.attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens),
+                                 _ptr(o), _ptr(lse), B, Hq, Hkv, d, int(page_size), int(max_blocks_per_seq),
+                                 _dtype_code(q), float(scale), int(chunk_tokens), _stream(stream))
+    _check(rc, "attn_decode_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # ATTN_DECODE_NOALLOC_SCRATCH_BYTES of include/attn.h
 
 
 def attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse,

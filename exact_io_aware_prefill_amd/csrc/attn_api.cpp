@@ -106,7 +106,7 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
                 int n_q_heads, int n_kv_heads, int head_dim, int page_size, int max_blocks_per_seq, int dtype,
                 float scale, int window_left, float softcap, int chunk_tokens, void *workspace,
                 size_t workspace_bytes, void *stream, bool kv_e4m3 = false, const float *descale_k = nullptr,
-                const float *descale_v = nullptr)
+                const float *descale_v = nullptr, bool static_scratch = false)
 {
     if (batch < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || page_size <= 0 ||
         max_blocks_per_seq <= 0 || chunk_tokens < 0 || !variant_ok(window_left, softcap))
@@ -124,9 +124,13 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
     if (append && (!k_new || !v_new)) return ATTN_ERR_NULL;
     const size_t need = attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
                                                     page_size, max_blocks_per_seq, chunk_tokens);
-    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (static_scratch) {
+        if (need > attn::kNoAllocScratchBytes) return ATTN_ERR_SCRATCH;
+    } else if (!workspace || workspace_bytes < need) {
+        return ATTN_ERR_WORKSPACE;
+    }
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
-        !aligned16(workspace) || (lse_or_null && !aligned16(lse_or_null)) ||
+        (!static_scratch && !aligned16(workspace)) || (lse_or_null && !aligned16(lse_or_null)) ||
         (append && (!aligned16(k_new) || !aligned16(v_new))) ||
         (reinterpret_cast<uintptr_t>(descale_k) & 3u) != 0 || (reinterpret_cast<uintptr_t>(descale_v) & 3u) != 0)
         return ATTN_ERR_ALIGN;
@@ -135,6 +139,8 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
     if (max_chunks > attn::kMaxSplits || max_chunks * n_kv_heads > attn::kMaxSplitWorkgroups ||
         batch > 65535 || (long long)batch * n_q_heads > attn::kMaxCombineRows)
         return ATTN_ERR_UNSUPPORTED;
+    // every host check has passed: only now look up this GPU's static scratch
+    if (static_scratch && attn::decode_scratch(&workspace) != hipSuccess) return ATTN_ERR_HIP;
 
     attn::DecodeParams p;
     p.q = q; p.k_cache = k_cache; p.v_cache = v_cache;
@@ -198,6 +204,7 @@ const char *attn_status_string(int status)
     case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    case ATTN_ERR_SCRATCH: return "the decode's partials exceed the static scratch of attn_decode_noalloc";
     default: return "unknown status";
     }
 }
@@ -331,6 +338,16 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
     return decode_impl(false, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, o, lse_or_null, batch,
                        n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale, -1, 0.f,
                        chunk_tokens, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int32_t *block_table,
+                        const int32_t *seq_lens, void *o, float *lse_or_null, int batch, int n_q_heads,
+                        int n_kv_heads, int head_dim, int page_size, int max_blocks_per_seq, int dtype, float scale,
+                        int chunk_tokens, void *stream)
+{
+    return decode_impl(false, q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, o, lse_or_null, batch,
+                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, dtype, scale, -1, 0.f,
+                       chunk_tokens, nullptr, 0, stream, false, nullptr, nullptr, true);
 }
 
 int attn_decode_append(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,

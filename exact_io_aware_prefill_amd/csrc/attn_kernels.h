@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn.h"
+
 namespace attn {
 
 // Tiled prefill, bf16 inputs on matrix cores (prefill_bf16.hip).
@@ -92,6 +94,11 @@ struct TableCheckParams {
     int32_t *bad_out;            // one int32, overwritten
 };
 hipError_t launch_check_tables(const TableCheckParams &p, hipStream_t stream);
+// Device scratch of attn_decode_noalloc: the address of this GPU's static
+// array (looked up once per device, with that device current).
+constexpr size_t kNoAllocScratchBytes = ATTN_DECODE_NOALLOC_SCRATCH_BYTES;
+hipError_t decode_scratch(void **out);
+
 // Decode tiling constants the host front end needs for validation/sizing.
 constexpr int kDecodeMaxGroup = 16;  // largest supported n_q_heads / n_kv_heads
 constexpr int kDecodeTokenQuantum = 16;  // chunk sizes are multiples of this

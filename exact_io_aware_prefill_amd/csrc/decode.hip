@@ -52,6 +52,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "attn_kernels.h"
@@ -836,6 +837,28 @@ __global__ __launch_bounds__(kCheckThreads) void check_tables_kernel(TableCheckP
 }
 
 }  // namespace
+
+// Partials of attn_decode_noalloc: one static array per GPU, alive until the process
+// ends.  Host code never passes its name to a kernel (on the host the name is only a
+// stand-in); it passes the device address looked up below.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t decode_scratch(void **out)
+{
+    constexpr int kMaxDevices = 64;
+    static std::once_flag once[kMaxDevices];
+    static void *addr[kMaxDevices];
+    static hipError_t status[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    // once per device, with that device current (each GPU holds its own copy)
+    std::call_once(once[dev], [&] { status[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch)); });
+    if (status[dev] != hipSuccess) return status[dev];
+    *out = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_check_tables(const TableCheckParams &p, hipStream_t stream)
 {

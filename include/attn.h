@@ -28,6 +28,8 @@
  *     "The bottleneck it attacks");
  *   - attn_prefill_fp8_varlen: the FP8 prefill over a packed batch;
  *   - attn_decode_fp8: the decode over an FP8 (E4M3) KV cache;
+ *   - attn_decode_noalloc: attn_decode with its partials in a static device
+ *     array, for callers that cannot allocate;
  *   - attn_lse_combine: that reduction on its own -- the combine rule for
  *     independent partials, a softmax over the partials' log-sum-exps
  *     (section "The online softmax, with every symbol defined" and the
@@ -36,7 +38,9 @@
  * Conventions shared by every entry point
  *   - Every tensor argument is a DEVICE pointer owned by the caller; the
  *     library allocates nothing, keeps no state between calls and is safe to
- *     call from several host threads.  Tensors are dense, row-major, with the
+ *     call from several host threads.  (One exception: attn_decode_noalloc keeps
+ *     its partials in a static per-GPU device array, so its calls that overlap
+ *     on one GPU race; see there.)  Tensors are dense, row-major, with the
  *     layouts stated per call, and must be 16-byte aligned.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     null stream).  Nothing synchronises with the host.
@@ -79,6 +83,7 @@ extern "C" {
 #define ATTN_ERR_WORKSPACE   -5  /* workspace NULL or smaller than required             */
 #define ATTN_ERR_ALIGN       -6  /* a tensor pointer is not 16-byte aligned             */
 #define ATTN_ERR_HIP         -7  /* the HIP runtime reported an error at launch          */
+#define ATTN_ERR_SCRATCH     -8  /* attn_decode_noalloc: partials exceed its static scratch */
 
 /* ---- element types ----------------------------------------------------- */
 #define ATTN_F32  0  /* IEEE binary32                                   */
@@ -265,6 +270,33 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
                 float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim,
                 int page_size, int max_blocks_per_seq, int dtype, float scale,
                 int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The per-chunk partials go to a static device
+ * array of ATTN_DECODE_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU,
+ * which each GPU the library runs on holds until the process ends; its address is
+ * looked up once per device (with that device current) on the first call there.
+ * The call allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ *
+ *   Arguments, layouts, arithmetic, limits and results are those of attn_decode
+ *   (the same kernels run; the outputs are bit for bit those of attn_decode).
+ *   A call whose partials, attn_decode_workspace_bytes(batch, n_q_heads,
+ *   n_kv_heads, head_dim, page_size, max_blocks_per_seq, chunk_tokens), exceed
+ *   ATTN_DECODE_NOALLOC_SCRATCH_BYTES is ATTN_ERR_SCRATCH (checked on the host,
+ *   before any HIP call).  The scratch keeps the last call's partials; nothing in
+ *   it needs to start at zero (every partial the combine weighs is written first).
+ *   Calls on one GPU share that GPU's array: calls that may overlap in time (on
+ *   different streams, or from several host threads without ordering) race on it
+ *   and must be serialised by the caller, e.g. by issuing them on one stream.
+ */
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *block_table, const int32_t *seq_lens, void *o,
+                        float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim,
+                        int page_size, int max_blocks_per_seq, int dtype, float scale,
+                        int chunk_tokens, void *stream);
 
 /*
  * attn_decode_append -- attn_decode with the new token's key and value appended

@@ -43,7 +43,7 @@ def test_status_codes_match_header():
                  "ATTN_ERR_WORKSPACE", "ATTN_ERR_ALIGN", "ATTN_ERR_HIP", "ATTN_F32", "ATTN_BF16"):
         m = re.search(r"#define\s+%s\s+(-?\d+)" % name, text)
         assert m and int(m.group(1)) == getattr(attn, name), name
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         s = attn.attn_status_string(code)
         assert s and s != "unknown status"
     assert attn.attn_status_string(-99) == "unknown status"
@@ -382,3 +382,28 @@ def decode_fp8_ext(q=FAKE, kc=FAKE, vc=FAKE, dk=0, dv=0, bt=FAKE, sl=FAKE, o=FAK
 ])
 def test_decode_fp8_ext_argument_errors(kw, code):
     assert decode_fp8_ext(**kw) == code
+
+
+def test_decode_noalloc_host_checks():
+    """attn_decode_noalloc checks its arguments on the host before any HIP call: the
+    argument errors of attn_decode, and ATTN_ERR_SCRATCH when the partials would not
+    fit its static scratch (no workspace argument to grow)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+ATTN_DECODE_NOALLOC_SCRATCH_BYTES\s+\(\(size_t\)(\d+)\s*<<\s*(\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == attn.NOALLOC_SCRATCH_BYTES
+    assert re.search(r"#define\s+ATTN_ERR_SCRATCH\s+-8", text) and attn.ATTN_ERR_SCRATCH == -8
+    assert attn.attn_status_string(attn.ATTN_ERR_SCRATCH) != "unknown status"
+
+    def call(B=4, Hq=8, Hkv=2, d=128, page=16, maxb=64, chunk=0, q=FAKE, sl=FAKE):
+        return attn.lib.attn_decode_noalloc(P(q), P(FAKE), P(FAKE), None, P(sl), P(FAKE), None, B, Hq, Hkv, d,
+                                            page, maxb, 1, 0.1, chunk, None)
+    assert call(q=0) == attn.ATTN_ERR_NULL
+    assert call(Hq=6, Hkv=4) == attn.ATTN_ERR_GQA
+    assert call(d=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert call(B=0) == attn.ATTN_OK
+    # 4096 x 32 rows x one 16-token chunk x 129 floats = 67.6 MB > 16 MiB
+    assert attn.attn_decode_workspace_bytes(4096, 32, 8, 128, 16, 1, 16) > attn.NOALLOC_SCRATCH_BYTES
+    assert call(B=4096, Hq=32, Hkv=8, maxb=1, chunk=16) == attn.ATTN_ERR_SCRATCH
+    # exactly at the limit is accepted by the size check (checked via the workspace formula)
+    rows = attn.NOALLOC_SCRATCH_BYTES // (129 * 4)
+    assert attn.attn_decode_workspace_bytes(rows, 1, 1, 128, 16, 1, 16) <= attn.NOALLOC_SCRATCH_BYTES
