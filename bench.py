@@ -32,7 +32,7 @@ CSRC = os.path.join(ROOT, "exact_io_aware_prefill_amd", "csrc")
 # valid while the kernel source they were taken on is unchanged (sha256 recorded)
 TRAFFIC = {
     "prefill": {"file": os.path.join(ROOT, "profiles", "prefill_bf16_n16384_traffic.json"),
-                "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel<128, false>"},
+                "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel<128, false, 1>"},
     "decode": {"file": os.path.join(ROOT, "profiles", "decode_split_s32768_traffic.json"),
                "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel<128, false, false, false>"},
     "fp8": {"file": os.path.join(ROOT, "profiles", "prefill_fp8_n16384_traffic.json"),
@@ -351,6 +351,43 @@ def main():
         torch.cuda.synchronize()
         dec_bb_ms = e0.elapsed_time(e1) / reps
 
+    # Floor of the decode call, timed the same way (back-to-back, rotating the same KV
+    # copies): one kernel that reads the K and V caches once on the split kernel's
+    # grid (one 256-thread workgroup per (chunk, KV head)), then the same read followed
+    # by an empty dependent launch, the least a two-kernel split + combine can cost.
+    floor = None
+    if do_d:
+        wgs = -(-kcs[0].shape[1] // chunk) * kcs[0].shape[2]
+        sink = torch.zeros(4 * wgs, dtype=torch.int32, device=dev)
+        reps = 5 * args.steps
+
+        def time_calls(fn):
+            for i in range(10):
+                fn(i)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(reps):
+                fn(i)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        def read(i):
+            attn.attn_bench_stream_read(kcs[i % N_KV_COPIES], vcs[i % N_KV_COPIES], wgs, sink)
+
+        def read_and_launch(i):
+            read(i)
+            attn.attn_bench_empty()
+        read_ms = time_calls(read)
+        read2_ms = time_calls(read_and_launch)
+        floor = {"read_ms": read_ms, "read_GBps": decode_bytes / (read_ms * 1e-3) / 1e9,
+                 "read_plus_launch_ms": read2_ms, "workgroups": wgs,
+                 "what": "one kernel reading the decode's K and V caches once (16-byte loads, grid-stride, %d "
+                         "workgroups of 256 threads, the split kernel's grid), then the same read followed by an "
+                         "empty dependent launch; %d back-to-back calls between two events, rotating the %d KV copies"
+                         % (wgs, reps, N_KV_COPIES)}
+
     # FP8 prefill of the same prompt (E4M3 inputs), timed on its own after the step
     fp8 = None
     if args.only in (None, "fp8") and not args.no_fp8:
@@ -448,7 +485,7 @@ def main():
         out["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                            "traffic": measured_traffic("prefill"),
-                           "kernel": "prefill_bf16_kernel<128, false>", "avg_launch_ms": pre_ms,
+                           "kernel": "prefill_bf16_kernel<128, false, 1>", "avg_launch_ms": pre_ms,
                            "algorithmic_flop_per_launch": prefill_flop}
     if do_d:
         gbs = decode_bytes / (dec_bb_ms * 1e-3) / 1e9
@@ -459,6 +496,9 @@ def main():
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode"),
                                       "kernels": "decode_split_kernel<128, false, false, false> + lse_combine_kernel<128>",
                                       "algorithmic_bytes_per_launch": decode_bytes}}
+        if floor is not None:
+            floor["call_over_read_plus_launch"] = dec_bb_ms / floor["read_plus_launch_ms"]
+            out["decode"]["floor"] = floor
     if fp8 is not None:
         out["fp8_prefill"] = fp8
     if fp8_dec is not None:

@@ -82,6 +82,12 @@ lib.attn_lse_combine.argtypes = [_P, _P, _P, _I, _I, _I, _P, _I, _P, _P]
 lib.attn_lse_combine.restype = _I
 lib.attn_status_string.argtypes = [_I]
 lib.attn_status_string.restype = ctypes.c_char_p
+# measurement helpers of include/attn_bench.h (not part of the attention path)
+BENCH_EXPORTS = ("attn_bench_stream_read", "attn_bench_empty")
+lib.attn_bench_stream_read.argtypes = [_P, _P, ctypes.c_size_t, _I, _P, _P]
+lib.attn_bench_stream_read.restype = _I
+lib.attn_bench_empty.argtypes = [_P]
+lib.attn_bench_empty.restype = _I
 
 
 class AttnError(RuntimeError):
@@ -341,6 +347,24 @@ def attn_decode_check_tables(block_table, seq_lens, page_size: int, max_blocks_p
                                       int(max_blocks_per_seq), int(num_blocks), 1 if appended else 0, _ptr(bad_out),
                                       _stream(stream))
     _check(rc, "attn_decode_check_tables")
+
+def attn_bench_stream_read(a, b, workgroups: int, sink, stream=None) -> None:
+    """Read device tensors a and b (same byte size) once in one kernel on `workgroups`
+    workgroups (the floor of a decode that reads them); sink: int32 tensor of at least
+    4 * workgroups elements."""
+    nbytes = a.numel() * a.element_size()
+    assert b.numel() * b.element_size() == nbytes and sink.numel() >= 4 * workgroups
+    rc = lib.attn_bench_stream_read(_ptr(a), _ptr(b), nbytes, int(workgroups), _ptr(sink), _stream(stream))
+    if rc != 0:
+        raise RuntimeError("attn_bench_stream_read failed (%d)" % rc)
+
+
+def attn_bench_empty(stream=None) -> None:
+    """One empty kernel: the cost of a further dependent launch."""
+    rc = lib.attn_bench_empty(_stream(stream))
+    if rc != 0:
+        raise RuntimeError("attn_bench_empty failed (%d)" % rc)
+
 
 # ---- conveniences that allocate outputs with PyTorch (allocation only) ----------
 # Outputs and the decode workspace are allocated on the stream the kernels run on,

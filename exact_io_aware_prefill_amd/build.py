@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "prefill_fp8.hip", "decode.hip"]
+SOURCES = ["attn_api.cpp", "prefill_bf16.hip", "prefill_f32.hip", "prefill_fp8.hip", "decode.hip", "bench_floor.hip"]
 # per-source extra flags: the bf16 and fp8 prefills assume finite inputs so their
 # row max compiles to v_max3_f32 without NaN-quieting copies (infinities stay IEEE)
 EXTRA_FLAGS = {"prefill_bf16.hip": ["-fno-honor-nans"], "prefill_fp8.hip": ["-fno-honor-nans"]}

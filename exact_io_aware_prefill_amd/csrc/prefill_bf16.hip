@@ -296,22 +296,39 @@ __device__ __forceinline__ float soft_cap(float x, float cap, float cap_k)
 }
 
 // EXT selects the variant with a sliding window and logit soft-capping (a separate
-// instantiation, so the plain kernel keeps its instruction schedule).
-template <int D, bool EXT>
-__global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16_kernel(Args a)
+// instantiation, so the plain kernel keeps its instruction schedule).  KS = 2
+// selects the key-split variant for prompts too short to fill the GPU: the
+// workgroup is two groups of 4 waves over the same 128 query rows, group g walks
+// half g of the tile's key range with its own tile buffers and online-softmax
+// state, and group 1 hands its (m, l, acc) to group 0 through LDS at the end,
+// where the two are merged by the combine rule (split-KV inside one workgroup).
+template <int D, bool EXT, int KS = 1>
+__global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : waves_per_simd<D>()) void prefill_bf16_kernel(Args a)
 {
-    constexpr int NT = kWaves * 64;
+    static_assert(KS == 1 || (KS == 2 && !EXT && D <= 128), "key split: plain kernel, d <= 128");
+    // rows may meet tiles with no visible key before any reference exists (window,
+    // or a key group whose range starts past the row): the reference is then taken
+    // on the rare path instead of in the prologue
+    constexpr bool REF = EXT || KS > 1;
+    constexpr int NT = kWaves * 64;  // threads of one key group
     constexpr int TE = kBlockN * D;  // elements per K or V tile
     // separate LDS objects, so in-flight loads into one buffer do not make the
-    // compiler wait before reading another
-    __shared__ __attribute__((aligned(1024))) uint16_t KB0[TE];
-    __shared__ __attribute__((aligned(1024))) uint16_t KB1[TE];
-    __shared__ __attribute__((aligned(1024))) uint16_t VB0[TE];
-    __shared__ __attribute__((aligned(1024))) uint16_t VB1[TE];
+    // compiler wait before reading another; one set per key group
+    __shared__ __attribute__((aligned(1024))) uint16_t KB0s[KS][TE];
+    __shared__ __attribute__((aligned(1024))) uint16_t KB1s[KS][TE];
+    __shared__ __attribute__((aligned(1024))) uint16_t VB0s[KS][TE];
+    __shared__ __attribute__((aligned(1024))) uint16_t VB1s[KS][TE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
+    const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
+    const int grp = KS > 1 ? wave_wg / kWaves : 0;  // key group
+    const int wave = KS > 1 ? wave_wg % kWaves : wave_wg;  // query block and loader slot in the group
+    const int gtid = KS > 1 ? tid % NT : tid;
+    uint16_t *const KB0 = KB0s[grp];
+    uint16_t *const KB1 = KB1s[grp];
+    uint16_t *const VB0 = VB0s[grp];
+    uint16_t *const VB1 = VB1s[grp];
     const int l32 = lane & 31, hh = lane >> 5;
 
     // ---- work item: (q tile descending, b, kv head, q head), query head fastest ----
@@ -410,17 +427,26 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
     const int kend = a.causal ? min(N, q0 + kBM) : N;  // keys this tile may see
     // with a window, the first tile that holds a key of row q0's window
     const int kbeg = (EXT && a.window >= 0) ? max(0, q0 - a.window) / kBlockN * kBlockN : 0;
-    const int ntiles = (kend - kbeg + kBlockN - 1) / kBlockN;  // >= 1: key q0 is visible to row q0
+    int ntiles = (kend - kbeg + kBlockN - 1) / kBlockN;  // >= 1: key q0 is visible to row q0
+    int gbeg = kbeg;  // first key of this group's tiles
+    if (KS > 1) {
+        // group g takes tiles g*half .. g*half + half - 1; tiles past the range (the
+        // second group's last one when the count is odd) lie past the diagonal or
+        // past N, so the mask hides all their keys and they add nothing
+        const int half = (ntiles + 1) / 2;
+        gbeg = kbeg + grp * half * kBlockN;
+        ntiles = half;
+    }
 
     // ---- prologue ------------------------------------------------------------------
     // V buffers start as zeros: "tile -1" is multiplied by P = 0, and rows past N
     // of a ragged last tile must be finite whether or not the loads write them.
-    for (int i = tid; i < TE / 8; i += NT) {
+    for (int i = gtid; i < TE / 8; i += NT) {
         reinterpret_cast<uint4 *>(VB0)[i] = make_uint4(0, 0, 0, 0);
         reinterpret_cast<uint4 *>(VB1)[i] = make_uint4(0, 0, 0, 0);
     }
-    kld.load(kh, N, kbeg, wave, KB0);
-    if (ntiles > 1) kld.load(kh, N, kbeg + kBlockN, wave, KB1);
+    kld.load(kh, N, gbeg, wave, KB0);
+    if (ntiles > 1) kld.load(kh, N, gbeg + kBlockN, wave, KB1);
     wait_loads();
     __syncthreads();
     f32x16_t S[kBlocks][kKB];
@@ -454,7 +480,7 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
         return fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
     };
     qk_tile<D>(S, KB0, qf, kad);
-    if (!EXT) {
+    if (!REF) {
         // The plain kernel starts from the first tile's true max: every row sees key
         // 0 (causal) or all keys < N, so it is finite, and the steps need no check
         // for a missing reference.  (The variant's soft-cap and window act at the
@@ -477,7 +503,7 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
     // K(t+2) into Kw and V(t) into Vw.
     auto step = [&](bf16x8_t (&Pp)[kBlocks][kKS], bf16x8_t (&Pc)[kBlocks][kKS], int t, const uint16_t *Kn,
                     const uint16_t *Vp, uint16_t *Kw, uint16_t *Vw) {
-        const int k0 = kbeg + t * kBlockN;
+        const int k0 = gbeg + t * kBlockN;
         if (t + 2 < ntiles) kld.load(kh, N, k0 + 2 * kBlockN, wave, Kw);
         vld.load(vh, N, k0, wave, Vw);
         if (EXT && a.cap_raw > 0.f) {  // soft-cap before masking, so masked scores stay -inf
@@ -513,7 +539,7 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
         __builtin_amdgcn_s_setprio(0);
         // ---- rare: some probability may exceed 2^8 (or a row has no reference yet):
         // raise the reference to the true running max, rescale, redo the tile
-        bool redo = EXT && mb[0] == -INFINITY;
+        bool redo = REF && mb[0] == -INFINITY;
 #pragma unroll
         for (int bb = 0; bb < kBlocks; ++bb) redo = redo || rs[bb] > kMaxLaneSum;
         if (__builtin_amdgcn_ballot_w64(redo)) {
@@ -529,7 +555,7 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
                 // c = 0 while mb = -inf.  Only the variant can meet a row with no visible
                 // key yet (mb_new = -inf); its state stays (mb, l, acc) = (-inf, 0, 0),
                 // and a reference of 0 gives the masked scores probability 0.
-                const bool none = EXT && mb_new == -INFINITY;
+                const bool none = REF && mb_new == -INFINITY;
                 const float c = none ? 1.f : __builtin_amdgcn_exp2f(mb[bb] - mb_new);
                 l[bb] *= c;
 #pragma unroll
@@ -569,6 +595,47 @@ __global__ __launch_bounds__(kWaves * 64, waves_per_simd<D>()) void prefill_bf16
         pv_tile<D>(acc, VB0, P0, vad);
     else
         pv_tile<D>(acc, VB1, P1, vad);
+
+    if constexpr (KS > 1) {
+        // group 1 hands its state to group 0 through LDS (the tile buffers are free
+        // once every wave has finished its last product); group 0 merges it by the
+        // combine rule: weights c_g = 2^(m_g - M) with M the larger reference (0 for
+        // a group that saw no key of the row), l = sum c_g l_g, acc = sum c_g acc_g
+        __shared__ float xml[kWaves][2][64];
+        __syncthreads();
+        // wave w of each group uses the w-th tile buffer array (KS * TE elements)
+        static_assert(kWaves == 4 && (D / 32) * 16 * 64 * 4 <= KS * TE * 2, "one exchange slab per wave");
+        uint16_t *const xbuf = wave == 0 ? &KB0s[0][0] : wave == 1 ? &KB1s[0][0] : wave == 2 ? &VB0s[0][0] : &VB1s[0][0];
+        f32x16_t *const slab = reinterpret_cast<f32x16_t *>(xbuf);
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    reinterpret_cast<float4 *>(slab)[(db * 4 + c) * 64 + lane] =
+                        make_float4(acc[0][db][4 * c], acc[0][db][4 * c + 1], acc[0][db][4 * c + 2], acc[0][db][4 * c + 3]);
+            xml[wave][0][lane] = mb[0];
+            xml[wave][1][lane] = l[0];
+        }
+        __syncthreads();
+        if (grp == 1) return;
+        const float m1 = xml[wave][0][lane], l1 = xml[wave][1][lane];
+        const float M = fmaxf(mb[0], m1);
+        const float c0 = mb[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mb[0] - M);
+        const float c1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+        l[0] = c0 * l[0] + c1 * l1;
+        mb[0] = M;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float4 o1 = reinterpret_cast<const float4 *>(slab)[(db * 4 + c) * 64 + lane];
+                acc[0][db][4 * c] = c0 * acc[0][db][4 * c] + c1 * o1.x;
+                acc[0][db][4 * c + 1] = c0 * acc[0][db][4 * c + 1] + c1 * o1.y;
+                acc[0][db][4 * c + 2] = c0 * acc[0][db][4 * c + 2] + c1 * o1.z;
+                acc[0][db][4 * c + 3] = c0 * acc[0][db][4 * c + 3] + c1 * o1.w;
+            }
+    }
 
     // ---- epilogue: O = acc / l, LSE = m * scale + ln l ---------------------------------
 #pragma unroll
@@ -640,13 +707,30 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     const long long rows = (long long)a.n_qtiles * kBM;
     if (rows * a.q_row * 2 > 0xffffffffLL || rows * a.kv_row * 2 > 0xffffffffLL) return hipErrorInvalidValue;
     a.n_items = (int)items;
-    const dim3 grid((unsigned)items), block(kWaves * 64);
+    // Key split for grids that leave the GPU mostly idle: with at most
+    // kSplitMaxItems workgroups (two per compute unit on 256 compute units) the
+    // longest query tiles' key walks set the time, and a second wave group that
+    // takes half of each walk shortens them, at the cost of residency (one 8-wave
+    // workgroup per compute unit; its throughput is about 82% of three 4-wave
+    // ones).  Measured at 28/4 heads, d = 128: +6% at N = 1024, +3.5% at 2048, and
+    // -14% at 3072 (672 workgroups), hence the bound.  Both groups share one
+    // compute unit, so the longest tile's compute unit still does all of that
+    // tile's work, which caps the gain.  Needs at least two query tiles.
+    constexpr long long kSplitMaxItems = 2 * 256;
+    const bool split = !ext && p.head_dim <= 128 && items <= kSplitMaxItems && a.n_qtiles >= 2;
+    const dim3 grid((unsigned)items), block(kWaves * 64 * (split ? 2 : 1));
     auto launch = [&](auto dconst) {
         constexpr int DD = decltype(dconst)::value;
         if (ext)
             hipLaunchKernelGGL((prefill_bf16_kernel<DD, true>), grid, block, 0, stream, a);
-        else
+        else if constexpr (DD <= 128) {
+            if (split)
+                hipLaunchKernelGGL((prefill_bf16_kernel<DD, false, 2>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((prefill_bf16_kernel<DD, false>), grid, block, 0, stream, a);
+        } else {
             hipLaunchKernelGGL((prefill_bf16_kernel<DD, false>), grid, block, 0, stream, a);
+        }
     };
     if (p.head_dim == 128)
         launch(std::integral_constant<int, 128>());

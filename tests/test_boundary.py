@@ -28,6 +28,26 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted(attn.EXPORTS)
 
 
+BENCH_HEADER = os.path.join(ROOT, "include", "attn_bench.h")
+
+
+def test_bench_header_declares_the_measurement_helpers():
+    text = open(BENCH_HEADER).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(attn_bench_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+    assert names == sorted(attn.BENCH_EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", attn._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\s[TW]\s+(attn_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    # host-side argument checks, before any HIP call
+    f = attn.lib.attn_bench_stream_read
+    assert f(None, P(FAKE), 16, 1, P(FAKE), None) == -1
+    assert f(P(FAKE), P(FAKE), 15, 1, P(FAKE), None) == -2
+    assert f(P(FAKE), P(MIS), 16, 1, P(FAKE), None) == -2
+    assert f(P(FAKE), P(FAKE), 16, 0, P(FAKE), None) == -2
+    assert f(P(FAKE), P(FAKE), 0, 4, P(FAKE), None) == 0
+
+
 def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(attn.lib, name), name

@@ -369,3 +369,16 @@ def test_decode_without_lse_output(attn, paged):
     say("decode lse NULL paged=%d: O max_abs=%.3e rms=%.3e" % (paged, so["max_abs"], so["rms"]))
     assert so["max_abs"] <= BF16_TOL["o"], so
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("N,causal", [(2000, True), (1111, False)])
+def test_prefill_key_split_odd_tile_counts(attn, N, causal):
+    """Short prompts run the key-split instantiation (two wave groups per query tile,
+    each over half of its key tiles, merged by the combine rule).  With N = 2000 the
+    last query tile has 63 key tiles (causal), with N = 1111 every tile has 35
+    (full): the second group's last tile lies wholly past the diagonal or past N."""
+    say("case: key-split prefill N=%d causal=%s" % (N, causal))
+    x = W.prefill_inputs(1300 + N, 1, 28, 4, N, 128, W.BF16, causal=causal)
+    o, lse = run_prefill(attn, x)
+    ro, rl = oracle.prefill(x.q, x.k, x.v, causal, x.scale)
+    check("key split N=%d causal=%d" % (N, causal), o, lse, ro, rl, BF16_TOL)
