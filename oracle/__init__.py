@@ -368,3 +368,32 @@ def decode_fp8(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_len
                             softcap)
         o[b], lse[b] = ob[0], lb[0]
     return o, lse
+
+
+def decode_fp8_append(q, k_new8, v_new8, k_cache8, v_cache8, descale_k, descale_v, block_table, cache_seqlens,
+                      scale: float, page_size: int, max_blocks: int):
+    """Decode over an E4M3 cache with the new token appended in place first (pofe.ai
+    page, section "Minimal implementation", on the 8-bit cache of decode_fp8): the new
+    rows' codes k_new8, v_new8 [B, Hkv, d] go to token t = cache_seqlens[b] of sequence
+    b (slot t % P of page block_table[b][t // P], or row t of a contiguous cache), t
+    clamped into [0, capacity - 1], and the query attends t + 1 tokens of the cache
+    with its per-(sequence, KV head) descales.  Returns (o, lse, k_cache8_after,
+    v_cache8_after); the arguments are not modified."""
+    kc, vc = _u8(k_cache8).copy(), _u8(v_cache8).copy()
+    kn, vn = _u8(k_new8), _u8(v_new8)
+    sl = _i32(cache_seqlens)
+    bt = None if block_table is None else _i32(block_table)
+    cap = int(max_blocks) * int(page_size)
+    t_new = np.clip(sl.astype(np.int64), 0, cap - 1)
+    for b in range(sl.shape[0]):
+        t = int(t_new[b])
+        if bt is None:
+            kc[b, t] = kn[b]
+            vc[b, t] = vn[b]
+        else:
+            page = int(bt[b, t // page_size])
+            kc[page, t % page_size] = kn[b]
+            vc[page, t % page_size] = vn[b]
+    o, lse = decode_fp8(q, kc, vc, descale_k, descale_v, bt, (t_new + 1).astype(np.int32), scale, page_size,
+                        max_blocks)
+    return o, lse, kc, vc

@@ -781,6 +781,64 @@ def test_fp8_decode_worked_example_and_invariants():
     assert np.array_equal(op[0, :, L - 1], od[0]) and np.array_equal(lp[0, :, L - 1], ld[0])
 
 
+def _e4m3_codes(rng, shape):
+    """Random finite E4M3 codes (exponent fields below 15 and the sign bit random)."""
+    return (rng.integers(0, 256, size=shape).astype(np.uint8) & 0x77) | (
+        rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+
+
+def test_fp8_append_into_empty_cache_is_the_new_token_alone():
+    """E4M3 cache, nothing cached: the softmax has the new key alone, so O is the new
+    value row dequantised, descale_v * e4m3(v_new), and LSE = scale * descale_k *
+    <q, e4m3(k_new)> (closed form, with the E4M3 values from the format definition)."""
+    rng = np.random.default_rng(34)
+    B, Hq, Hkv, d, P, nb = 2, 4, 2, 8, 16, 2
+    q = rng.standard_normal((B, Hq, d))
+    kn, vn = _e4m3_codes(rng, (B, Hkv, d)), _e4m3_codes(rng, (B, Hkv, d))
+    kc, vc = _e4m3_codes(rng, (B, nb * P, Hkv, d)), _e4m3_codes(rng, (B, nb * P, Hkv, d))
+    dk = rng.uniform(0.5, 2, (B, Hkv)); dv = rng.uniform(0.5, 2, (B, Hkv))
+    o, lse, kc2, vc2 = oracle.decode_fp8_append(q, kn, vn, kc, vc, dk, dv, None, np.zeros(B, np.int32), 0.3, P, nb)
+    g = Hq // Hkv
+    val = np.vectorize(lambda c: math.ldexp(1 + (int(c) & 7) / 8, ((int(c) >> 3) & 15) - 7) if (int(c) >> 3) & 15
+                       else math.ldexp((int(c) & 7) / 8, -6))
+    sign = lambda c: np.where(c >> 7, -1.0, 1.0)
+    ke, ve = val(kn) * sign(kn), val(vn) * sign(vn)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // g
+            assert np.max(np.abs(o[b, h] - dv[b, hk] * ve[b, hk])) < 1e-12
+            assert abs(lse[b, h] - 0.3 * dk[b, hk] * float(q[b, h] @ ke[b, hk])) < 1e-12
+    assert np.array_equal(kc2[:, 0], kn) and np.array_equal(vc2[:, 0], vn)
+    assert np.array_equal(kc2[:, 1:], kc[:, 1:]) and np.array_equal(vc2[:, 1:], vc[:, 1:])
+
+
+def test_fp8_append_of_a_cached_row_equals_decode_of_one_more_token():
+    """Appending the codes the E4M3 cache already holds at token L changes no byte, so
+    the result is decode_fp8 over L + 1 tokens, bit for bit; paged and contiguous; and a
+    paged append writes only slot L % P of page bt[b][L // P]."""
+    rng = np.random.default_rng(35)
+    B, Hq, Hkv, d, P, nb = 3, 4, 2, 16, 16, 4
+    q = rng.standard_normal((B, Hq, d))
+    kc, vc = _e4m3_codes(rng, (B, nb * P, Hkv, d)), _e4m3_codes(rng, (B, nb * P, Hkv, d))
+    dk = rng.uniform(0.5, 2, (B, Hkv)); dv = rng.uniform(0.5, 2, (B, Hkv))
+    lens = np.array([15, 16, 63], np.int32)
+    kn = np.stack([kc[b, lens[b]] for b in range(B)]); vn = np.stack([vc[b, lens[b]] for b in range(B)])
+    o, lse, kc2, vc2 = oracle.decode_fp8_append(q, kn, vn, kc, vc, dk, dv, None, lens, 0.25, P, nb)
+    ro, rl = oracle.decode_fp8(q, kc, vc, dk, dv, None, lens + 1, 0.25, P, nb)
+    assert np.array_equal(o, ro) and np.array_equal(lse, rl)
+    assert np.array_equal(kc2, kc) and np.array_equal(vc2, vc)
+    # paged: pool of 9 pages, sequence b's logical page j at bt[b, j]
+    bt = np.array([[4, 0, 7, 2], [8, 1, 3, 6], [5, 2, 0, 1]], np.int32)
+    kp, vp = _e4m3_codes(rng, (9, P, Hkv, d)), _e4m3_codes(rng, (9, P, Hkv, d))
+    kn2, vn2 = _e4m3_codes(rng, (B, Hkv, d)), _e4m3_codes(rng, (B, Hkv, d))
+    lens2 = np.array([17, 5, 40], np.int32)
+    _, _, kp2, vp2 = oracle.decode_fp8_append(q, kn2, vn2, kp, vp, dk, dv, bt, lens2, 0.25, P, nb)
+    ek, ev = kp.copy(), vp.copy()
+    for b, (page, slot) in enumerate([(0, 1), (8, 5), (0, 8)]):
+        ek[page, slot] = kn2[b]; ev[page, slot] = vn2[b]
+    assert np.array_equal(kp2, ek) and np.array_equal(vp2, ev)
+
+
 def test_oracle_result_does_not_depend_on_its_thread_count():
     """The oracle's threads split rows and heads, never one row's sums, so its results
     are bitwise the same on one thread as on all of them (the single-core timing
