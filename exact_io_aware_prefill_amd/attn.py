@@ -34,7 +34,8 @@ ATTN_BF16 = 1
 
 EXPORTS = ("attn_prefill", "attn_prefill_varlen", "attn_prefill_ext", "attn_prefill_fp8", "attn_prefill_fp8_varlen",
            "attn_prefill_fp8_ext",
-           "attn_decode", "attn_decode_noalloc", "attn_decode_append", "attn_decode_ext", "attn_decode_fp8", "attn_decode_fp8_ext",
+           "attn_decode", "attn_decode_noalloc", "attn_decode_append", "attn_decode_ext", "attn_decode_fp8",
+           "attn_decode_fp8_append", "attn_decode_fp8_ext",
            "attn_decode_chunk_tokens",
            "attn_decode_workspace_bytes", "attn_lse_combine", "attn_decode_check_tables", "attn_status_string")
 
@@ -61,6 +62,9 @@ lib.attn_decode_ext.restype = _I
 lib.attn_decode_fp8.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P,
                                 ctypes.c_size_t, _P]
 lib.attn_decode_fp8.restype = _I
+lib.attn_decode_fp8_append.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       ctypes.c_float, _I, _P, ctypes.c_size_t, _P]
+lib.attn_decode_fp8_append.restype = _I
 lib.attn_decode_fp8_ext.argtypes = [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
                                     ctypes.c_float, _I, _P, ctypes.c_size_t, _P]
 lib.attn_decode_fp8_ext.restype = _I
@@ -292,6 +296,23 @@ def attn_decode_fp8(q, k_cache8, v_cache8, descale_k, descale_v, block_table, se
     _check(rc, "attn_decode_fp8")
 
 
+def attn_decode_fp8_append(q, k_new8, v_new8, k_cache8, v_cache8, descale_k, descale_v, block_table, cache_seqlens,
+                           o, lse, page_size: int, max_blocks_per_seq: int, scale: float, chunk_tokens: int, workspace,
+                           stream=None) -> None:
+    """attn_decode_fp8 after writing the new token's E4M3 codes k_new8, v_new8 [B, Hkv, d]
+    into the caches at token cache_seqlens[b]; the query attends cache_seqlens[b] + 1
+    tokens.  cache_seqlens is not modified."""
+    B, Hq, d = q.shape
+    Hkv = k_cache8.shape[-2]
+    rc = lib.attn_decode_fp8_append(_ptr(q), _ptr(k_new8), _ptr(v_new8), _ptr(k_cache8), _ptr(v_cache8),
+                                    _ptr(descale_k), _ptr(descale_v), _ptr(block_table), _ptr(cache_seqlens), _ptr(o),
+                                    _ptr(lse), B, Hq, Hkv, d, int(page_size), int(max_blocks_per_seq), float(scale),
+                                    int(chunk_tokens), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                    _stream(stream))
+    _check(rc, "attn_decode_fp8_append")
+
+
 def attn_decode_fp8_ext(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, o, lse, page_size: int,
                         max_blocks_per_seq: int, scale: float, window_left: int, softcap: float, chunk_tokens: int,
                         workspace, stream=None) -> None:
@@ -325,6 +346,23 @@ def decode_fp8(q, k_cache8, v_cache8, block_table, seq_lens, page_size: int, max
         else:
             attn_decode_fp8_ext(q, k_cache8, v_cache8, descale_k, descale_v, block_table, seq_lens, o, lse, page_size,
                                 max_blocks_per_seq, scale, window_left, softcap, chunk_tokens, workspace, stream)
+        return o, lse
+
+
+def decode_fp8_append(q, k_new8, v_new8, k_cache8, v_cache8, block_table, cache_seqlens, page_size: int,
+                      max_blocks_per_seq: int, descale_k=None, descale_v=None, scale: float | None = None,
+                      chunk_tokens: int = 0, stream=None, workspace=None):
+    with _on(stream):
+        B, Hq, d = q.shape
+        Hkv = k_cache8.shape[-2]
+        need = attn_decode_workspace_bytes(B, Hq, Hkv, d, page_size, max_blocks_per_seq, chunk_tokens)
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+        scale = d ** -0.5 if scale is None else scale
+        attn_decode_fp8_append(q, k_new8, v_new8, k_cache8, v_cache8, descale_k, descale_v, block_table, cache_seqlens,
+                               o, lse, page_size, max_blocks_per_seq, scale, chunk_tokens, workspace, stream)
         return o, lse
 
 

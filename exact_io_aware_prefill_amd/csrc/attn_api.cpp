@@ -383,6 +383,17 @@ int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache, con
                        chunk_tokens, workspace, workspace_bytes, stream, true, descale_k_or_null, descale_v_or_null);
 }
 
+int attn_decode_fp8_append(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                           const float *descale_k_or_null, const float *descale_v_or_null, const int32_t *block_table,
+                           const int32_t *cache_seqlens, void *o, float *lse_or_null, int batch, int n_q_heads,
+                           int n_kv_heads, int head_dim, int page_size, int max_blocks_per_seq, float scale,
+                           int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return decode_impl(true, q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse_or_null, batch,
+                       n_q_heads, n_kv_heads, head_dim, page_size, max_blocks_per_seq, ATTN_BF16, scale, -1, 0.f,
+                       chunk_tokens, workspace, workspace_bytes, stream, true, descale_k_or_null, descale_v_or_null);
+}
+
 int attn_decode_fp8_ext(const void *q, const void *k_cache, const void *v_cache, const float *descale_k_or_null,
                         const float *descale_v_or_null, const int32_t *block_table, const int32_t *seq_lens, void *o,
                         float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,

@@ -338,7 +338,6 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
 {
     using Gm = Geo<D>;
     using Lg = KvGeo<D, KV8>;
-    static_assert(!KV8 || !APPEND, "the E4M3 cache has no in-place append");
     constexpr int kWaves = split_waves<D>();
     // one slab per wave; reused at the end for the eight waves' [16][D] float outputs
     static_assert(Gm::SLAB == 16 * D * 4, "slab must hold a wave's 16 x D float output");
@@ -437,15 +436,18 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
     if (APPEND && has_new) {
         // Write the new rows into the cache slot first: this workgroup is the only
         // reader of that slot, and its loads below are issued after the barrier,
-        // which orders them after these stores.
+        // which orders them after these stores.  A row is Lg::RB bytes (bf16, or
+        // the E4M3 codes of an 8-bit cache, which the caller quantised with that
+        // cache's descales), copied as RB / 16 16-byte chunks.
+        constexpr int NCH = Lg::RB / 16;
         const long long row = token_index(a, b, t_new) * a.Hkv + hk;
-        const size_t src = ((size_t)b * a.Hkv + hk) * D;
-        if (tid < D / 8)
-            reinterpret_cast<uint4 *>(const_cast<uint16_t *>(a.k) + row * D)[tid] =
-                reinterpret_cast<const uint4 *>(a.k_new + src)[tid];
-        else if (tid < D / 4)
-            reinterpret_cast<uint4 *>(const_cast<uint16_t *>(a.v) + row * D)[tid - D / 8] =
-                reinterpret_cast<const uint4 *>(a.v_new + src)[tid - D / 8];
+        const size_t src = ((size_t)b * a.Hkv + hk) * Lg::RB;
+        if (tid < NCH)
+            reinterpret_cast<uint4 *>(const_cast<char *>(reinterpret_cast<const char *>(a.k)) + row * Lg::RB)[tid] =
+                reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(a.k_new) + src)[tid];
+        else if (tid < 2 * NCH)
+            reinterpret_cast<uint4 *>(const_cast<char *>(reinterpret_cast<const char *>(a.v)) + row * Lg::RB)[tid - NCH] =
+                reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(a.v_new) + src)[tid - NCH];
         __syncthreads();
     }
     // with a window, skip this wave's steps that end before it starts
@@ -753,7 +755,9 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
         constexpr int kThreads = split_waves<DD>() * 64;
         if constexpr (DD != 256) {
             if (p.kv_e4m3) {
-                if (ext)
+                if (append)  // (the host allows no window or soft-cap with the E4M3 append)
+                    hipLaunchKernelGGL((decode_split_kernel<DD, true, false, true>), grid, dim3(kThreads), 0, stream, a);
+                else if (ext)
                     hipLaunchKernelGGL((decode_split_kernel<DD, false, true, true>), grid, dim3(kThreads), 0, stream, a);
                 else
                     hipLaunchKernelGGL((decode_split_kernel<DD, false, false, true>), grid, dim3(kThreads), 0, stream, a);

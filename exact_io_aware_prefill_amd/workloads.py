@@ -297,6 +297,17 @@ def decode_new_rows(seed: int, B: int, Hkv: int, d: int, dtype: str = BF16):
     return _draw(rng, (B, Hkv, d), dtype), _draw(rng, (B, Hkv, d), dtype)
 
 
+def decode_fp8_new_rows(seed: int, d: int, descale_k, descale_v):
+    """The appended token's rows for an E4M3 cache: float32 draws [B, Hkv, d] (as
+    decode_new_rows) quantised to E4M3 codes with the cache's per-(sequence, KV head)
+    descales [B, Hkv] (code = value / descale, clamped to +-448, PyTorch's conversion)."""
+    B, Hkv = descale_k.shape
+    kn, vn = decode_new_rows(seed, B, Hkv, d, F32)
+    k8 = (kn / descale_k[:, :, None]).clamp(-448, 448).to(torch.float8_e4m3fn)
+    v8 = (vn / descale_v[:, :, None]).clamp(-448, 448).to(torch.float8_e4m3fn)
+    return k8, v8
+
+
 # --------------------------------------------------------------------------
 # Named workloads: the pages' shapes (Qwen2.5-7B attention layout for prefill
 # and single-sequence decode, Llama-3-8B layout for batched paged decode).

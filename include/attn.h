@@ -28,6 +28,7 @@
  *     "The bottleneck it attacks");
  *   - attn_prefill_fp8_varlen: the FP8 prefill over a packed batch;
  *   - attn_decode_fp8: the decode over an FP8 (E4M3) KV cache;
+ *   - attn_decode_fp8_append: the same with the new token's codes appended in place;
  *   - attn_decode_noalloc: attn_decode with its partials in a static device
  *     array, for callers that cannot allocate;
  *   - attn_lse_combine: that reduction on its own -- the combine rule for
@@ -355,6 +356,31 @@ int attn_decode_fp8(const void *q, const void *k_cache, const void *v_cache, con
                     float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim, int page_size,
                     int max_blocks_per_seq, float scale, int chunk_tokens, void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * attn_decode_fp8_append -- attn_decode_fp8 with the new token's key and value
+ * written into the E4M3 cache in place first: the decode step of the pofe.ai
+ * page's section "Minimal implementation" (the cache takes the new rows, then the
+ * query attends them) on the 8-bit cache whose half-size rows section "Decode: a
+ * different bottleneck" says decode is bound by.
+ *
+ *   k_new, v_new [batch, n_kv_heads, head_dim]  E4M3 codes, one byte each, already
+ *                quantised with the cache's descales (value = descale * code);
+ *                written unchanged at token cache_seqlens[b] of sequence b, exactly as
+ *                attn_decode_append places its rows (slot t % page_size of page
+ *                block_table[b][t / page_size], or row t of a contiguous cache; t
+ *                clamped into [0, capacity - 1])
+ *   cache_seqlens [batch] int32, read only: tokens already cached; the query
+ *                attends cache_seqlens[b] + 1 tokens and the caller advances it
+ *   Every other argument, the descales, head sizes (64, 128), workspace, limits and
+ *   errors are those of attn_decode_fp8; k_new and v_new are required (ATTN_ERR_NULL)
+ *   and 16-byte aligned (ATTN_ERR_ALIGN).  No window or soft-cap.
+ */
+int attn_decode_fp8_append(const void *q, const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                           const float *descale_k_or_null, const float *descale_v_or_null, const int32_t *block_table,
+                           const int32_t *cache_seqlens, void *o, float *lse_or_null, int batch, int n_q_heads,
+                           int n_kv_heads, int head_dim, int page_size, int max_blocks_per_seq, float scale,
+                           int chunk_tokens, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * attn_decode_fp8_ext -- attn_decode_fp8 with the sliding window and the logit

@@ -427,3 +427,21 @@ def test_decode_noalloc_host_checks():
     # exactly at the limit is accepted by the size check (checked via the workspace formula)
     rows = attn.NOALLOC_SCRATCH_BYTES // (129 * 4)
     assert attn.attn_decode_workspace_bytes(rows, 1, 1, 128, 16, 1, 16) <= attn.NOALLOC_SCRATCH_BYTES
+
+
+def test_decode_fp8_append_host_checks():
+    """attn_decode_fp8_append: the append's rows are required and aligned, head sizes
+    64 and 128 only, and the workspace is checked, all on the host."""
+    def call(kn=FAKE, vn=FAKE, d=128, ws=FAKE, wsb=1 << 30, B=2, q=FAKE):
+        return attn.lib.attn_decode_fp8_append(P(q), P(kn) if kn else None, P(vn) if vn else None, P(FAKE),
+                                               P(FAKE), None, None, None, P(FAKE), P(FAKE), None, B, 8, 2, d, 16,
+                                               64, 0.1, 0, P(ws) if ws else None, wsb, None)
+    assert call(kn=0) == attn.ATTN_ERR_NULL
+    assert call(vn=0) == attn.ATTN_ERR_NULL
+    assert call(q=0) == attn.ATTN_ERR_NULL
+    assert call(kn=MIS) == attn.ATTN_ERR_ALIGN
+    assert call(d=256) == attn.ATTN_ERR_UNSUPPORTED
+    assert call(d=96) == attn.ATTN_ERR_UNSUPPORTED
+    assert call(ws=0) == attn.ATTN_ERR_WORKSPACE
+    assert call(wsb=16) == attn.ATTN_ERR_WORKSPACE
+    assert call(B=0) == attn.ATTN_OK
