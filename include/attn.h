@@ -62,8 +62,8 @@
  *     n_kv_heads) (consecutive query heads share a KV head).
  *   - Head sizes 64, 128 and 256 (256 being the largest the page's section
  *     "Interaction with post-trained models" names) on every entry point except
- *     the FP8 ones (attn_prefill_fp8, attn_prefill_fp8_varlen, attn_decode_fp8:
- *     64 and 128).
+ *     the FP8 ones (attn_prefill_fp8, attn_prefill_fp8_varlen, attn_prefill_fp8_ext,
+ *     attn_decode_fp8, attn_decode_fp8_append, attn_decode_fp8_ext: 64 and 128).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
