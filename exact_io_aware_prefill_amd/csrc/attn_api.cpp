@@ -251,7 +251,7 @@ int prefill_fp8_impl(bool packed, const void *q, const void *k, const void *v, v
         head_dim <= 0 || !variant_ok(window_left, softcap))
         return ATTN_ERR_SHAPE;
     if (n_q_heads % n_kv_heads != 0) return ATTN_ERR_GQA;
-    if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return ATTN_ERR_UNSUPPORTED;
     if (batch == 0 || seqlen == 0 || (packed && total_tokens == 0)) return ATTN_OK;
     if (!q || !k || !v || !o || !lse || (packed && !cu_seqlens)) return ATTN_ERR_NULL;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) ||

@@ -102,18 +102,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes, kBufferFlags);
 }
 
-// Chunk permutations (see the header).  D = 128: rows are 128 bytes (two per
-// bank line).  D = 64: rows are 64 bytes (four per bank line).
-template <int D> __device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r >> 1) & 7 : (r >> 2) & 3; }
+// Chunk permutations (see the header).  D = 256: rows are 256 bytes (one bank
+// line): the K operand reads (16 rows per pass, one chunk each) need 16 distinct
+// slots, r & 15; the transpose reads (rows 0-3 and 8-11, or 4-7 and 12-15, two
+// chunks each per 32 lanes) need those 8 rows' chunk pairs on distinct banks,
+// 2 ((r & 3) | ((r >> 3) & 1) << 2).  D = 128: rows are 128 bytes (two per bank
+// line).  D = 64: rows are 64 bytes (four per bank line).  Every permutation
+// repeats within 16 rows, the spacing of a lane's rows in the loader.
+template <int D> __device__ __forceinline__ int k_swz(int r)
+{
+    return D == 256 ? (r & 15) : D == 128 ? (r >> 1) & 7 : (r >> 2) & 3;
+}
 template <int D> __device__ __forceinline__ int v_swz(int r)
 {
-    return D == 128 ? 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) : 2 * ((r >> 3) & 1);
+    return D == 256 ? 2 * ((r & 3) | (((r >> 3) & 1) << 2))
+                    : D == 128 ? 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) : 2 * ((r >> 3) & 1);
 }
 
 // Memory -> LDS loader of one 64-row tile of D bytes per row: D/16 wave
-// instructions of 64 16-byte chunks, wave w issuing instructions w, w + 4.
-// A lane's rows in its instructions are 32 apart, which no permutation above
-// distinguishes, so one per-lane offset serves them all.
+// instructions of 64 16-byte chunks, wave w issuing instructions w, w + 4, ...
+// A lane's rows in its instructions are 32 apart (16 for D = 256), which no
+// permutation above distinguishes, so one per-lane offset serves them all.
 template <int D>
 struct TileLoader {
     static constexpr int NC = D / 16;           // chunks per row
@@ -121,7 +130,7 @@ struct TileLoader {
     static constexpr int INSTR = kBlockN * NC / 64;
     static constexpr int PER_WAVE = INSTR / kWaves;
     static_assert(INSTR % kWaves == 0, "tile instructions split evenly over the waves");
-    static_assert(RPI * kWaves == 32 || PER_WAVE == 1, "a lane's rows are 32 apart");
+    static_assert(RPI * kWaves % 16 == 0 || PER_WAVE == 1, "a lane's rows are a multiple of 16 apart");
     uint32_t voff;  // per-lane byte offset from the first row an instruction fills
     uint32_t rowb;  // bytes between consecutive key rows in memory
 
@@ -232,9 +241,13 @@ __device__ __forceinline__ float soft_cap(float x, float cap, float cap_k)
 }
 
 // EXT selects the sliding-window / soft-cap instantiation (the plain ones keep
-// their instruction schedule).
+// their instruction schedule).  D = 256 keeps twice the accumulators (128
+// values) and Q fragments, about 280 live values, so it runs one wave per SIMD
+// with the accumulation registers in use; D <= 128 runs two.
+template <int D> constexpr int fp8_waves_per_simd() { return D == 256 ? 1 : 2; }
+
 template <int D, bool PACKED, bool EXT>
-__global__ __launch_bounds__(kWaves * 64, 2) void prefill_fp8_kernel(Args a)
+__global__ __launch_bounds__(kWaves * 64, fp8_waves_per_simd<D>()) void prefill_fp8_kernel(Args a)
 {
     constexpr int NT = kWaves * 64;
     constexpr int TB = kBlockN * D;  // bytes per K or V tile
@@ -530,6 +543,8 @@ hipError_t launch_prefill_fp8(const PrefillFp8Params &p, hipStream_t stream)
     };
     if (p.head_dim == 128)
         by_packed(std::integral_constant<int, 128>());
+    else if (p.head_dim == 256)
+        by_packed(std::integral_constant<int, 256>());
     else
         by_packed(std::integral_constant<int, 64>());
     return hipGetLastError();

@@ -62,8 +62,8 @@
  *     n_kv_heads) (consecutive query heads share a KV head).
  *   - Head sizes 64, 128 and 256 (256 being the largest the page's section
  *     "Interaction with post-trained models" names) on every entry point except
- *     the FP8 ones (attn_prefill_fp8, attn_prefill_fp8_varlen, attn_prefill_fp8_ext,
- *     attn_decode_fp8, attn_decode_fp8_append, attn_decode_fp8_ext: 64 and 128).
+ *     the E4M3-cache decodes (attn_decode_fp8, attn_decode_fp8_append,
+ *     attn_decode_fp8_ext: 64 and 128).
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -170,7 +170,7 @@ int attn_prefill_ext(const void *q, const void *k, const void *v, void *o, float
  *   descale_q/k/v_or_null [batch, n_kv_heads] float32 on the device, 4-byte
  *        aligned, one factor per (sequence, KV head) shared by the group's query
  *        heads; NULL means 1.
- *   head_dim in {64, 128}; causal and scale as attn_prefill.  Arithmetic: both
+ *   head_dim in {64, 128, 256}; causal and scale as attn_prefill.  Arithmetic: both
  *   products on the FP8 matrix cores with float32 accumulation; the
  *   probabilities are rounded to E4M3 (nearest even, each <= 256) before the
  *   P*V product, so O carries up to 2^-4 relative error per term (2^-10
@@ -199,7 +199,7 @@ int attn_prefill_fp8(const void *q, const void *k, const void *v, void *o, float
  *         KV head); NULL means 1.
  *   cu_seqlens, max_seqlen: as attn_prefill_varlen (offsets outside
  *         [0, total_tokens] or lengths above max_seqlen are clamped).
- *   head_dim in {64, 128}; arithmetic as attn_prefill_fp8.
+ *   head_dim in {64, 128, 256}; arithmetic as attn_prefill_fp8.
  *   (max_seqlen + 127) * n_q_heads * head_dim >= 2^32 is ATTN_ERR_UNSUPPORTED;
  *   batch, max_seqlen or total_tokens of 0 does nothing.
  */

@@ -164,7 +164,7 @@ def prefill_fp8(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dq=0, dk=0, dv=0, B=1,
     (dict(N=-1), attn.ATTN_ERR_SHAPE),
     (dict(Hkv=0), attn.ATTN_ERR_SHAPE),
     (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
-    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),     # fp8: head sizes 64 and 128
+    (dict(d=512), attn.ATTN_ERR_UNSUPPORTED),     # fp8 prefill: head sizes 64, 128 and 256
     (dict(d=96), attn.ATTN_ERR_UNSUPPORTED),
     (dict(k=MIS), attn.ATTN_ERR_ALIGN),
     (dict(dv=FAKE + 2), attn.ATTN_ERR_ALIGN),     # descales are float arrays: 4-byte aligned
@@ -191,7 +191,7 @@ def prefill_fp8_varlen(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dq=0, dk=0, dv=
     (dict(T=-1), attn.ATTN_ERR_SHAPE),
     (dict(B=-1), attn.ATTN_ERR_SHAPE),
     (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
-    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=512), attn.ATTN_ERR_UNSUPPORTED),
     (dict(N=1 << 24, Hq=32), attn.ATTN_ERR_UNSUPPORTED),  # a packed row holds all heads: 32-bit offsets
     (dict(T=0, q=0, k=0, v=0, o=0, lse=0, cu=0), attn.ATTN_OK),
     (dict(N=0, q=0, k=0, v=0, o=0, lse=0, cu=0), attn.ATTN_OK),
@@ -376,7 +376,7 @@ def prefill_fp8_ext(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dq=0, dk=0, dv=0, 
     (dict(o=MIS), attn.ATTN_ERR_ALIGN),
     (dict(dk=FAKE + 2), attn.ATTN_ERR_ALIGN),
     (dict(Hq=6, Hkv=4), attn.ATTN_ERR_GQA),
-    (dict(d=256), attn.ATTN_ERR_UNSUPPORTED),
+    (dict(d=512), attn.ATTN_ERR_UNSUPPORTED),
     (dict(B=0, q=0, k=0, v=0, o=0, lse=0), attn.ATTN_OK),
 ])
 def test_prefill_fp8_ext_argument_errors(kw, code):

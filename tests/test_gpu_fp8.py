@@ -95,7 +95,7 @@ def test_fp8_worked_example(attn):
 
 
 @pytest.mark.parametrize("N", [1, 63, 64, 65, 300, 1000])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 def test_fp8_prefill_ragged(attn, N, d, causal):
     say("case: fp8 prefill N=%d d=%d causal=%s" % (N, d, causal))
@@ -128,6 +128,21 @@ def test_fp8_prefill_without_descales(attn):
     torch.cuda.synchronize()
     ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, None, None, None, True, x.scale)
     check_fp8("fp8 no descales", o, lse, ro, rl, row_bounds(x))
+
+
+def test_fp8_prefill_d256_8k_sampled_rows(attn):
+    """d = 256 (one wave per SIMD, 256-byte rows) at 8k tokens, 16 query / 8 KV heads,
+    every 31st row."""
+    N, step = 8192, 31
+    say("case: fp8 prefill d=256 N=%d sampled every %d" % (N, step))
+    x = W.prefill_fp8_inputs(3150, 1, 16, 8, N, 256)
+    o, lse = run(attn, x)
+    assert torch.isfinite(lse).all() and torch.isfinite(o.float()).all()
+    ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, True, x.scale,
+                                row_step=step)
+    rows = np.arange(0, N, step)
+    check_fp8("fp8 d=256 8k (sampled)", o[:, :, rows], lse[:, :, rows], ro[:, :, rows], rl[:, :, rows],
+              row_bounds(x, rows))
 
 
 def test_fp8_prefill_16k_sampled_rows(attn):
@@ -224,7 +239,7 @@ def run_packed(attn, x):
     return o, lse
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 def test_fp8_prefill_varlen_ragged(attn, d, causal):
     lens = [1, 7, 0, 128, 129, 300, 64]

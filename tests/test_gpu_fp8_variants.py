@@ -61,7 +61,7 @@ def padded_bounds(x, window, softcap, rows=None):
                      for b in range(B)])
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("window,softcap", [(0, 0.0), (37, 0.0), (200, 0.0), (-1, 20.0), (64, 5.0)])
 def test_fp8_window_softcap_padded(attn, d, causal, window, softcap):
