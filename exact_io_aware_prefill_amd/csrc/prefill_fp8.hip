@@ -34,9 +34,10 @@
 //     absolute below the normal range).
 //   * Step t issues QK(t+1) into a second score buffer and PV(t-1), then the
 //     softmax of tile t; scheduling groups spread the softmax's vector work
-//     over the eight products (two LDS reads and twenty VALU instructions after
-//     each), so the matrix cores and the VALUs overlap inside the wave.  Two
-//     waves per SIMD (about 205 VGPRs).
+//     over the eight products (two LDS reads and ten VALU instructions after
+//     each; twenty, which bunched the softmax's ~110 instructions behind the
+//     first products, measured 1.6% slower), so the matrix cores and the VALUs
+//     overlap inside the wave.  Two waves per SIMD (about 205 VGPRs).
 //   * K and V tiles go straight from memory into LDS (buffer loads with the LDS
 //     destination bit), double-buffered.  16-byte chunk c of key row r sits at
 //     slot c ^ swz(r); the permutations make the K operand reads (16 rows per
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(kWaves * 64, fp8_waves_per_simd<D>()) void prefill_
         for (int i = 0; i < (D / 64) * 2 + D / 32; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
         }
         if (__builtin_amdgcn_ballot_w64(m == -INFINITY || rs > kMaxLaneSum)) {
             asm volatile("" ::"v"(Pc));
