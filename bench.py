@@ -16,6 +16,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -34,11 +35,15 @@ TRAFFIC = {
     "prefill": {"file": os.path.join(ROOT, "profiles", "prefill_bf16_n16384_traffic.json"),
                 "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel<128, false, 1>"},
     "decode": {"file": os.path.join(ROOT, "profiles", "decode_split_s32768_traffic.json"),
-               "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel<128, false, false, false>"},
+               "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel<128, false, false, false>",
+               # the 32k decode's dispatches only (256 workgroups of 512 threads), not the
+               # paged batch's, which run the same kernel on a larger grid
+               "grid": 256 * 512},
     "fp8": {"file": os.path.join(ROOT, "profiles", "prefill_fp8_n16384_traffic.json"),
             "src": os.path.join(CSRC, "prefill_fp8.hip"), "kernel": "prefill_fp8_kernel<128, false, false>"},
 }
 COPY_BYTES = 1 << 30  # reference dispatch for the counters: a 1 GiB device-to-device copy
+READ_GRIDS = (256, 512, 1024, 2048, 4096, 8192)  # workgroup counts of the floor's read sweep
 N_KV_COPIES = 8
 
 
@@ -52,6 +57,7 @@ def parse():
     ap.add_argument("--only", choices=["prefill", "decode", "fp8"], default=None,
                     help="time one part only (profiling runs)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 prefill measurement")
+    ap.add_argument("--no-paged", action="store_true", help="skip the batched paged decode measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference dispatch for HBM counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -93,7 +99,7 @@ def _counter_rows(csv_path: str, counter: str):
     with open(csv_path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] == counter:
-                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+                rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
     return rows
 
 
@@ -105,10 +111,10 @@ def write_traffic(fetch_csv: str, write_csv: str, command: str):
     out = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, name)
-        copy_kib = max(v for k, v in rows if "copyBuffer" in k)  # the 1 GiB copy is the largest
+        copy_kib = max(v for k, _, v in rows if "copyBuffer" in k)  # the 1 GiB copy is the largest
         factor = COPY_BYTES / (copy_kib * 1024.0)
         for which, t in TRAFFIC.items():
-            vals = [v for k, v in rows if t["kernel"] in k]
+            vals = [v for k, g, v in rows if t["kernel"] in k and t.get("grid") in (None, g)]
             if not vals:
                 continue
             rec = out.setdefault(which, {"calibration": {}})
@@ -412,8 +418,17 @@ def main():
             attn.attn_bench_empty()
         read_ms = time_calls(read)
         read2_ms = time_calls(read_and_launch)
+        # the same read on other grids: the fastest plain read of these bytes here
+        sweep = {}
+        for g in READ_GRIDS:
+            gsink = torch.zeros(4 * g, dtype=torch.int32, device=dev)
+            sweep[g] = time_calls(lambda i, g=g, gsink=gsink: attn.attn_bench_stream_read(
+                kcs[i % N_KV_COPIES], vcs[i % N_KV_COPIES], g, gsink))
+        gbest = min(sweep, key=sweep.get)
         floor = {"read_ms": read_ms, "read_GBps": decode_bytes / (read_ms * 1e-3) / 1e9,
                  "read_plus_launch_ms": read2_ms, "workgroups": wgs,
+                 "best_read": {"ms": sweep[gbest], "GBps": decode_bytes / (sweep[gbest] * 1e-3) / 1e9,
+                               "workgroups": gbest, "grids_tried": list(READ_GRIDS)},
                  "what": "one kernel reading the decode's K and V caches once (16-byte loads, grid-stride, %d "
                          "workgroups of 256 threads, the split kernel's grid), then the same read followed by an "
                          "empty dependent launch; %d back-to-back calls between two events, rotating the %d KV copies"
@@ -456,6 +471,81 @@ def main():
                                 "kernels": "decode_split_kernel<128, false, false, true> + lse_combine_kernel<128>",
                                 "algorithmic_bytes_per_launch": bytes8},
                    "speedup_vs_bf16_cache": dec_bb_ms / ms8}
+
+    # Batched paged decode: 32 sequences with lengths uniform in [1024, 32768], 32/8
+    # heads, 16-token pages placed by a seeded permutation of one shared pool.  The
+    # lengths and block table are the paged workload's own (its seeded draws); the K/V
+    # values are drawn on the device (N(0,1), bf16), which keeps the leg short.  The
+    # pool (about 2.2 GB) is far larger than the Infinity Cache, so no copies are
+    # rotated.  Timed as the 32k decode (back-to-back calls between two events), with
+    # its own floor: the same read kernel over the whole pool on the split kernel's grid.
+    paged = None
+    if do_d and not args.no_paged:
+        pc = W.DECODE_PAGED
+        pq, pbt, psl, pool, pmb = W.decode_paged_layout(pc["seed"], pc["B"], pc["Hq"], pc["d"], pc["page_size"],
+                                                         pc["len_min"], pc["len_max"])
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(pc["seed"])
+        pshape = (pool, pc["page_size"], pc["Hkv"], pc["d"])
+        pk = torch.randn(pshape, generator=gen, device=dev, dtype=torch.bfloat16)
+        pv = torch.randn(pshape, generator=gen, device=dev, dtype=torch.bfloat16)
+        pqd, pbtd, psld = pq.to(dev), pbt.to(dev), psl.to(dev)
+        pod = torch.empty_like(pqd)
+        pld = torch.empty((pc["B"], pc["Hq"]), dtype=torch.float32, device=dev)
+        pchunk = attn.attn_decode_chunk_tokens(pc["B"], pc["Hkv"], pc["page_size"], pmb, 0)
+        pws = torch.empty(attn.attn_decode_workspace_bytes(pc["B"], pc["Hq"], pc["Hkv"], pc["d"], pc["page_size"],
+                                                           pmb, pchunk), dtype=torch.uint8, device=dev)
+        pscale = 1.0 / math.sqrt(pc["d"])
+
+        def run_paged():
+            attn.attn_decode(pqd, pk, pv, pbtd, psld, pod, pld, pc["page_size"], pmb, pscale, pchunk, pws)
+
+        def time_back_to_back(fn, reps):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        preps = max(10, args.steps)
+        pms = time_back_to_back(run_paged, preps)
+        pbytes = (int(psl.to(torch.int64).sum()) * pc["Hkv"] * pc["d"] * 2 * 2 + pqd.numel() * 2 * 2
+                  + pld.numel() * 4)
+        pgrid = pc["B"] * pc["Hkv"] * -(-(pmb * pc["page_size"]) // pchunk)
+        psink = torch.zeros(4 * pgrid, dtype=torch.int32, device=dev)
+        pool_bytes = pk.numel() * 2
+        pread_ms = time_back_to_back(lambda: attn.attn_bench_stream_read(pk, pv, pgrid, psink), preps)
+        psweep = {}
+        for g in READ_GRIDS:
+            gsink = torch.zeros(4 * g, dtype=torch.int32, device=dev)
+            psweep[g] = time_back_to_back(lambda g=g, gsink=gsink: attn.attn_bench_stream_read(pk, pv, g, gsink),
+                                          preps)
+        pbest = min(psweep, key=psweep.get)
+        pgbs = pbytes / (pms * 1e-3) / 1e9
+        paged = {"value": pgbs, "unit": "GB/s", "avg_ms": pms,
+                 "timing": "%d back-to-back calls between two events" % preps,
+                 "config": {"workload": pc["name"], "batch": pc["B"], "q_heads": pc["Hq"], "kv_heads": pc["Hkv"],
+                            "head_dim": pc["d"], "page_size": pc["page_size"],
+                            "cached_tokens": int(psl.to(torch.int64).sum()), "chunk_tokens": pchunk,
+                            "values": "lengths and block table of the paged workload; K/V drawn on the device"},
+                 "roofline": {"bound": "hbm", "achieved": pgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": pgbs / PEAK_HBM_GBS, "traffic": None,
+                              "kernels": "decode_split_kernel<128, false, false, false> + lse_combine_kernel<128>",
+                              "algorithmic_bytes_per_launch": pbytes},
+                 "floor": {"read_ms": pread_ms, "read_GBps": 2 * pool_bytes / (pread_ms * 1e-3) / 1e9,
+                           "workgroups": pgrid,
+                           "what": "one kernel reading the whole K and V page pools once (%d bytes; 16-byte loads, "
+                                   "grid-stride, the split kernel's %d workgroups of 256 threads), %d back-to-back "
+                                   "calls between two events" % (2 * pool_bytes, pgrid, preps),
+                           "call_over_read": pms / pread_ms,
+                           "best_read": {"ms": psweep[pbest], "GBps": 2 * pool_bytes / (psweep[pbest] * 1e-3) / 1e9,
+                                         "workgroups": pbest, "grids_tried": list(READ_GRIDS)}}}
+        del pk, pv
 
     if args.copy_calibration:  # reference dispatch for the HBM byte counters: copy 1 GiB
         src = torch.empty(COPY_BYTES // 2, dtype=torch.float16, device=dev).fill_(1)
@@ -506,6 +596,8 @@ def main():
         out["fp8_prefill"] = fp8
     if fp8_dec is not None:
         out["fp8_decode"] = fp8_dec
+    if paged is not None:
+        out["decode_paged"] = paged
     if do_p and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(px, args.cpu_seconds)
         out["cpu_baseline"]["host"] = host_info()

@@ -246,7 +246,7 @@ def attn_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, o, lse, page
     _check(rc, "attn_decode_noalloc")
 
 
-NOALLOC_SCRATCH_BYTES = 16 << 20  # ATTN_DECODE_NOALLOC_SCRATCH_BYTES of include/attn.h
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ATTN_DECODE_NOALLOC_SCRATCH_BYTES of include/attn.h
 
 
 def attn_decode_append(q, k_new, v_new, k_cache, v_cache, block_table, cache_seqlens, o, lse,

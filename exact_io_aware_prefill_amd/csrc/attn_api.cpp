@@ -52,6 +52,34 @@ int resolve_chunk(int batch, int n_kv_heads, int page_size, int max_blocks, int 
     return (int)chunk;
 }
 
+// Balanced split: with automatic chunking and several sequences, the split kernel
+// runs this many workgroups in all (one resident 8-wave workgroup on each of the
+// 256 compute units; 512 and 1024 measured slower on a batch of 32 mixed lengths),
+// each KV head's share taking an equal part of that head's tokens across sequence
+// boundaries, so a batch of mixed lengths ends with every workgroup busy until
+// about the same time.
+constexpr int kDecodeBalancedWorkgroups = 256;
+
+int balanced_gh(int batch, int n_kv_heads, int chunk_tokens, bool variant)
+{
+    if (chunk_tokens != 0 || batch < 2 || variant || n_kv_heads <= 0) return 0;
+    return kDecodeBalancedWorkgroups / n_kv_heads > 1 ? kDecodeBalancedWorkgroups / n_kv_heads : 1;
+}
+
+// Partials one sequence can have in the balanced split: at most one per workgroup
+// of its KV head, and at most one per unit (one workgroup pass) of its tokens.
+long long balanced_splits(int gh, int head_dim, long long capacity)
+{
+    const long long unit = (long long)attn::decode_split_waves(head_dim) * attn::kDecodeStepTokens;
+    const long long units = (capacity + unit - 1) / unit;
+    return units < gh ? units : gh;
+}
+
+size_t partial_bytes(int batch, int n_q_heads, long long splits, int head_dim)
+{
+    return (size_t)batch * (size_t)n_q_heads * (size_t)splits * (size_t)(head_dim + 1) * 4u;
+}
+
 // Variant options: window -1 (none) or >= 0; softcap 0 (none) or finite > 0.
 bool variant_ok(int window_left, float softcap)
 {
@@ -122,20 +150,26 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
     if (batch == 0) return ATTN_OK;
     if (!q || !k_cache || !v_cache || !seq_lens || !o) return ATTN_ERR_NULL;
     if (append && (!k_new || !v_new)) return ATTN_ERR_NULL;
-    const size_t need = attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim,
-                                                    page_size, max_blocks_per_seq, chunk_tokens);
+    const long long cap = (long long)max_blocks_per_seq * page_size;
+    const long long max_chunks = (cap + chunk - 1) / chunk;
+    int gh = balanced_gh(batch, n_kv_heads, chunk_tokens, window_left >= 0 || softcap > 0.f);
+    const long long bal_splits = gh > 0 ? balanced_splits(gh, head_dim, cap) : 0;
+    // the static scratch takes the per-chunk split when the balanced one's partials do not fit
+    if (static_scratch && gh > 0 && partial_bytes(batch, n_q_heads, bal_splits, head_dim) > attn::kNoAllocScratchBytes)
+        gh = 0;
+    const long long splits = gh > 0 ? bal_splits : max_chunks;
     if (static_scratch) {
-        if (need > attn::kNoAllocScratchBytes) return ATTN_ERR_SCRATCH;
-    } else if (!workspace || workspace_bytes < need) {
-        return ATTN_ERR_WORKSPACE;
+        if (partial_bytes(batch, n_q_heads, splits, head_dim) > attn::kNoAllocScratchBytes) return ATTN_ERR_SCRATCH;
+    } else {
+        const size_t need = attn_decode_workspace_bytes(batch, n_q_heads, n_kv_heads, head_dim, page_size,
+                                                        max_blocks_per_seq, chunk_tokens);
+        if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     }
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
         (!static_scratch && !aligned16(workspace)) || (lse_or_null && !aligned16(lse_or_null)) ||
         (append && (!aligned16(k_new) || !aligned16(v_new))) ||
         (reinterpret_cast<uintptr_t>(descale_k) & 3u) != 0 || (reinterpret_cast<uintptr_t>(descale_v) & 3u) != 0)
         return ATTN_ERR_ALIGN;
-    const long long cap = (long long)max_blocks_per_seq * page_size;
-    const long long max_chunks = (cap + chunk - 1) / chunk;
     if (max_chunks > attn::kMaxSplits || max_chunks * n_kv_heads > attn::kMaxSplitWorkgroups ||
         batch > 65535 || (long long)batch * n_q_heads > attn::kMaxCombineRows)
         return ATTN_ERR_UNSUPPORTED;
@@ -150,7 +184,8 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
     p.page_size = page_size; p.max_blocks = max_blocks_per_seq; p.dtype = dtype;
     p.scale = scale;
     p.chunk = chunk;
-    p.max_chunks = (int)max_chunks;
+    p.max_chunks = (int)splits;
+    p.bal_gh = gh;
     const size_t rows = (size_t)batch * n_q_heads;
     p.k_new = k_new;
     p.v_new = v_new;
@@ -160,7 +195,7 @@ int decode_impl(bool append, const void *q, const void *k_new, const void *v_new
     p.descale_k = descale_k;
     p.descale_v = descale_v;
     p.o_parts = static_cast<float *>(workspace);
-    p.lse_parts = p.o_parts + rows * (size_t)max_chunks * head_dim;
+    p.lse_parts = p.o_parts + rows * (size_t)splits * head_dim;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return run([&] { return attn::launch_decode(p, s); });
 }
@@ -326,7 +361,13 @@ size_t attn_decode_workspace_bytes(int batch, int n_q_heads, int n_kv_heads, int
     if (chunk <= 0) return 0;
     const long long cap = (long long)max_blocks_per_seq * page_size;
     const long long max_chunks = (cap + chunk - 1) / chunk;
-    return (size_t)batch * (size_t)n_q_heads * (size_t)max_chunks * (size_t)(head_dim + 1) * 4u;
+    // the larger of the per-chunk split's partials and (automatic chunking, several
+    // sequences) the balanced split's, so the workspace serves the call with or
+    // without a window or soft-cap
+    const int gh = balanced_gh(batch, n_kv_heads, chunk_tokens, false);
+    const long long splits = gh > 0 && balanced_splits(gh, head_dim, cap) > max_chunks
+                                 ? balanced_splits(gh, head_dim, cap) : max_chunks;
+    return partial_bytes(batch, n_q_heads, splits, head_dim);
 }
 
 int attn_decode(const void *q, const void *k_cache, const void *v_cache,

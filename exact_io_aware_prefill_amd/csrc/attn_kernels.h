@@ -57,7 +57,11 @@ struct DecodeParams {
     int B, Hq, Hkv, head_dim, page_size, max_blocks, dtype;
     float scale;
     int chunk;        // resolved chunk size (tokens)
-    int max_chunks;   // ceil(max_blocks * page_size / chunk)
+    int max_chunks;   // ceil(max_blocks * page_size / chunk), or the balanced split's bound
+    // Balanced split (0: one workgroup per (sequence, KV head, chunk)): bal_gh
+    // workgroups per KV head each take an equal share of the head's tokens, in units
+    // of one workgroup pass; max_chunks then bounds the splits of one sequence
+    int bal_gh = 0;
     float *o_parts;   // [B*Hq, max_chunks, head_dim]
     float *lse_parts; // [B*Hq, max_chunks]
     // in-place append (both NULL for plain decode): rows [B, Hkv, head_dim]
@@ -102,6 +106,9 @@ hipError_t decode_scratch(void **out);
 // Decode tiling constants the host front end needs for validation/sizing.
 constexpr int kDecodeMaxGroup = 16;  // largest supported n_q_heads / n_kv_heads
 constexpr int kDecodeTokenQuantum = 16;  // chunk sizes are multiples of this
+constexpr int kDecodeStepTokens = 32;    // tokens of one wave step of the split kernel
+// waves of one split workgroup: d = 256 runs 4, the others 8
+constexpr int decode_split_waves(int head_dim) { return head_dim == 256 ? 4 : 8; }
 // Largest number of partials per row: a row's partials (splits x head_dim x 4
 // bytes) are addressed through one buffer descriptor with a 31-bit range.
 constexpr long long kMaxSplits = (1LL << 22) - 1;

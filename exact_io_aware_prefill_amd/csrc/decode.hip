@@ -68,8 +68,8 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // Waves per split workgroup: 8 (two per SIMD).  d = 256 holds twice the K/V
 // registers per step, so its workgroups are 4 waves of one per SIMD, with the
 // same bytes in flight per compute unit.
-template <int D> constexpr int split_waves() { return D == 256 ? 4 : 8; }
-constexpr int kStep = 32;  // tokens per wave step (two 16-token blocks)
+template <int D> constexpr int split_waves() { return decode_split_waves(D); }
+constexpr int kStep = kDecodeStepTokens;  // tokens per wave step (two 16-token blocks)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBufferFlags = 0x00020000;       // raw buffer, 32-bit data format
@@ -83,6 +83,14 @@ struct SplitArgs {
     // [B, Hkv, D]; seq_lens then counts the tokens cached before it.
     const uint16_t *k_new, *v_new;
     int Hq, Hkv, group, page, max_blocks, chunk, max_chunks;
+    int B;
+    // Balanced work split (0: one workgroup per (sequence, KV head, chunk)).  With
+    // bal_gh > 0 the grid is Hkv * bal_gh workgroups, KV head fastest; each KV head's
+    // sequences, cut into units of one workgroup pass (256 tokens; 128 at d = 256),
+    // form one list in sequence order, and workgroup r of the head takes units r*R .. r*R + R - 1 of it (R =
+    // ceil(units / bal_gh)), writing one partial per sequence it touches: split k of
+    // sequence b is that of workgroup floor(U_b / R) + k, U_b the sequence's first unit.
+    int bal_gh;
     long long seq_tokens;  // tokens per sequence of the contiguous layout (= capacity)
     float scale_log2;
     // variant only: window (-1: none); soft-cap as x = cap_log2 * tanh(raw * scale / cap)
@@ -106,6 +114,58 @@ __device__ __forceinline__ int attended_tokens(const SplitArgs &a, int b, int &t
     }
     t_new = -1;
     return (int)max(0LL, min(sl, cap));
+}
+
+// Balanced split: units (workgroup passes of `unit` tokens) of sequence b.
+__device__ __forceinline__ int seq_units(const SplitArgs &a, int b, int unit)
+{
+    int t_new;
+    return (attended_tokens(a, b, t_new) + unit - 1) / unit;
+}
+
+__device__ __forceinline__ int wave_sum_int(int x)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Balanced split, per wave (the result is wave-uniform): the units of all sequences
+// and, for the unit `s`, the sequence holding it and that sequence's first unit.
+// Requires s < total (so such a sequence exists).
+__device__ __forceinline__ int bal_total_units(const SplitArgs &a, int unit, int lane)
+{
+    int total = 0;
+    for (int base = 0; base < a.B; base += 64) {
+        const int bb = base + lane;
+        total += wave_sum_int(bb < a.B ? seq_units(a, bb, unit) : 0);
+    }
+    return total;
+}
+
+__device__ __forceinline__ void bal_find(const SplitArgs &a, int unit, int lane, int s, int &b_out, int &u_first)
+{
+    int off = 0;  // units of the sequences before this block of 64
+    for (int base = 0; base < a.B; base += 64) {
+        const int bb = base + lane;
+        const int u = bb < a.B ? seq_units(a, bb, unit) : 0;
+        int incl = u;  // inclusive prefix within the block
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
+        }
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(bb < a.B && off + incl > s);
+        if (hit) {
+            const int j = __builtin_ctzll(hit);
+            b_out = base + j;
+            u_first = off + __shfl(incl - u, j);
+            return;
+        }
+        off += __shfl(incl, 63);
+    }
+    b_out = a.B - 1;  // not reached when s < total
+    u_first = off;
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
@@ -333,9 +393,10 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
 // APPEND selects the in-place append variant, EXT the window / soft-cap variant,
 // KV8 an E4M3 cache (separate instantiations, so the plain decode keeps its
 // register budget).
-template <int D, bool APPEND, bool EXT, bool KV8 = false>
-__global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(SplitArgs a)
+template <int D, bool APPEND, bool EXT, bool KV8 = false, bool BAL = false>
+__global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode_split_kernel(SplitArgs a)
 {
+    static_assert(!BAL || !EXT, "the balanced split has no window or cap variant");
     using Gm = Geo<D>;
     using Lg = KvGeo<D, KV8>;
     constexpr int kWaves = split_waves<D>();
@@ -344,45 +405,47 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
     __shared__ __attribute__((aligned(1024))) char slabs[kWaves * Gm::SLAB];
     __shared__ float ml[2][kWaves][16];
 
+    const int tid = threadIdx.x, lane = tid & 63;
     // the KV heads of one chunk are adjacent workgroups, so the heads' rows of the
     // same tokens (adjacent in memory) are requested at about the same time
-    const int hk = blockIdx.x % a.Hkv, chunk = blockIdx.x / a.Hkv, b = blockIdx.y;
-    // lengths outside [0, capacity] are clamped so no read leaves the sequence's cache
-    int t_new;
-    const int L = attended_tokens(a, b, t_new);
-    const int t_begin = chunk * a.chunk;
-    if (t_begin >= L) return;  // whole workgroup exits together: this chunk is empty
-    const int t_end = min(t_begin + a.chunk, L);
-    const int t_lo = window_start<EXT>(a, L);
+    const int hk = blockIdx.x % a.Hkv;
+    constexpr int UNIT = kWaves * kStep;  // balanced split: tokens of one unit (one workgroup pass)
+    // this workgroup's segment: tokens t_begin .. t_end - 1 of sequence b, partial `split`
+    int b, split, L, t_new, t_begin, t_end;
+    int R = 1, s_next = 0, s_stop = 0, u_b = 0;  // balanced split state (units)
+    if constexpr (!BAL) {
+        split = blockIdx.x / a.Hkv;
+        b = blockIdx.y;
+        // lengths outside [0, capacity] are clamped so no read leaves the sequence's cache
+        L = attended_tokens(a, b, t_new);
+        t_begin = split * a.chunk;
+        if (t_begin >= L) return;  // whole workgroup exits together: this chunk is empty
+        t_end = min(t_begin + a.chunk, L);
+    } else {
+        const int total = __builtin_amdgcn_readfirstlane(bal_total_units(a, UNIT, lane));
+        R = (total + a.bal_gh - 1) / a.bal_gh;
+        const int r = blockIdx.x / a.Hkv;
+        const int s0 = r * R;
+        s_stop = min(total, s0 + R);
+        if (s0 >= s_stop) return;  // whole workgroup: nothing left for it
+        bal_find(a, UNIT, lane, s0, b, u_b);
+        b = __builtin_amdgcn_readfirstlane(b);
+        u_b = __builtin_amdgcn_readfirstlane(u_b);
+        L = attended_tokens(a, b, t_new);
+        const int u_end = min(s_stop, u_b + (L + UNIT - 1) / UNIT);
+        t_begin = (s0 - u_b) * UNIT;
+        t_end = min(L, (u_end - u_b) * UNIT);
+        split = r - u_b / R;
+        s_next = u_end;
+    }
+    const int t_lo = EXT ? window_start<EXT>(a, L) : 0;
     if (EXT && t_end <= t_lo) return;  // the chunk ends before the window: the combine skips it
-    // append: only the workgroup whose chunk holds the new token touches it
-    const bool has_new = APPEND && t_new >= t_begin && t_new < t_end;  // workgroup-uniform
 
-    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, G = lane >> 4;
     const int g = a.group;
     const uint32_t rstride = (uint32_t)a.Hkv * Lg::RB;  // bytes between consecutive tokens of one head
 
-    // query fragments (B operand of S^T = K Q^T); rows >= g are zero padding.
-    // k-step s holds dims 32s + 8G .. +7, or with the E4M3 cache dims
-    // 64(s >> 1) + 16G + 8(s & 1) .. +7, the dims of the lane's converted K bytes.
-    bf16x8_t qf[D / 32];
-    {
-        const uint16_t *qrow = a.q + ((size_t)b * a.Hq + (size_t)hk * g + l16) * D;
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            const int d0 = KV8 ? 64 * (s >> 1) + 16 * G + 8 * (s & 1) : 32 * s + 8 * G;
-            if (l16 < g) u = *reinterpret_cast<const uint4 *>(qrow + d0);
-            qf[s] = as_bf16x8(u);
-        }
-    }
-    // effective scale (the E4M3 cache folds its K descale in) and the V descale
-    const float dkv = (KV8 && a.dk) ? a.dk[(size_t)b * a.Hkv + hk] : 1.f;
-    const float dvv = (KV8 && a.dv) ? a.dv[(size_t)b * a.Hkv + hk] : 1.f;
-    const float sl2 = a.scale_log2 * dkv;
-    const float cap_k = a.cap_k * dkv;  // the cap acts on the scaled score raw * scale * descale_k
 
     LaneOffsets lo;
     lo.l16 = l16;
@@ -419,6 +482,29 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
 
     const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)hk * Lg::RB;
     const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)hk * Lg::RB;
+
+    for (;;) {  // segments: one in the per-chunk split, one or more in the balanced one
+    // append: only the workgroup whose segment holds the new token touches it
+    const bool has_new = APPEND && t_new >= t_begin && t_new < t_end;  // workgroup-uniform
+    // query fragments (B operand of S^T = K Q^T); rows >= g are zero padding.
+    // k-step s holds dims 32s + 8G .. +7, or with the E4M3 cache dims
+    // 64(s >> 1) + 16G + 8(s & 1) .. +7, the dims of the lane's converted K bytes.
+    bf16x8_t qf[D / 32];
+    {
+        const uint16_t *qrow = a.q + ((size_t)b * a.Hq + (size_t)hk * g + l16) * D;
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) {
+            uint4 u = make_uint4(0, 0, 0, 0);
+            const int d0 = KV8 ? 64 * (s >> 1) + 16 * G + 8 * (s & 1) : 32 * s + 8 * G;
+            if (l16 < g) u = *reinterpret_cast<const uint4 *>(qrow + d0);
+            qf[s] = as_bf16x8(u);
+        }
+    }
+    // effective scale (the E4M3 cache folds its K descale in) and the V descale
+    const float dkv = (KV8 && a.dk) ? a.dk[(size_t)b * a.Hkv + hk] : 1.f;
+    const float dvv = (KV8 && a.dv) ? a.dv[(size_t)b * a.Hkv + hk] : 1.f;
+    const float sl2 = a.scale_log2 * dkv;
+    const float cap_k = a.cap_k * dkv;  // the cap acts on the scaled score raw * scale * descale_k
 
     f32x4_t acc[D / 16];
 #pragma unroll
@@ -522,9 +608,25 @@ __global__ __launch_bounds__(split_waves<D>() * 64) void decode_split_kernel(Spl
             for (int w = 0; w < kWaves; ++w)
                 sum += e[w] * *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(slabs + w * Gm::SLAB) +
                                                                  l16 * D + 4 * ((4 * nb + G) ^ l16));
-            *reinterpret_cast<f32x4_t *>(&a.o_parts[(row * a.max_chunks + chunk) * D + 16 * nb + 4 * G]) = sum * inv;
+            *reinterpret_cast<f32x4_t *>(&a.o_parts[(row * a.max_chunks + split) * D + 16 * nb + 4 * G]) = sum * inv;
         }
-        if (wave == 0 && G == 0) a.lse_parts[row * a.max_chunks + chunk] = (M + log2f(Lsum)) * kLn2;
+        if (wave == 0 && G == 0) a.lse_parts[row * a.max_chunks + split] = (M + log2f(Lsum)) * kLn2;
+    }
+    if (!BAL || s_next >= s_stop) break;
+    // balanced split: the next sequence with tokens, from its first unit (sequences
+    // in between with no tokens have no units and are passed over)
+    u_b += (L + UNIT - 1) / UNIT;
+    do {
+        ++b;
+        L = attended_tokens(a, b, t_new);
+    } while (L == 0);
+    b = __builtin_amdgcn_readfirstlane(b);
+    const int u_end = min(s_stop, u_b + (L + UNIT - 1) / UNIT);
+    t_begin = 0;
+    t_end = min(L, (u_end - u_b) * UNIT);
+    split = (blockIdx.x / a.Hkv) - u_b / R;
+    s_next = u_end;
+    __syncthreads();  // every wave is done with the slabs before the next segment's steps
     }
 }
 
@@ -582,12 +684,17 @@ struct CombineArgs {
     int Hq, chunk, max_splits, capacity;
     int append;  // decode with append: tokens = min(seq_lens, capacity - 1) + 1
     int window;  // decode with a window (-1: none): splits before the window's chunk are skipped
+    // decode with the balanced split (bal_gh > 0): sequence b's splits are the
+    // workgroups floor(U_b / R) .. floor((U_b + u_b - 1) / R) of its KV head, with u_b
+    // its units of `unit` tokens, U_b those of the sequences before it, R =
+    // ceil(all units / bal_gh); B sequences
+    int bal_gh, unit, B;
     void *o;
     int o_bf16;
     float *lse;
 };
 
-template <int D>
+template <int D, bool BAL = false>
 __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArgs a)
 {
     constexpr int C4 = D / 4;                    // float4 columns of a row
@@ -607,19 +714,42 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
     auto load_lam = [&](int k) {
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, 4u * (uint32_t)k, 0, 0));
     };
-    // first batch, issued ahead of the split count
+    // first batch, issued ahead of the split count: U splits per thread, or one with
+    // the balanced split, whose rows have few live splits among many slots
+    constexpr int pre = BAL ? 1 : U;
     f32x4_t v[U];
     float lk[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int k = sg + SG * u;
-        v[u] = __builtin_bit_cast(f32x4_t, bload16(ro, (uint32_t)k * (D * 4) + 16u * col, 0));
-        lk[u] = load_lam(k);
+        v[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lk[u] = -INFINITY;
+        if (u < pre) {
+            v[u] = __builtin_bit_cast(f32x4_t, bload16(ro, (uint32_t)k * (D * 4) + 16u * col, 0));
+            lk[u] = load_lam(k);
+        }
     }
     float x0 = load_lam(lane);  // the log-sum-exp pass's first 64 splits
 
     int ns, first = 0;
-    if (a.seq_lens) {
+    if (BAL) {
+        auto units = [&](int b) {
+            const int sl = a.seq_lens[b];
+            const int L = a.append ? max(0, min(sl, a.capacity - 1)) + 1 : max(0, min(sl, a.capacity));
+            return (L + a.unit - 1) / a.unit;
+        };
+        const int bq = (int)(row / a.Hq);
+        int before = 0, total = 0;  // units of the sequences before this row's, and of all
+        for (int base = 0; base < a.B; base += 64) {
+            const int bb = base + lane;
+            const int u = bb < a.B ? units(bb) : 0;
+            before += wave_sum_int(bb < bq ? u : 0);
+            total += wave_sum_int(u);
+        }
+        const int R = max(1, (total + a.bal_gh - 1) / a.bal_gh);
+        const int ub = units(bq);
+        ns = ub > 0 ? (before + ub - 1) / R - before / R + 1 : 0;
+    } else if (a.seq_lens) {
         const int sl = a.seq_lens[row / a.Hq];
         const int L = a.append ? max(0, min(sl, a.capacity - 1)) + 1 : max(0, min(sl, a.capacity));
         ns = (L + a.chunk - 1) / a.chunk;
@@ -633,7 +763,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
     first = min(first, ns);
     auto live = [&](int k) { return k >= first && k < ns; };
 #pragma unroll
-    for (int u = 0; u < U; ++u) lk[u] = live(sg + SG * u) ? lk[u] : -INFINITY;
+    for (int u = 0; u < U; ++u) lk[u] = (u < pre && live(sg + SG * u)) ? lk[u] : -INFINITY;
 
     // Lambda = mx + ln z, z = sum_k exp(lambda_k - mx), mx the largest live lambda:
     // every wave reduces the row on its own, a max pass, then one exponential per
@@ -667,7 +797,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
             const float w = expf(lk[u] - Lam);
             if (w != 0.f) acc += w * v[u];
         }
-        for (int k0 = sg + SG * U; k0 < ns; k0 += SG * U) {
+        for (int k0 = sg + SG * pre; k0 < ns; k0 += SG * U) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int k = k0 + SG * u;
@@ -706,7 +836,10 @@ template <int D>
 hipError_t launch_combine(const CombineArgs &c, int rows, hipStream_t stream)
 {
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(lse_combine_kernel<D>, dim3((unsigned)rows), dim3(kCombineThreads), 0, stream, c);
+    if (c.bal_gh > 0 && c.seq_lens)
+        hipLaunchKernelGGL((lse_combine_kernel<D, true>), dim3((unsigned)rows), dim3(kCombineThreads), 0, stream, c);
+    else
+        hipLaunchKernelGGL((lse_combine_kernel<D, false>), dim3((unsigned)rows), dim3(kCombineThreads), 0, stream, c);
     return hipGetLastError();
 }
 
@@ -741,6 +874,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     a.max_blocks = p.max_blocks;
     a.chunk = p.chunk;
     a.max_chunks = p.max_chunks;
+    a.B = p.B;
     a.seq_tokens = (long long)p.max_blocks * p.page_size;
     a.scale_log2 = p.scale * kLog2e;
     // a window that reaches back past the first slot limits nothing
@@ -748,11 +882,31 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     a.cap_log2 = p.softcap > 0.f ? p.softcap * kLog2e : 0.f;
     a.cap_k = p.softcap > 0.f ? 2.f * kLog2e * p.scale / p.softcap : 0.f;
     const bool ext = a.window >= 0 || p.softcap > 0.f;
-    const dim3 grid((unsigned)((long long)p.max_chunks * p.Hkv), (unsigned)p.B);
+    a.bal_gh = ext ? 0 : p.bal_gh;  // the window and cap variant keeps one workgroup per chunk
+    const dim3 grid = a.bal_gh > 0 ? dim3((unsigned)((long long)a.bal_gh * p.Hkv), 1u)
+                                   : dim3((unsigned)((long long)p.max_chunks * p.Hkv), (unsigned)p.B);
     const bool append = a.k_new != nullptr;
     auto kernel = [&](auto dconst) {
         constexpr int DD = decltype(dconst)::value;
         constexpr int kThreads = split_waves<DD>() * 64;
+        if (a.bal_gh > 0) {  // (never with a window or soft-cap)
+            if constexpr (DD != 256) {
+                if (p.kv_e4m3) {
+                    if (append)
+                        hipLaunchKernelGGL((decode_split_kernel<DD, true, false, true, true>), grid, dim3(kThreads), 0,
+                                           stream, a);
+                    else
+                        hipLaunchKernelGGL((decode_split_kernel<DD, false, false, true, true>), grid, dim3(kThreads), 0,
+                                           stream, a);
+                    return;
+                }
+            }
+            if (append)
+                hipLaunchKernelGGL((decode_split_kernel<DD, true, false, false, true>), grid, dim3(kThreads), 0, stream, a);
+            else
+                hipLaunchKernelGGL((decode_split_kernel<DD, false, false, false, true>), grid, dim3(kThreads), 0, stream, a);
+            return;
+        }
         if constexpr (DD != 256) {
             if (p.kv_e4m3) {
                 if (append)  // (the host allows no window or soft-cap with the E4M3 append)
@@ -793,6 +947,9 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     c.capacity = p.max_blocks * p.page_size;
     c.append = p.k_new != nullptr;
     c.window = a.window;
+    c.bal_gh = a.bal_gh;
+    c.unit = (p.head_dim == 256 ? split_waves<256>() : split_waves<128>()) * kStep;
+    c.B = p.B;
     c.o = p.o;
     c.o_bf16 = 1;
     c.lse = p.lse;
@@ -883,6 +1040,9 @@ hipError_t launch_lse_combine(const CombineParams &p, hipStream_t stream)
     c.capacity = 0;
     c.append = 0;
     c.window = -1;
+    c.bal_gh = 0;
+    c.unit = 1;
+    c.B = 0;
     c.o = p.o;
     c.o_bf16 = p.o_bf16 ? 1 : 0;
     c.lse = p.lse;

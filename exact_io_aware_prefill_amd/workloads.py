@@ -241,6 +241,26 @@ def decode_paged_inputs(seed: int, B: int, Hq: int, Hkv: int, d: int, page_size:
                         page_size, max_blocks, 1.0 / math.sqrt(d), dtype)
 
 
+def decode_paged_layout(seed: int, B: int, Hq: int, d: int, page_size: int, len_min: int, len_max: int):
+    """The query, lengths and block table of decode_paged_inputs(seed, ...) without
+    the cache contents: the same draws in the same order up to the page permutation,
+    so the layout equals that workload's.  Returns (q [B, Hq, d] bf16, block_table
+    [B, max_blocks] int32, seq_lens [B] int32, pool pages, max_blocks)."""
+    rng = np.random.default_rng(seed)
+    q = _draw(rng, (B, Hq, d), BF16)
+    lens = rng.integers(len_min, len_max + 1, size=B).astype(np.int64)
+    pages = (lens + page_size - 1) // page_size
+    pool = int(pages.sum())
+    perm = rng.permutation(pool) if pool > 0 else np.zeros(0, dtype=np.int64)
+    max_blocks = max(1, -(-len_max // page_size))
+    bt = np.full((B, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        bt[b, :pages[b]] = perm[off:off + pages[b]]
+        off += int(pages[b])
+    return q, torch.from_numpy(bt), torch.from_numpy(lens.astype(np.int32)), max(pool, 1), max_blocks
+
+
 @dataclass
 class Fp8DecodeInputs:
     q: torch.Tensor                      # [B, Hq, d] bf16

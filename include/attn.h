@@ -239,7 +239,15 @@ int attn_prefill_fp8_ext(const void *q, const void *k, const void *v, void *o, f
  * split-KV: the first seq_lens[b] tokens of sequence b are cut into chunks of
  * `chunk_tokens`; one workgroup per (sequence, KV head, chunk) computes the
  * chunk's normalised output and log-sum-exp for all query heads of that KV
- * head; a second kernel merges the chunks with the combine rule.
+ * head; a second kernel merges the chunks with the combine rule.  With
+ * chunk_tokens == 0 and batch >= 2 the split is balanced instead: each KV head's
+ * tokens of all sequences, in sequence order and in units of one workgroup pass
+ * (256 tokens; 128 at head_dim 256), are cut into 256 / n_kv_heads equal
+ * contiguous shares (256 workgroups in all, one per compute unit), and a
+ * workgroup writes one partial for every sequence its share touches, so a batch
+ * of mixed lengths keeps every workgroup busy to the end.  The pieces are found
+ * on the device from seq_lens; the combine rule is the same, only the grouping of
+ * the keys (and so the float32 rounding) differs between the two splits.
  *
  *   q        [batch, n_q_heads, head_dim]                      element `dtype`
  *   k_cache, v_cache:
@@ -252,11 +260,12 @@ int attn_prefill_fp8_ext(const void *q, const void *k, const void *v, void *o, f
  *               (already including the new token's own key/value)
  *   o           [batch, n_q_heads, head_dim]  element `dtype` (written)
  *   lse_or_null [batch, n_q_heads] float32 (written when not NULL)
- *   chunk_tokens: 0 = choose from batch, heads and capacity (see
- *               attn_decode_chunk_tokens); otherwise a positive multiple of 16.
+ *   chunk_tokens: 0 = balanced split for batch >= 2, else a chunk chosen from
+ *               batch, heads and capacity (attn_decode_chunk_tokens);
+ *               otherwise a positive multiple of 16 (one workgroup per chunk).
  *   workspace / workspace_bytes: device scratch of at least
- *               attn_decode_workspace_bytes(...) bytes for the per-chunk
- *               partials; contents on entry are ignored.
+ *               attn_decode_workspace_bytes(...) bytes for the partials;
+ *               contents on entry are ignored.
  *   Size limits (else ATTN_ERR_UNSUPPORTED): batch <= 65535, batch*n_q_heads < 2^24,
  *   chunks per sequence < 2^22 and chunks per sequence * n_kv_heads < 2^23.
  *   head_dim in {64, 128, 256}; n_q_heads / n_kv_heads <= 16; dtype ATTN_BF16 only
@@ -282,17 +291,18 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache,
  * The call allocates nothing: no hipMalloc, hipFree or allocating library routine.
  *
  *   Arguments, layouts, arithmetic, limits and results are those of attn_decode
- *   (the same kernels run; the outputs are bit for bit those of attn_decode).
- *   A call whose partials, attn_decode_workspace_bytes(batch, n_q_heads,
- *   n_kv_heads, head_dim, page_size, max_blocks_per_seq, chunk_tokens), exceed
- *   ATTN_DECODE_NOALLOC_SCRATCH_BYTES is ATTN_ERR_SCRATCH (checked on the host,
- *   before any HIP call).  The scratch keeps the last call's partials; nothing in
+ *   (the same kernels run; the outputs are bit for bit those of attn_decode),
+ *   except that a balanced split (chunk_tokens == 0, batch >= 2) whose partials
+ *   do not fit the array runs as the per-chunk split of the automatic chunk size
+ *   (attn_decode_chunk_tokens) instead, whose rounding differs.  A call whose
+ *   partials, per-chunk split included, exceed ATTN_DECODE_NOALLOC_SCRATCH_BYTES
+ *   is ATTN_ERR_SCRATCH (checked on the host, before any HIP call).  The scratch keeps the last call's partials; nothing in
  *   it needs to start at zero (every partial the combine weighs is written first).
  *   Calls on one GPU share that GPU's array: calls that may overlap in time (on
  *   different streams, or from several host threads without ordering) race on it
  *   and must be serialised by the caller, e.g. by issuing them on one stream.
  */
-#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+#define ATTN_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
                         const int32_t *block_table, const int32_t *seq_lens, void *o,
                         float *lse_or_null, int batch, int n_q_heads, int n_kv_heads, int head_dim,
@@ -400,8 +410,9 @@ int attn_decode_fp8_ext(const void *q, const void *k_cache, const void *v_cache,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * attn_decode_chunk_tokens -- the chunk size attn_decode uses for these
- * arguments (resolves chunk_tokens == 0), or a negative status.
+ * attn_decode_chunk_tokens -- the chunk size of the per-chunk split for these
+ * arguments (resolves chunk_tokens == 0; attn_decode uses it for batch 1 and with
+ * a window or soft-cap, the balanced split otherwise), or a negative status.
  */
 int attn_decode_chunk_tokens(int batch, int n_kv_heads, int page_size, int max_blocks_per_seq,
                              int chunk_tokens);
@@ -411,9 +422,12 @@ int attn_decode_chunk_tokens(int batch, int n_kv_heads, int page_size, int max_b
  * needs for its per-chunk partials: each chunk of a sequence's keys yields a
  * normalised partial output and its log-sum-exp, which the separate combine then
  * merges (pofe.ai page, section "Decode: a different bottleneck").  The size is
- *   batch * n_q_heads * ceil(max_blocks_per_seq * page_size / chunk) * (head_dim + 1) * 4
- * (partials are float32), where chunk is the chunk size attn_decode resolves for
- * the same arguments (attn_decode_chunk_tokens); 0 if the arguments are invalid.
+ *   batch * n_q_heads * splits * (head_dim + 1) * 4
+ * (partials are float32), where splits = ceil(max_blocks_per_seq * page_size /
+ * chunk) with chunk the chunk size attn_decode_chunk_tokens resolves; with
+ * chunk_tokens == 0 and batch >= 2, splits is the larger of that and the balanced
+ * split's bound min(256 / n_kv_heads, ceil(capacity / unit)), unit 256 tokens
+ * (128 at head_dim 256).  0 if the arguments are invalid.
  * The arguments are those of attn_decode that fix the chunk count: the capacity
  * max_blocks_per_seq * page_size bounds every sequence's length, and n_kv_heads
  * and page_size enter the automatic chunk choice (chunk_tokens == 0).  Pure host

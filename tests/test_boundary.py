@@ -309,12 +309,20 @@ def test_workspace_formula_and_chunk_choice():
     assert attn.attn_decode_workspace_bytes(1, 28, 4, 128, 16, 2048, 512) == 1 * 28 * 64 * 129 * 4
     assert attn.attn_decode_workspace_bytes(3, 8, 2, 64, 16, 10, 48) == 3 * 8 * 4 * 65 * 4
     assert attn.attn_decode_chunk_tokens(1, 4, 16, 2048, 512) == 512
-    # automatic choice: a multiple of 256 tokens between 256 and 2048
-    for B, Hkv, maxb in [(1, 4, 2048), (32, 8, 2048), (1, 1, 1), (128, 8, 64), (4, 2, 100000)]:
+    # automatic choice: a multiple of 256 tokens between 256 and 2048; with several
+    # sequences the workspace also holds the balanced split's partials, at most
+    # min(256 / Hkv, ceil(capacity / unit)) per sequence, unit 256 tokens (128 at d = 256)
+    for B, Hkv, maxb in [(1, 4, 2048), (32, 8, 2048), (1, 1, 1), (128, 8, 64), (4, 2, 100000), (3, 32, 8)]:
         c = attn.attn_decode_chunk_tokens(B, Hkv, 16, maxb, 0)
         assert 256 <= c <= 2048 and c % 256 == 0
-        assert attn.attn_decode_workspace_bytes(B, 4 * Hkv, Hkv, 128, 16, maxb, 0) == \
-            B * 4 * Hkv * (-(-(maxb * 16) // c)) * 129 * 4
+        for d, unit in ((128, 256), (256, 128)):
+            splits = -(-(maxb * 16) // c)
+            if B >= 2:
+                splits = max(splits, min(max(1, 256 // Hkv), -(-(maxb * 16) // unit)))
+            assert attn.attn_decode_workspace_bytes(B, 4 * Hkv, Hkv, d, 16, maxb, 0) == \
+                B * 4 * Hkv * splits * (d + 1) * 4, (B, Hkv, maxb, d)
+    # the c5 batch: 32 splits of the balanced split (256 / 8 KV heads) against 16 chunks of 2048
+    assert attn.attn_decode_workspace_bytes(32, 32, 8, 128, 16, 2048, 0) == 32 * 32 * 32 * 129 * 4
     assert attn.attn_decode_workspace_bytes(1, 28, 4, 128, 16, 2048, 24) == 0
     with pytest.raises(attn.AttnError):
         attn.attn_decode_chunk_tokens(1, 4, 16, 2048, 20)
@@ -445,3 +453,15 @@ def test_decode_fp8_append_host_checks():
     assert call(ws=0) == attn.ATTN_ERR_WORKSPACE
     assert call(wsb=16) == attn.ATTN_ERR_WORKSPACE
     assert call(B=0) == attn.ATTN_OK
+
+
+def test_paged_layout_helper_matches_the_paged_workload():
+    """bench.py's paged decode leg takes its lengths and page placement from
+    decode_paged_layout; they must be the paged workload's own (same seeded draws)."""
+    from exact_io_aware_prefill_amd import workloads as W
+    import torch
+    for seed, B, lo, hi in ((5, 4, 100, 300), (9, 7, 1, 64)):
+        q, bt, sl, pool, mb = W.decode_paged_layout(seed, B, 8, 64, 16, lo, hi)
+        x = W.decode_paged_inputs(seed, B, 8, 2, 64, 16, lo, hi)
+        assert torch.equal(q, x.q) and torch.equal(bt, x.block_table) and torch.equal(sl, x.seq_lens)
+        assert pool == x.k_cache.shape[0] and mb == x.max_blocks

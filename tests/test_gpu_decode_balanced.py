@@ -1,0 +1,90 @@
+"""The decode's balanced split (automatic chunking, two or more sequences): each KV
+head's tokens of all sequences are cut into equal contiguous shares, one per
+workgroup, across sequence boundaries, and the combine merges every sequence's
+pieces (pofe.ai page, section "Decode: a different bottleneck": split-KV over the
+keys, merged by the combine rule).  Cases that stress the share boundaries:
+empty sequences inside the batch, more than 64 sequences (the device-side unit
+scan runs over several blocks of 64), many short sequences per workgroup, and
+all head sizes, against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_io_aware_prefill_amd import workloads as W
+from gpu_common import BF16_TOL, check, dev, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def attn():
+    from exact_io_aware_prefill_amd import attn as a  # raises if libattn.so is missing
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return a
+
+
+def run(attn, x, chunk=0):
+    o, lse = attn.decode(dev(x.q), dev(x.k_cache), dev(x.v_cache), dev(x.block_table), dev(x.seq_lens),
+                         x.page_size, x.max_blocks, x.scale, chunk)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def reference(x):
+    return oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale, x.page_size, x.max_blocks)
+
+
+RAGGED = [0, 1, 255, 256, 257, 4000, 0, 9000, 31, 17000]
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("g", [1, 4, 7])
+@pytest.mark.parametrize("paged", [False, True])
+def test_balanced_decode_ragged_batch(attn, d, g, paged):
+    say("case: balanced decode d=%d g=%d paged=%s lengths=%s" % (d, g, paged, RAGGED))
+    Hkv, cap = 2, 17024
+    if paged:
+        x = W.decode_paged_inputs(900 + d + g, len(RAGGED), g * Hkv, Hkv, d, 16, 1, cap, lengths=RAGGED)
+    else:
+        x = W.decode_contiguous_inputs(900 + d + g, len(RAGGED), g * Hkv, Hkv, cap, d, seq_lens=RAGGED)
+    o, lse = run(attn, x)
+    for b, L in enumerate(RAGGED):
+        if L == 0:  # an empty sequence: output 0, log-sum-exp -inf
+            assert (o[b] == 0).all() and torch.isneginf(lse[b]).all()
+    ro, rl = reference(x)
+    check("balanced d=%d g=%d paged=%d" % (d, g, paged), o, lse, ro, rl, BF16_TOL)
+
+
+@pytest.mark.parametrize("B,Hkv,g,d,lmax", [(200, 32, 1, 64, 600), (100, 2, 4, 128, 3000), (65, 8, 4, 128, 2048)])
+def test_balanced_decode_many_sequences(attn, B, Hkv, g, d, lmax):
+    """More than 64 sequences (several scan blocks), many of them per workgroup share
+    (32 KV heads leave 8 workgroups per head), zero lengths among them."""
+    rng = np.random.default_rng(B + Hkv)
+    lens = rng.integers(0, lmax + 1, size=B)
+    lens[::17] = 0
+    say("case: balanced decode B=%d Hkv=%d g=%d d=%d, lengths up to %d" % (B, Hkv, g, d, lmax))
+    x = W.decode_paged_inputs(1000 + B, B, g * Hkv, Hkv, d, 16, 1, lmax, lengths=lens.tolist())
+    o, lse = run(attn, x)
+    ro, rl = reference(x)
+    check("balanced many B=%d Hkv=%d" % (B, Hkv), o, lse, ro, rl, BF16_TOL)
+
+
+def test_balanced_and_per_chunk_splits_agree(attn):
+    """The two splits group the keys differently; both are the same exact decode, so
+    they agree with each other within the float32 rounding of their merges."""
+    x = W.decode_paged_inputs(1234, len(RAGGED), 8, 2, 128, 16, 1, 17024, lengths=RAGGED)
+    ob, lb = run(attn, x, 0)
+    oc, lc = run(attn, x, 512)
+    fin = torch.isfinite(lc)
+    assert torch.equal(torch.isneginf(lb), torch.isneginf(lc))
+    assert (ob.float() - oc.float()).abs().max().item() <= 1e-2
+    assert (lb[fin] - lc[fin]).abs().max().item() <= 1e-5
+
+
+def test_balanced_decode_is_deterministic(attn):
+    """Fixed shares and a fixed merge order: two calls give the same bits."""
+    x = W.decode_paged_inputs(77, len(RAGGED), 28, 4, 128, 16, 1, 17024, lengths=RAGGED)
+    o1, l1 = run(attn, x)
+    o2, l2 = run(attn, x)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
