@@ -422,16 +422,43 @@ __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode
         if (t_begin >= L) return;  // whole workgroup exits together: this chunk is empty
         t_end = min(t_begin + a.chunk, L);
     } else {
-        const int total = __builtin_amdgcn_readfirstlane(bal_total_units(a, UNIT, lane));
-        R = (total + a.bal_gh - 1) / a.bal_gh;
         const int r = blockIdx.x / a.Hkv;
-        const int s0 = r * R;
-        s_stop = min(total, s0 + R);
-        if (s0 >= s_stop) return;  // whole workgroup: nothing left for it
-        bal_find(a, UNIT, lane, s0, b, u_b);
-        b = __builtin_amdgcn_readfirstlane(b);
-        u_b = __builtin_amdgcn_readfirstlane(u_b);
-        L = attended_tokens(a, b, t_new);
+        int s0;
+        if (a.B <= 64) {
+            // one load per lane: lane j holds sequence j's length, units and their
+            // inclusive prefix, which give the total, the first sequence of this
+            // workgroup's share and its length without further loads
+            int tn = -1;
+            const int Lj = lane < a.B ? attended_tokens(a, lane, tn) : 0;
+            const int u = (Lj + UNIT - 1) / UNIT;
+            int incl = u;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+            R = (total + a.bal_gh - 1) / a.bal_gh;
+            s0 = r * R;
+            s_stop = min(total, s0 + R);
+            if (s0 >= s_stop) return;  // whole workgroup: nothing left for it
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < a.B && incl > s0);
+            const int j = __builtin_ctzll(hit);
+            b = __builtin_amdgcn_readfirstlane(j);
+            u_b = __builtin_amdgcn_readfirstlane(__shfl(incl - u, j));
+            L = __builtin_amdgcn_readfirstlane(__shfl(Lj, j));
+            t_new = __builtin_amdgcn_readfirstlane(__shfl(tn, j));
+        } else {
+            const int total = __builtin_amdgcn_readfirstlane(bal_total_units(a, UNIT, lane));
+            R = (total + a.bal_gh - 1) / a.bal_gh;
+            s0 = r * R;
+            s_stop = min(total, s0 + R);
+            if (s0 >= s_stop) return;  // whole workgroup: nothing left for it
+            bal_find(a, UNIT, lane, s0, b, u_b);
+            b = __builtin_amdgcn_readfirstlane(b);
+            u_b = __builtin_amdgcn_readfirstlane(u_b);
+            L = attended_tokens(a, b, t_new);
+        }
         const int u_end = min(s_stop, u_b + (L + UNIT - 1) / UNIT);
         t_begin = (s0 - u_b) * UNIT;
         t_end = min(L, (u_end - u_b) * UNIT);
