@@ -35,10 +35,12 @@ TRAFFIC = {
     "prefill": {"file": os.path.join(ROOT, "profiles", "prefill_bf16_n16384_traffic.json"),
                 "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel<128, false, 1>"},
     "decode": {"file": os.path.join(ROOT, "profiles", "decode_split_s32768_traffic.json"),
-               "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel<128, false, false, false>",
+               "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel<128, false, false, false, false>",
                # the 32k decode's dispatches only (256 workgroups of 512 threads), not the
                # paged batch's, which run the same kernel on a larger grid
                "grid": 256 * 512},
+    "paged": {"file": os.path.join(ROOT, "profiles", "decode_split_paged_b32_traffic.json"),
+              "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel<128, false, false, false, true>"},
     "fp8": {"file": os.path.join(ROOT, "profiles", "prefill_fp8_n16384_traffic.json"),
             "src": os.path.join(CSRC, "prefill_fp8.hip"), "kernel": "prefill_fp8_kernel<128, false, false>"},
 }
@@ -468,7 +470,7 @@ def main():
                    "dtype": "fp8-e4m3 cache, bf16 q/o",
                    "roofline": {"bound": "hbm", "achieved": bytes8 / (ms8 * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": bytes8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                                "kernels": "decode_split_kernel<128, false, false, true> + lse_combine_kernel<128>",
+                                "kernels": "decode_split_kernel<128, false, false, true, false> + lse_combine_kernel<128, false>",
                                 "algorithmic_bytes_per_launch": bytes8},
                    "speedup_vs_bf16_cache": dec_bb_ms / ms8}
 
@@ -534,8 +536,8 @@ def main():
                             "cached_tokens": int(psl.to(torch.int64).sum()), "chunk_tokens": pchunk,
                             "values": "lengths and block table of the paged workload; K/V drawn on the device"},
                  "roofline": {"bound": "hbm", "achieved": pgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": pgbs / PEAK_HBM_GBS, "traffic": None,
-                              "kernels": "decode_split_kernel<128, false, false, false> + lse_combine_kernel<128>",
+                              "frac": pgbs / PEAK_HBM_GBS, "traffic": measured_traffic("paged"),
+                              "kernels": "decode_split_kernel<128, false, false, false, true> + lse_combine_kernel<128, true>",
                               "algorithmic_bytes_per_launch": pbytes},
                  "floor": {"read_ms": pread_ms, "read_GBps": 2 * pool_bytes / (pread_ms * 1e-3) / 1e9,
                            "workgroups": pgrid,
@@ -587,7 +589,7 @@ def main():
                          "avg_ms_events_around_each_call": dec_ms,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode"),
-                                      "kernels": "decode_split_kernel<128, false, false, false> + lse_combine_kernel<128>",
+                                      "kernels": "decode_split_kernel<128, false, false, false, false> + lse_combine_kernel<128, false>",
                                       "algorithmic_bytes_per_launch": decode_bytes}}
         if floor is not None:
             floor["call_over_read_plus_launch"] = dec_bb_ms / floor["read_plus_launch_ms"]
