@@ -511,149 +511,155 @@ __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode
     const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)hk * Lg::RB;
 
     for (;;) {  // segments: one in the per-chunk split, one or more in the balanced one
-    // append: only the workgroup whose segment holds the new token touches it
-    const bool has_new = APPEND && t_new >= t_begin && t_new < t_end;  // workgroup-uniform
-    // query fragments (B operand of S^T = K Q^T); rows >= g are zero padding.
-    // k-step s holds dims 32s + 8G .. +7, or with the E4M3 cache dims
-    // 64(s >> 1) + 16G + 8(s & 1) .. +7, the dims of the lane's converted K bytes.
-    bf16x8_t qf[D / 32];
-    {
-        const uint16_t *qrow = a.q + ((size_t)b * a.Hq + (size_t)hk * g + l16) * D;
+        // append: only the workgroup whose segment holds the new token touches it
+        const bool has_new = APPEND && t_new >= t_begin && t_new < t_end;  // workgroup-uniform
+        // query fragments (B operand of S^T = K Q^T); rows >= g are zero padding.
+        // k-step s holds dims 32s + 8G .. +7, or with the E4M3 cache dims
+        // 64(s >> 1) + 16G + 8(s & 1) .. +7, the dims of the lane's converted K bytes.
+        bf16x8_t qf[D / 32];
+        {
+            const uint16_t *qrow = a.q + ((size_t)b * a.Hq + (size_t)hk * g + l16) * D;
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            const int d0 = KV8 ? 64 * (s >> 1) + 16 * G + 8 * (s & 1) : 32 * s + 8 * G;
-            if (l16 < g) u = *reinterpret_cast<const uint4 *>(qrow + d0);
-            qf[s] = as_bf16x8(u);
+            for (int s = 0; s < D / 32; ++s) {
+                uint4 u = make_uint4(0, 0, 0, 0);
+                const int d0 = KV8 ? 64 * (s >> 1) + 16 * G + 8 * (s & 1) : 32 * s + 8 * G;
+                if (l16 < g) u = *reinterpret_cast<const uint4 *>(qrow + d0);
+                qf[s] = as_bf16x8(u);
+            }
         }
-    }
-    // effective scale (the E4M3 cache folds its K descale in) and the V descale
-    const float dkv = (KV8 && a.dk) ? a.dk[(size_t)b * a.Hkv + hk] : 1.f;
-    const float dvv = (KV8 && a.dv) ? a.dv[(size_t)b * a.Hkv + hk] : 1.f;
-    const float sl2 = a.scale_log2 * dkv;
-    const float cap_k = a.cap_k * dkv;  // the cap acts on the scaled score raw * scale * descale_k
+        // effective scale (the E4M3 cache folds its K descale in) and the V descale
+        const float dkv = (KV8 && a.dk) ? a.dk[(size_t)b * a.Hkv + hk] : 1.f;
+        const float dvv = (KV8 && a.dv) ? a.dv[(size_t)b * a.Hkv + hk] : 1.f;
+        const float sl2 = a.scale_log2 * dkv;
+        const float cap_k = a.cap_k * dkv;  // the cap acts on the scaled score raw * scale * descale_k
 
-    f32x4_t acc[D / 16];
+        f32x4_t acc[D / 16];
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb)
+        for (int nb = 0; nb < D / 16; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[nb][i] = 0.f;
-    float m = -INFINITY, l = 0.f;
+            for (int i = 0; i < 4; ++i) acc[nb][i] = 0.f;
+        float m = -INFINITY, l = 0.f;
 
-    // This wave's steps start at t_begin + (wave + 8j) * 32, two in flight.  Loads
-    // are issued unconditionally (a step past the chunk has empty descriptors and
-    // reads nothing), so the number of loads in flight is the same on every path
-    // and each step waits only for its own loads.
-    const int stride = kWaves * kStep;
-    int tb = t_begin + wave * kStep;
-    if (APPEND && has_new) {
-        // Write the new rows into the cache slot first: this workgroup is the only
-        // reader of that slot, and its loads below are issued after the barrier,
-        // which orders them after these stores.  A row is Lg::RB bytes (bf16, or
-        // the E4M3 codes of an 8-bit cache, which the caller quantised with that
-        // cache's descales), copied as RB / 16 16-byte chunks.
-        constexpr int NCH = Lg::RB / 16;
-        const long long row = token_index(a, b, t_new) * a.Hkv + hk;
-        const size_t src = ((size_t)b * a.Hkv + hk) * Lg::RB;
-        if (tid < NCH)
-            reinterpret_cast<uint4 *>(const_cast<char *>(reinterpret_cast<const char *>(a.k)) + row * Lg::RB)[tid] =
-                reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(a.k_new) + src)[tid];
-        else if (tid < 2 * NCH)
-            reinterpret_cast<uint4 *>(const_cast<char *>(reinterpret_cast<const char *>(a.v)) + row * Lg::RB)[tid - NCH] =
-                reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(a.v_new) + src)[tid - NCH];
-        __syncthreads();
-    }
-    // with a window, skip this wave's steps that end before it starts
-    if (EXT && tb + kStep <= t_lo) tb += ((t_lo - tb - kStep) / stride + 1) * stride;
-    if constexpr (!KV8) {
-        StepRegs<D, KV8> r0, r1;
-        issue_step<D, KV8>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
-        while (tb < t_end) {
-            issue_step<D, KV8>(a, r1, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-            consume_step<D, EXT, KV8>(a, r0, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
-            tb += stride;
-            if (tb >= t_end) break;
-            issue_step<D, KV8>(a, r0, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-            consume_step<D, EXT, KV8>(a, r1, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
-            tb += stride;
+        // This wave's steps start at t_begin + (wave + 8j) * 32, two in flight.  Loads
+        // are issued unconditionally (a step past the chunk has empty descriptors and
+        // reads nothing), so the number of loads in flight is the same on every path
+        // and each step waits only for its own loads.
+        const int stride = kWaves * kStep;
+        int tb = t_begin + wave * kStep;
+        if (APPEND && has_new) {
+            // Write the new rows into the cache slot first: this workgroup is the only
+            // reader of that slot, and its loads below are issued after the barrier,
+            // which orders them after these stores.  A row is Lg::RB bytes (bf16, or
+            // the E4M3 codes of an 8-bit cache, which the caller quantised with that
+            // cache's descales), copied as RB / 16 16-byte chunks.
+            constexpr int NCH = Lg::RB / 16;
+            const long long row = token_index(a, b, t_new) * a.Hkv + hk;
+            const size_t src = ((size_t)b * a.Hkv + hk) * Lg::RB;
+            if (tid < NCH)
+                reinterpret_cast<uint4 *>(const_cast<char *>(reinterpret_cast<const char *>(a.k)) + row * Lg::RB)[tid] =
+                    reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(a.k_new) + src)[tid];
+            else if (tid < 2 * NCH)
+                reinterpret_cast<uint4 *>(const_cast<char *>(reinterpret_cast<const char *>(a.v)) +
+                                          row * Lg::RB)[tid - NCH] =
+                    reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(a.v_new) + src)[tid - NCH];
+            __syncthreads();
         }
-    } else {
-        // A ring of NS register sets, NS - 1 steps issued ahead.  An E4M3 step is
-        // half the bytes of a bf16 one, yet three or four steps in flight measured
-        // slower than two (32k cache: 13.9 -> 14.5 / 14.7 us), so NS stays 2.
-        constexpr int NS = 2;
-        StepRegs<D, KV8> r[NS];
+        // with a window, skip this wave's steps that end before it starts
+        if (EXT && tb + kStep <= t_lo) tb += ((t_lo - tb - kStep) / stride + 1) * stride;
+        if constexpr (!KV8) {
+            StepRegs<D, KV8> r0, r1;
+            issue_step<D, KV8>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
+            while (tb < t_end) {
+                issue_step<D, KV8>(a, r1, kbase, vbase, b, tb + stride, t_end, rstride, lo);
+                consume_step<D, EXT, KV8>(a, r0, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
+                tb += stride;
+                if (tb >= t_end) break;
+                issue_step<D, KV8>(a, r0, kbase, vbase, b, tb + stride, t_end, rstride, lo);
+                consume_step<D, EXT, KV8>(a, r1, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
+                tb += stride;
+            }
+        } else {
+            // A ring of NS register sets, NS - 1 steps issued ahead.  An E4M3 step is
+            // half the bytes of a bf16 one, yet three or four steps in flight measured
+            // slower than two (32k cache: 13.9 -> 14.5 / 14.7 us), so NS stays 2.
+            constexpr int NS = 2;
+            StepRegs<D, KV8> r[NS];
 #pragma unroll
-        for (int j = 0; j < NS - 1; ++j) issue_step<D, KV8>(a, r[j], kbase, vbase, b, tb + j * stride, t_end, rstride, lo);
-        bool more = tb < t_end;
-        while (more) {
+            for (int j = 0; j < NS - 1; ++j)
+                issue_step<D, KV8>(a, r[j], kbase, vbase, b, tb + j * stride, t_end, rstride, lo);
+            bool more = tb < t_end;
+            while (more) {
 #pragma unroll
-            for (int j = 0; j < NS; ++j) {
-                if (more) {
-                    issue_step<D, KV8>(a, r[(j + NS - 1) % NS], kbase, vbase, b, tb + (NS - 1) * stride, t_end,
-                                       rstride, lo);
-                    consume_step<D, EXT, KV8>(a, r[j], slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
-                    tb += stride;
-                    more = tb < t_end;
+                for (int j = 0; j < NS; ++j) {
+                    if (more) {
+                        issue_step<D, KV8>(a, r[(j + NS - 1) % NS], kbase, vbase, b, tb + (NS - 1) * stride, t_end,
+                                           rstride, lo);
+                        consume_step<D, EXT, KV8>(a, r[j], slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread,
+                                                  sl2, cap_k);
+                        tb += stride;
+                        more = tb < t_end;
+                    }
                 }
             }
         }
-    }
 
-    // ---- merge the eight wave states (combine rule) ------------------------------
-    // row sum of query l16 over the four token groups of the lane's column
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
-    if (G == 0) {
-        ml[0][wave][l16] = m;  // -inf for a wave that saw no token
-        ml[1][wave][l16] = lt;
-    }
-    // The wave's slab now holds its unscaled output as [query][D] floats, the
-    // 16-byte column chunk c of query row r at chunk c ^ r: the 16 rows a store
-    // or load instruction touches per pass then fall on distinct banks.
-    float *wo = reinterpret_cast<float *>(slab);
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) *reinterpret_cast<f32x4_t *>(&wo[l16 * D + 4 * ((4 * nb + G) ^ l16)]) = acc[nb];
-    __syncthreads();
-    // wave w merges d-blocks w, w + kWaves, ... of all waves and writes the chunk's partial
-    if (wave < D / 16 && l16 < g) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[0][w][l16]);
-        float Lsum = 0.f, e[kWaves];
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            e[w] = __builtin_amdgcn_exp2f(ml[0][w][l16] - M);  // 0 for a wave that saw no token
-            Lsum += e[w] * ml[1][w][l16];
+        // ---- merge the eight wave states (combine rule) ------------------------------
+        // row sum of query l16 over the four token groups of the lane's column
+        float lt = l + __shfl_xor(l, 16);
+        lt += __shfl_xor(lt, 32);
+        if (G == 0) {
+            ml[0][wave][l16] = m;  // -inf for a wave that saw no token
+            ml[1][wave][l16] = lt;
         }
-        const size_t row = (size_t)b * a.Hq + (size_t)hk * g + l16;
-        const float inv = dvv / Lsum;  // Lsum >= 1: the row's largest term is exp2(0)
+        // The wave's slab now holds its unscaled output as [query][D] floats, the
+        // 16-byte column chunk c of query row r at chunk c ^ r: the 16 rows a store
+        // or load instruction touches per pass then fall on distinct banks.
+        float *wo = reinterpret_cast<float *>(slab);
 #pragma unroll
-        for (int nb = wave; nb < D / 16; nb += kWaves) {
-            f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+        for (int nb = 0; nb < D / 16; ++nb)
+            *reinterpret_cast<f32x4_t *>(&wo[l16 * D + 4 * ((4 * nb + G) ^ l16)]) = acc[nb];
+        __syncthreads();
+        // wave w merges d-blocks w, w + kWaves, ... of all waves and writes the chunk's partial
+        if (wave < D / 16 && l16 < g) {
+            float M = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w)
-                sum += e[w] * *reinterpret_cast<const f32x4_t *>(reinterpret_cast<const float *>(slabs + w * Gm::SLAB) +
-                                                                 l16 * D + 4 * ((4 * nb + G) ^ l16));
-            *reinterpret_cast<f32x4_t *>(&a.o_parts[(row * a.max_chunks + split) * D + 16 * nb + 4 * G]) = sum * inv;
+            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml[0][w][l16]);
+            float Lsum = 0.f, e[kWaves];
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                e[w] = __builtin_amdgcn_exp2f(ml[0][w][l16] - M);  // 0 for a wave that saw no token
+                Lsum += e[w] * ml[1][w][l16];
+            }
+            const size_t row = (size_t)b * a.Hq + (size_t)hk * g + l16;
+            const float inv = dvv / Lsum;  // Lsum >= 1: the row's largest term is exp2(0)
+#pragma unroll
+            for (int nb = wave; nb < D / 16; nb += kWaves) {
+                f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w)
+                    sum += e[w] * *reinterpret_cast<const f32x4_t *>(
+                                      reinterpret_cast<const float *>(slabs + w * Gm::SLAB) +
+                                                                     l16 * D + 4 * ((4 * nb + G) ^ l16));
+                *reinterpret_cast<f32x4_t *>(&a.o_parts[(row * a.max_chunks + split) * D + 16 * nb + 4 * G]) =
+                    sum * inv;
+            }
+            if (wave == 0 && G == 0) a.lse_parts[row * a.max_chunks + split] = (M + log2f(Lsum)) * kLn2;
         }
-        if (wave == 0 && G == 0) a.lse_parts[row * a.max_chunks + split] = (M + log2f(Lsum)) * kLn2;
-    }
-    if (!BAL || s_next >= s_stop) break;
-    // balanced split: the next sequence with tokens, from its first unit (sequences
-    // in between with no tokens have no units and are passed over)
-    u_b += (L + UNIT - 1) / UNIT;
-    do {
-        ++b;
-        L = attended_tokens(a, b, t_new);
-    } while (L == 0);
-    b = __builtin_amdgcn_readfirstlane(b);
-    const int u_end = min(s_stop, u_b + (L + UNIT - 1) / UNIT);
-    t_begin = 0;
-    t_end = min(L, (u_end - u_b) * UNIT);
-    split = (blockIdx.x / a.Hkv) - u_b / R;
-    s_next = u_end;
-    __syncthreads();  // every wave is done with the slabs before the next segment's steps
+        if (!BAL || s_next >= s_stop) break;
+        // balanced split: the next sequence with tokens, from its first unit (sequences
+        // in between with no tokens have no units and are passed over)
+        u_b += (L + UNIT - 1) / UNIT;
+        do {
+            ++b;
+            L = attended_tokens(a, b, t_new);
+        } while (L == 0);
+        b = __builtin_amdgcn_readfirstlane(b);
+        const int u_end = min(s_stop, u_b + (L + UNIT - 1) / UNIT);
+        t_begin = 0;
+        t_end = min(L, (u_end - u_b) * UNIT);
+        split = (blockIdx.x / a.Hkv) - u_b / R;
+        s_next = u_end;
+        __syncthreads();  // every wave is done with the slabs before the next segment's steps
     }
 }
 
@@ -929,9 +935,11 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
                 }
             }
             if (append)
-                hipLaunchKernelGGL((decode_split_kernel<DD, true, false, false, true>), grid, dim3(kThreads), 0, stream, a);
+                hipLaunchKernelGGL((decode_split_kernel<DD, true, false, false, true>), grid, dim3(kThreads), 0,
+                                   stream, a);
             else
-                hipLaunchKernelGGL((decode_split_kernel<DD, false, false, false, true>), grid, dim3(kThreads), 0, stream, a);
+                hipLaunchKernelGGL((decode_split_kernel<DD, false, false, false, true>), grid, dim3(kThreads), 0,
+                                   stream, a);
             return;
         }
         if constexpr (DD != 256) {
