@@ -638,8 +638,8 @@ __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w)
                     sum += e[w] * *reinterpret_cast<const f32x4_t *>(
-                                      reinterpret_cast<const float *>(slabs + w * Gm::SLAB) +
-                                                                     l16 * D + 4 * ((4 * nb + G) ^ l16));
+                                      reinterpret_cast<const float *>(slabs + w * Gm::SLAB) + l16 * D +
+                                      4 * ((4 * nb + G) ^ l16));
                 *reinterpret_cast<f32x4_t *>(&a.o_parts[(row * a.max_chunks + split) * D + 16 * nb + 4 * G]) =
                     sum * inv;
             }
