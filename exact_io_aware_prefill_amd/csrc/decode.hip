@@ -205,6 +205,17 @@ __device__ __forceinline__ int slab_swz(int r)
     return KV8 ? base + (D >= 128 ? (r & 1) : ((r >> 1) & 1)) : base;
 }
 
+// K slab (bf16 cache): chunk c of key row r at slot c ^ kslab_swz(r).  Rows of
+// 256 bytes or more (d >= 128) permute by r & 15, rows of 128 bytes (two per bank
+// line) by (r >> 1) & 7.  Both the row stores (16 lanes = one row's 16 chunks, or
+// two rows' 8) and the score operand reads (16 lanes = chunk 4ks + G of 16
+// consecutive rows) then hit 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int kslab_swz(int r)
+{
+    return D >= 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
 template <int D>
 struct Geo {
     static constexpr int RB = D * 2;          // bytes of one token row of one head
@@ -253,7 +264,7 @@ struct LaneOffsets {
     int l16, vtok;
 };
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool KSL = false>
 __device__ __forceinline__ void issue_step(const SplitArgs &a, StepRegs<D, KV8> &s, const char *kbase,
                                            const char *vbase, int b, int tb, int t_end, uint32_t rstride,
                                            const LaneOffsets &lo)
@@ -267,9 +278,24 @@ __device__ __forceinline__ void issue_step(const SplitArgs &a, StepRegs<D, KV8> 
         const uint32_t nrec = live ? 16u * rstride : 0u;
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + row0 * Gm::RB, nrec);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + row0 * Gm::RB, nrec);
-        const uint32_t ko = (t0 + lo.l16 < t_end) ? lo.k : kOutOfRange;
+        if constexpr (!KSL) {
+            // each lane loads its own score operand's bytes (key row l16): 16 rows of
+            // 64 bytes per instruction (bf16), or their E4M3 codes
+            const uint32_t ko = (t0 + lo.l16 < t_end) ? lo.k : kOutOfRange;
 #pragma unroll
-        for (int st = 0; st < Gm::KL; ++st) s.k[blk][st] = bload16(rk, ko + 64u * st, 0);
+            for (int st = 0; st < Gm::KL; ++st) s.k[blk][st] = bload16(rk, ko + 64u * st, 0);
+        } else {
+            // K rows read as V rows are (RPI whole rows per instruction), which streams
+            // faster; the step moves them through the wave's K slab into the operand
+            // layout
+            static_assert(Gm::KL * Gm::RPI == 16, "one 16-token block of K rows per block's loads");
+#pragma unroll
+            for (int st = 0; st < Gm::KL; ++st) {
+                const int tok = Gm::RPI * st + lo.vtok;  // token within the block
+                const uint32_t ko = (t0 + tok < t_end) ? lo.v : kOutOfRange;
+                s.k[blk][st] = bload16(rk, ko, (uint32_t)(Gm::RPI * st) * rstride);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < Gm::VIB; ++i) {
             const int tok = Gm::RPI * i + lo.vtok;  // token within the block
@@ -298,14 +324,27 @@ __device__ __forceinline__ float soft_cap_log2(float raw, float cap_log2, float 
 // 64j + 16G ..) become the bf16 operands of k-steps 2j and 2j+1, so its query
 // fragments take the same dims (see the kernel); V rows are converted to bf16 on
 // their way into the slab, as two 16-byte chunks per loaded chunk.
-template <int D, bool EXT, bool KV8>
+template <int D, bool EXT, bool KV8, bool KSL = false>
 __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<D, KV8> &s, char *slab,
                                              const bf16x8_t *qf, f32x4_t *acc, float &m, float &l, int tb,
                                              int t_lo, int t_end, int G, const uint32_t *vstore, uint32_t vread,
-                                             float scale_log2, float cap_k)
+                                             float scale_log2, float cap_k, char *kslab, uint32_t kstore,
+                                             uint32_t kread)
 {
     using Gm = Geo<D>;
     using Lg = KvGeo<D, KV8>;
+    if constexpr (KSL) {
+        // K rows into the wave's K slab (in order with this wave's other LDS accesses,
+        // so after the previous step's operand reads).  Load i holds rows RPI i + vtok,
+        // whose permutation is that of row vtok XOR that of row RPI i, so its offset is
+        // the lane's row-vtok offset XOR a constant, plus RPI i rows.
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < Lg::KL; ++i)
+                *reinterpret_cast<uint4 *>(kslab + (blk * 16 + Lg::RPI * i) * Gm::RB +
+                                           (kstore ^ (16u * kslab_swz<D>(Lg::RPI * i)))) = s.k[blk][i];
+    }
     // scores of the two 16-token blocks
     f32x4_t st[2];
 #pragma unroll
@@ -320,6 +359,9 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
                 const uint2 a0 = e4m3x4_to_bf16((ks & 1) ? w.z : w.x);
                 const uint2 a1 = e4m3x4_to_bf16((ks & 1) ? w.w : w.y);
                 kf = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
+            } else if constexpr (KSL) {
+                // key row 16 blk + l16, chunk 4 ks + G, at slot (4 ks + G) ^ swz = 4 ks ^ (G ^ swz)
+                kf = *reinterpret_cast<const bf16x8_t *>(kslab + blk * 16 * Gm::RB + (kread ^ (64u * ks)));
             } else {
                 kf = as_bf16x8(s.k[blk][ks]);
             }
@@ -397,12 +439,17 @@ template <int D, bool APPEND, bool EXT, bool KV8 = false, bool BAL = false>
 __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode_split_kernel(SplitArgs a)
 {
     static_assert(!BAL || !EXT, "the balanced split has no window or cap variant");
+    // K rows through a wave-private LDS slab (bf16 cache, balanced split, d >= 128):
+    // whole-row loads stream faster than loads in the score operand's layout, which
+    // pays off on long shares; the per-chunk split's short chunks keep K in registers
+    constexpr bool KSL = BAL && !KV8 && D >= 128;
     using Gm = Geo<D>;
     using Lg = KvGeo<D, KV8>;
     constexpr int kWaves = split_waves<D>();
     // one slab per wave; reused at the end for the eight waves' [16][D] float outputs
     static_assert(Gm::SLAB == 16 * D * 4, "slab must hold a wave's 16 x D float output");
     __shared__ __attribute__((aligned(1024))) char slabs[kWaves * Gm::SLAB];
+    __shared__ __attribute__((aligned(1024))) char kslabs[KSL ? kWaves * Gm::SLAB : 16];
     __shared__ float ml[2][kWaves][16];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -506,6 +553,12 @@ __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode
     // swaps the two chunks of a pair, so d-block nb is a XOR by 32nb
     const int vrow = 4 * G + (l16 >> 2), vq = l16 & 3;
     const uint32_t vread = (uint32_t)(vrow * Gm::RB + 16 * ((vq >> 1) ^ slab_swz<D, KV8>(vrow)) + 8 * (vq & 1));
+    // K slab: this lane stores chunk vchunk of rows RPI i + vtok of each block (offset
+    // of row vtok here) and reads chunk 4 ks + G of row l16 (both blocks' rows, 16
+    // apart, share the permutation)
+    char *kslab = KSL ? kslabs + wave * Gm::SLAB : kslabs;
+    const uint32_t kstore = (uint32_t)(lo.vtok * Gm::RB + 16 * (vchunk ^ kslab_swz<D>(lo.vtok)));
+    const uint32_t kread = (uint32_t)(l16 * Gm::RB + 16 * (G ^ kslab_swz<D>(l16)));
 
     const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)hk * Lg::RB;
     const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)hk * Lg::RB;
@@ -568,14 +621,16 @@ __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode
         if (EXT && tb + kStep <= t_lo) tb += ((t_lo - tb - kStep) / stride + 1) * stride;
         if constexpr (!KV8) {
             StepRegs<D, KV8> r0, r1;
-            issue_step<D, KV8>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
+            issue_step<D, KV8, KSL>(a, r0, kbase, vbase, b, tb, t_end, rstride, lo);
             while (tb < t_end) {
-                issue_step<D, KV8>(a, r1, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-                consume_step<D, EXT, KV8>(a, r0, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
+                issue_step<D, KV8, KSL>(a, r1, kbase, vbase, b, tb + stride, t_end, rstride, lo);
+                consume_step<D, EXT, KV8, KSL>(a, r0, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k,
+                                      kslab, kstore, kread);
                 tb += stride;
                 if (tb >= t_end) break;
-                issue_step<D, KV8>(a, r0, kbase, vbase, b, tb + stride, t_end, rstride, lo);
-                consume_step<D, EXT, KV8>(a, r1, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k);
+                issue_step<D, KV8, KSL>(a, r0, kbase, vbase, b, tb + stride, t_end, rstride, lo);
+                consume_step<D, EXT, KV8, KSL>(a, r1, slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread, sl2, cap_k,
+                                      kslab, kstore, kread);
                 tb += stride;
             }
         } else {
@@ -586,16 +641,16 @@ __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode
             StepRegs<D, KV8> r[NS];
 #pragma unroll
             for (int j = 0; j < NS - 1; ++j)
-                issue_step<D, KV8>(a, r[j], kbase, vbase, b, tb + j * stride, t_end, rstride, lo);
+                issue_step<D, KV8, KSL>(a, r[j], kbase, vbase, b, tb + j * stride, t_end, rstride, lo);
             bool more = tb < t_end;
             while (more) {
 #pragma unroll
                 for (int j = 0; j < NS; ++j) {
                     if (more) {
-                        issue_step<D, KV8>(a, r[(j + NS - 1) % NS], kbase, vbase, b, tb + (NS - 1) * stride, t_end,
+                        issue_step<D, KV8, KSL>(a, r[(j + NS - 1) % NS], kbase, vbase, b, tb + (NS - 1) * stride, t_end,
                                            rstride, lo);
-                        consume_step<D, EXT, KV8>(a, r[j], slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread,
-                                                  sl2, cap_k);
+                        consume_step<D, EXT, KV8, KSL>(a, r[j], slab, qf, acc, m, l, tb, t_lo, t_end, G, vstore, vread,
+                                                  sl2, cap_k, kslab, kstore, kread);
                         tb += stride;
                         more = tb < t_end;
                     }
