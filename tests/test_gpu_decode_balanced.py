@@ -88,3 +88,63 @@ def test_balanced_decode_is_deterministic(attn):
     o1, l1 = run(attn, x)
     o2, l2 = run(attn, x)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _random_case(seed):
+    """A seeded random batch shape for the balanced split: batch 2..160 (fewer for large
+    heads and capacities), KV heads 1..32,
+    group 1..16 (at most 16 query heads per KV head), d 64/128/256, lengths 0..capacity
+    with zeros among them, paged or contiguous."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(2, 161))
+    Hkv = int(rng.choice([1, 2, 4, 8, 32]))
+    g = int(rng.choice([1, 2, 4, 7, 16]))
+    d = int(rng.choice([64, 128, 256]))
+    cap = int(rng.choice([256, 1024, 3000]))
+    # at most about 200 MB of K/V at full capacity, so the fp64 oracle finishes in seconds
+    B = max(2, min(B, int(200e6 // (cap * Hkv * d * 4))))
+    lens = rng.integers(0, cap + 1, size=B)
+    lens[rng.random(B) < 0.15] = 0
+    paged = bool(rng.integers(0, 2))
+    return B, Hkv, g, d, cap, lens.tolist(), paged
+
+
+@pytest.mark.parametrize("seed", list(range(24)))
+def test_balanced_decode_random_shapes(attn, seed):
+    B, Hkv, g, d, cap, lens, paged = _random_case(seed)
+    say("case: balanced decode random seed=%d B=%d Hkv=%d g=%d d=%d cap=%d paged=%s" % (seed, B, Hkv, g, d, cap, paged))
+    if paged:
+        x = W.decode_paged_inputs(5000 + seed, B, g * Hkv, Hkv, d, 16, 1, cap, lengths=lens)
+    else:
+        capc = -(-cap // 16) * 16
+        x = W.decode_contiguous_inputs(5000 + seed, B, g * Hkv, Hkv, capc, d, seq_lens=lens)
+    o, lse = run(attn, x)
+    ro, rl = reference(x)
+    check("balanced random seed=%d" % seed, o, lse, ro, rl, BF16_TOL)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("paged", [False, True])
+def test_balanced_decode_append(attn, d, paged):
+    """The in-place append under the balanced split: the new rows land in their slots
+    (bit for bit) and the query attends them, for a batch whose sequences cross
+    workgroup shares; compared with the oracle's append."""
+    lens = [0, 1, 255, 256, 4000, 9000, 31, 2000, 700]
+    B, Hkv, g, cap = len(lens), 4, 4, 9216
+    say("case: balanced decode append d=%d paged=%s" % (d, paged))
+    seed = 7000 + d + paged
+    if paged:
+        x = W.decode_paged_inputs(seed, B, g * Hkv, Hkv, d, 16, 1, cap, lengths=[L + 1 for L in lens])
+    else:
+        x = W.decode_contiguous_inputs(seed, B, g * Hkv, Hkv, cap, d, seq_lens=lens)
+    cached = torch.tensor(lens, dtype=torch.int32)
+    kn, vn = W.decode_new_rows(seed + 1, B, Hkv, d)
+    kc, vc = dev(x.k_cache), dev(x.v_cache)
+    o, lse = attn.decode_append(dev(x.q), dev(kn), dev(vn), kc, vc, dev(x.block_table), dev(cached), x.page_size,
+                                x.max_blocks, x.scale, 0)
+    torch.cuda.synchronize()
+    ro, rl, rk, rv = oracle.decode_append(x.q, kn, vn, x.k_cache, x.v_cache, x.block_table, cached, x.scale,
+                                          x.page_size, x.max_blocks)
+    check("balanced append d=%d paged=%d" % (d, paged), o, lse, ro, rl, BF16_TOL)
+    assert np.array_equal(kc.cpu().double().numpy(), rk), "K cache after the append differs"
+    assert np.array_equal(vc.cpu().double().numpy(), rv), "V cache after the append differs"
