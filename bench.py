@@ -46,6 +46,7 @@ TRAFFIC = {
 }
 COPY_BYTES = 1 << 30  # reference dispatch for the counters: a 1 GiB device-to-device copy
 READ_GRIDS = (256, 512, 1024, 2048, 4096, 8192)  # workgroup counts of the floor's read sweep
+BALANCED_WORKGROUPS = 256  # the decode's balanced split: workgroups in all (include/attn.h, attn_decode)
 N_KV_COPIES = 8
 
 
@@ -494,7 +495,7 @@ def main():
         pqd, pbtd, psld = pq.to(dev), pbt.to(dev), psl.to(dev)
         pod = torch.empty_like(pqd)
         pld = torch.empty((pc["B"], pc["Hq"]), dtype=torch.float32, device=dev)
-        pchunk = attn.attn_decode_chunk_tokens(pc["B"], pc["Hkv"], pc["page_size"], pmb, 0)
+        pchunk = 0  # automatic: the balanced split, for a batch
         pws = torch.empty(attn.attn_decode_workspace_bytes(pc["B"], pc["Hq"], pc["Hkv"], pc["d"], pc["page_size"],
                                                            pmb, pchunk), dtype=torch.uint8, device=dev)
         pscale = 1.0 / math.sqrt(pc["d"])
@@ -518,7 +519,7 @@ def main():
         pms = time_back_to_back(run_paged, preps)
         pbytes = (int(psl.to(torch.int64).sum()) * pc["Hkv"] * pc["d"] * 2 * 2 + pqd.numel() * 2 * 2
                   + pld.numel() * 4)
-        pgrid = pc["B"] * pc["Hkv"] * -(-(pmb * pc["page_size"]) // pchunk)
+        pgrid = pc["Hkv"] * max(1, BALANCED_WORKGROUPS // pc["Hkv"])  # the balanced split's grid
         psink = torch.zeros(4 * pgrid, dtype=torch.int32, device=dev)
         pool_bytes = pk.numel() * 2
         pread_ms = time_back_to_back(lambda: attn.attn_bench_stream_read(pk, pv, pgrid, psink), preps)
@@ -533,7 +534,8 @@ def main():
                  "timing": "%d back-to-back calls between two events" % preps,
                  "config": {"workload": pc["name"], "batch": pc["B"], "q_heads": pc["Hq"], "kv_heads": pc["Hkv"],
                             "head_dim": pc["d"], "page_size": pc["page_size"],
-                            "cached_tokens": int(psl.to(torch.int64).sum()), "chunk_tokens": pchunk,
+                            "cached_tokens": int(psl.to(torch.int64).sum()),
+                            "split": "balanced (equal shares of each KV head's tokens, %d workgroups)" % pgrid,
                             "values": "lengths and block table of the paged workload; K/V drawn on the device"},
                  "roofline": {"bound": "hbm", "achieved": pgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": pgbs / PEAK_HBM_GBS, "traffic": measured_traffic("paged"),
@@ -542,8 +544,8 @@ def main():
                  "floor": {"read_ms": pread_ms, "read_GBps": 2 * pool_bytes / (pread_ms * 1e-3) / 1e9,
                            "workgroups": pgrid,
                            "what": "one kernel reading the whole K and V page pools once (%d bytes; 16-byte loads, "
-                                   "grid-stride, the split kernel's %d workgroups of 256 threads), %d back-to-back "
-                                   "calls between two events" % (2 * pool_bytes, pgrid, preps),
+                                   "grid-stride, %d workgroups of 256 threads, the split kernel's count), %d "
+                                   "back-to-back calls between two events" % (2 * pool_bytes, pgrid, preps),
                            "call_over_read": pms / pread_ms,
                            "best_read": {"ms": psweep[pbest], "GBps": 2 * pool_bytes / (psweep[pbest] * 1e-3) / 1e9,
                                          "workgroups": pbest, "grids_tried": list(READ_GRIDS)}}}
