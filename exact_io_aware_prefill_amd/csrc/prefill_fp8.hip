@@ -32,12 +32,15 @@
 //     in float32 from the unrounded values, so the LSE does not see the
 //     8-bit rounding; O does, by at most 2^-4 relative per term (and 2^-10
 //     absolute below the normal range).
-//   * Step t issues QK(t+1) into a second score buffer and PV(t-1), then the
+//   * Step t issues QK(t+1) into a second score buffer, then PV(t-1) with the
 //     softmax of tile t; scheduling groups spread the softmax's vector work
-//     over the eight products (two LDS reads and ten VALU instructions after
-//     each; twenty, which bunched the softmax's ~110 instructions behind the
-//     first products, measured 1.6% slower), so the matrix cores and the VALUs
-//     overlap inside the wave.  Two waves per SIMD (about 205 VGPRs).
+//     over the four P*V products (two LDS reads and ten VALU instructions
+//     after each), so the matrix cores and the VALUs overlap inside the wave.
+//     The QK products stay in a block of their own (the guard on the last
+//     step); pulling them into the interleave as well measured 0-1% slower.
+//     Two waves per SIMD (about 205 VGPRs) cover each other's QK bursts; a
+//     wave raises its priority over the P*V + softmax block (+2 to +3% at
+//     8k-16k prompts, +8% at 4k), as the bf16 kernel does.
 //   * K and V tiles go straight from memory into LDS (buffer loads with the LDS
 //     destination bit), double-buffered.  16-byte chunk c of key row r sits at
 //     slot c ^ swz(r); the permutations make the K operand reads (16 rows per
@@ -416,6 +419,9 @@ __global__ __launch_bounds__(kWaves * 64, fp8_waves_per_simd<D>()) void prefill_
                 }
         }
         if (t + 1 < ntiles) qk_tile<D>(Sn, Kn, qf, kad0, kad1);
+        // raised wave priority over the P*V products and the softmax: the SIMD's
+        // other wave, in its QK products or at the barrier, yields the issue slots
+        __builtin_amdgcn_s_setprio(1);
         pv_tile<D>(acc, Vp, Pp, vad);
         float rs = softmax_tile(S, sl2, m * sl2, Pc);
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
@@ -425,6 +431,7 @@ __global__ __launch_bounds__(kWaves * 64, fp8_waves_per_simd<D>()) void prefill_
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (__builtin_amdgcn_ballot_w64(m == -INFINITY || rs > kMaxLaneSum)) {
             asm volatile("" ::"v"(Pc));
             float mx = -INFINITY;
