@@ -638,28 +638,78 @@ __global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : waves_per_simd<D>())
     }
 
     // ---- epilogue: O = acc / l, LSE = m * scale + ln l ---------------------------------
-#pragma unroll
-    for (int bb = 0; bb < kBlocks; ++bb) {
-        const int qrow = wrow0 + 32 * bb + l32;
-        const float lt =
-            l[bb] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, l[bb])));
-        if (qrow < N) {
+    if constexpr (KS > 1) {
+        // key split (short prompts): O goes through the wave's own tile buffer in LDS, free
+        // once the groups have merged, so the global stores write whole rows, 16 bytes per
+        // lane (a store in accumulator order touches 32 rows per instruction, this one
+        // 64 / (d / 8)): -0.6 us per workgroup, +4% at 2k prompts.  The plain kernel keeps
+        // the direct stores: the staging's registers cost its main loop operand lookahead.
+        static_assert(kBlocks == 1, "one 32-row query block per wave");
+        char *const obuf = reinterpret_cast<char *>(wave == 0   ? &KB0s[0][0]
+                                                    : wave == 1 ? &KB1s[0][0]
+                                                    : wave == 2 ? &VB0s[0][0]
+                                                                : &VB1s[0][0]);
+        constexpr int RB = 2 * D;  // bytes per staged row
+        constexpr int CH = D / 8;  // 16-byte chunks per row
+        // chunk c of row r sits at slot c ^ oswz(r): the 32 rows a store instruction writes
+        // and the rows a load instruction reads then spread over the banks
+        auto oswz = [](int row) { return D == 64 ? ((row >> 1) & 7) : (row & 15); };
+        {
+            const int qrow = wrow0 + l32;
+            const float lt =
+                l[0] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, l[0])));
             const float inv = 1.f / lt;
-            uint16_t *orow = a.o + qo + (long long)qrow * a.q_row;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
                 for (int ig = 0; ig < 4; ++ig) {
-                    const int d0 = 32 * db + 8 * ig + 4 * hh;
-                    const bf16x2_t lo = {(__bf16)(acc[bb][db][4 * ig + 0] * inv), (__bf16)(acc[bb][db][4 * ig + 1] * inv)};
-                    const bf16x2_t hi = {(__bf16)(acc[bb][db][4 * ig + 2] * inv), (__bf16)(acc[bb][db][4 * ig + 3] * inv)};
+                    // dims 32 db + 8 ig + 4 hh .. + 3 of row l32: 16-byte chunk 4 db + ig, half hh
+                    const bf16x2_t lo = {(__bf16)(acc[0][db][4 * ig + 0] * inv), (__bf16)(acc[0][db][4 * ig + 1] * inv)};
+                    const bf16x2_t hi = {(__bf16)(acc[0][db][4 * ig + 2] * inv), (__bf16)(acc[0][db][4 * ig + 3] * inv)};
                     uint2 pk;
                     pk.x = __builtin_bit_cast(uint32_t, lo);
                     pk.y = __builtin_bit_cast(uint32_t, hi);
-                    *reinterpret_cast<uint2 *>(orow + d0) = pk;
+                    *reinterpret_cast<uint2 *>(obuf + l32 * RB + 16 * ((4 * db + ig) ^ oswz(l32)) + 8 * hh) = pk;
                 }
             }
-            if (hh == 0) a.lse[lse_off + qrow] = (mb[bb] + log2f(lt)) * kLn2;  // mb * ln 2 = max * |scale|
+            if (qrow < N && hh == 0) a.lse[lse_off + qrow] = (mb[0] + log2f(lt)) * kLn2;  // mb * ln 2 = max * |scale|
+        }
+        {
+            constexpr int LPR = CH;        // lanes per row
+            constexpr int RPI = 64 / LPR;  // rows per instruction
+            const int c = lane % LPR;
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int rr = RPI * k + lane / LPR;  // the wave's own rows: no barrier needed
+                const uint4 v = *reinterpret_cast<const uint4 *>(obuf + rr * RB + 16 * (c ^ oswz(rr)));
+                const int qrow = wrow0 + rr;
+                if (qrow < N) *reinterpret_cast<uint4 *>(a.o + qo + (long long)qrow * a.q_row + 8 * c) = v;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int bb = 0; bb < kBlocks; ++bb) {
+            const int qrow = wrow0 + 32 * bb + l32;
+            const float lt =
+                l[bb] + __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, l[bb])));
+            if (qrow < N) {
+                const float inv = 1.f / lt;
+                uint16_t *orow = a.o + qo + (long long)qrow * a.q_row;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                    for (int ig = 0; ig < 4; ++ig) {
+                        const int d0 = 32 * db + 8 * ig + 4 * hh;
+                        const bf16x2_t lo = {(__bf16)(acc[bb][db][4 * ig + 0] * inv), (__bf16)(acc[bb][db][4 * ig + 1] * inv)};
+                        const bf16x2_t hi = {(__bf16)(acc[bb][db][4 * ig + 2] * inv), (__bf16)(acc[bb][db][4 * ig + 3] * inv)};
+                        uint2 pk;
+                        pk.x = __builtin_bit_cast(uint32_t, lo);
+                        pk.y = __builtin_bit_cast(uint32_t, hi);
+                        *reinterpret_cast<uint2 *>(orow + d0) = pk;
+                    }
+                }
+                if (hh == 0) a.lse[lse_off + qrow] = (mb[bb] + log2f(lt)) * kLn2;  // mb * ln 2 = max * |scale|
+            }
         }
     }
 }
