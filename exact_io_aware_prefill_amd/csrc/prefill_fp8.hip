@@ -34,8 +34,10 @@
 //     absolute below the normal range).
 //   * Step t issues QK(t+1) into a second score buffer, then PV(t-1) with the
 //     softmax of tile t; scheduling groups spread the softmax's vector work
-//     over the four P*V products (two LDS reads and ten VALU instructions
-//     after each), so the matrix cores and the VALUs overlap inside the wave.
+//     over the four P*V products (after each, the four transpose reads of the
+//     next product's V operand and twelve VALU instructions; two reads and ten
+//     VALU measured 2% slower), so the matrix cores and the VALUs overlap
+//     inside the wave.
 //     The QK products stay in a block of their own (the guard on the last
 //     step); pulling them into the interleave as well measured 0-1% slower.
 //     Two waves per SIMD (about 205 VGPRs) cover each other's QK bursts; a
@@ -428,8 +430,8 @@ __global__ __launch_bounds__(kWaves * 64, fp8_waves_per_simd<D>()) void prefill_
 #pragma unroll
         for (int i = 0; i < (D / 64) * 2 + D / 32; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
         }
         __builtin_amdgcn_s_setprio(0);
         if (__builtin_amdgcn_ballot_w64(m == -INFINITY || rs > kMaxLaneSum)) {
