@@ -205,15 +205,16 @@ __device__ __forceinline__ int slab_swz(int r)
     return KV8 ? base + (D >= 128 ? (r & 1) : ((r >> 1) & 1)) : base;
 }
 
-// K slab (bf16 cache): chunk c of key row r at slot c ^ kslab_swz(r).  Rows of
-// 256 bytes or more (d >= 128) permute by r & 15, rows of 128 bytes (two per bank
-// line) by (r >> 1) & 7.  Both the row stores (16 lanes = one row's 16 chunks, or
-// two rows' 8) and the score operand reads (16 lanes = chunk 4ks + G of 16
-// consecutive rows) then hit 16 distinct 16-byte bank groups.
-template <int D>
+// K slab: chunk c of key row r at slot c ^ kslab_swz(r), rows as stored in the
+// cache (2D bytes for bf16, D bytes of E4M3 codes).  Rows of 256 bytes or more
+// permute by r & 15, rows of 128 bytes (two per bank line) by (r >> 1) & 7.  Both
+// the row stores (16 lanes = one row's 16 chunks, or two rows' 8) and the score
+// operand reads (16 lanes = one chunk of 16 consecutive rows) then hit 16 distinct
+// 16-byte bank groups.
+template <int D, bool KV8 = false>
 __device__ __forceinline__ int kslab_swz(int r)
 {
-    return D >= 128 ? (r & 15) : ((r >> 1) & 7);
+    return (KV8 ? D : 2 * D) >= 256 ? (r & 15) : ((r >> 1) & 7);
 }
 
 template <int D>
@@ -342,8 +343,8 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int i = 0; i < Lg::KL; ++i)
-                *reinterpret_cast<uint4 *>(kslab + (blk * 16 + Lg::RPI * i) * Gm::RB +
-                                           (kstore ^ (16u * kslab_swz<D>(Lg::RPI * i)))) = s.k[blk][i];
+                *reinterpret_cast<uint4 *>(kslab + (blk * 16 + Lg::RPI * i) * Lg::RB +
+                                           (kstore ^ (16u * kslab_swz<D, KV8>(Lg::RPI * i)))) = s.k[blk][i];
     }
     // scores of the two 16-token blocks
     f32x4_t st[2];
@@ -355,7 +356,11 @@ __device__ __forceinline__ void consume_step(const SplitArgs &a, const StepRegs<
         for (int ks = 0; ks < D / 32; ++ks) {
             bf16x8_t kf;
             if constexpr (KV8) {
-                const uint4 w = s.k[blk][ks >> 1];
+                // E4M3 codes of dims 64 (ks >> 1) + 16G .. + 15 of key row 16 blk + l16: chunk
+                // 4 (ks >> 1) + G, from the slab at slot (4 (ks >> 1) + G) ^ swz
+                const uint4 w = KSL ? *reinterpret_cast<const uint4 *>(kslab + blk * 16 * Lg::RB +
+                                                                      (kread ^ (64u * (ks >> 1))))
+                                    : s.k[blk][ks >> 1];
                 const uint2 a0 = e4m3x4_to_bf16((ks & 1) ? w.z : w.x);
                 const uint2 a1 = e4m3x4_to_bf16((ks & 1) ? w.w : w.y);
                 kf = as_bf16x8(make_uint4(a0.x, a0.y, a1.x, a1.y));
@@ -439,10 +444,10 @@ template <int D, bool APPEND, bool EXT, bool KV8 = false, bool BAL = false>
 __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode_split_kernel(SplitArgs a)
 {
     static_assert(!BAL || !EXT, "the balanced split has no window or cap variant");
-    // K rows through a wave-private LDS slab (bf16 cache, balanced split, d >= 128):
-    // whole-row loads stream faster than loads in the score operand's layout, which
-    // pays off on long shares; the per-chunk split's short chunks keep K in registers
-    constexpr bool KSL = BAL && !KV8 && D >= 128;
+    // K rows through a wave-private LDS slab (balanced split, d >= 128): whole-row
+    // loads stream faster than loads in the score operand's layout, which pays off on
+    // long shares; the per-chunk split's short chunks keep K in registers
+    constexpr bool KSL = BAL && D >= 128;
     using Gm = Geo<D>;
     using Lg = KvGeo<D, KV8>;
     constexpr int kWaves = split_waves<D>();
@@ -557,8 +562,8 @@ __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode
     // of row vtok here) and reads chunk 4 ks + G of row l16 (both blocks' rows, 16
     // apart, share the permutation)
     char *kslab = KSL ? kslabs + wave * Gm::SLAB : kslabs;
-    const uint32_t kstore = (uint32_t)(lo.vtok * Gm::RB + 16 * (vchunk ^ kslab_swz<D>(lo.vtok)));
-    const uint32_t kread = (uint32_t)(l16 * Gm::RB + 16 * (G ^ kslab_swz<D>(l16)));
+    const uint32_t kstore = (uint32_t)(lo.vtok * Lg::RB + 16 * (vchunk ^ kslab_swz<D, KV8>(lo.vtok)));
+    const uint32_t kread = (uint32_t)(l16 * Lg::RB + 16 * (G ^ kslab_swz<D, KV8>(l16)));
 
     const char *kbase = reinterpret_cast<const char *>(a.k) + (size_t)hk * Lg::RB;
     const char *vbase = reinterpret_cast<const char *>(a.v) + (size_t)hk * Lg::RB;

@@ -4,8 +4,8 @@ workgroup, across sequence boundaries, and the combine merges every sequence's
 pieces (pofe.ai page, section "Decode: a different bottleneck": split-KV over the
 keys, merged by the combine rule).  Cases that stress the share boundaries:
 empty sequences inside the batch, more than 64 sequences (the device-side unit
-scan runs over several blocks of 64), many short sequences per workgroup, and
-all head sizes, against the fp64 oracle."""
+scan runs over several blocks of 64), many short sequences per workgroup, all
+head sizes, and the E4M3 cache, against the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -68,6 +68,61 @@ def test_balanced_decode_many_sequences(attn, B, Hkv, g, d, lmax):
     o, lse = run(attn, x)
     ro, rl = reference(x)
     check("balanced many B=%d Hkv=%d" % (B, Hkv), o, lse, ro, rl, BF16_TOL)
+
+
+def run_fp8(attn, x, chunk=0):
+    o, lse = attn.decode_fp8(dev(x.q), dev(x.k_cache8), dev(x.v_cache8), dev(x.block_table), dev(x.seq_lens),
+                             x.page_size, x.max_blocks, dev(x.descale_k), dev(x.descale_v), x.scale, chunk)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def reference_fp8(x):
+    return oracle.decode_fp8(x.q, x.k_cache8, x.v_cache8, x.descale_k, x.descale_v, x.block_table, x.seq_lens,
+                             x.scale, x.page_size, x.max_blocks)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 7])
+@pytest.mark.parametrize("paged", [False, True])
+def test_balanced_fp8_cache_decode_ragged_batch(attn, d, g, paged):
+    """The balanced split over an E4M3 cache (d = 128 moves K rows through the wave's
+    LDS slab as the bf16 cache does): the ragged batch with empty sequences, against
+    the oracle's plain decode of the dequantised cache."""
+    say("case: balanced fp8-cache decode d=%d g=%d paged=%s lengths=%s" % (d, g, paged, RAGGED))
+    x = W.decode_fp8_inputs(1900 + d + g, len(RAGGED), g * 2, 2, d, RAGGED, 17024, paged)
+    o, lse = run_fp8(attn, x)
+    for b, L in enumerate(RAGGED):
+        if L == 0:
+            assert (o[b] == 0).all() and torch.isneginf(lse[b]).all()
+    ro, rl = reference_fp8(x)
+    check("balanced fp8 d=%d g=%d paged=%d" % (d, g, paged), o, lse, ro, rl, BF16_TOL)
+
+
+def test_balanced_fp8_cache_decode_many_sequences(attn):
+    """More than 64 sequences over an E4M3 cache: several unit-scan blocks, many short
+    sequences per workgroup share, zero lengths among them."""
+    B, Hkv, g, d, lmax = 90, 4, 4, 128, 2500
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, lmax + 1, size=B)
+    lens[::13] = 0
+    say("case: balanced fp8-cache decode B=%d Hkv=%d g=%d d=%d, lengths up to %d" % (B, Hkv, g, d, lmax))
+    x = W.decode_fp8_inputs(1950, B, g * Hkv, Hkv, d, lens.tolist(), lmax, True)
+    o, lse = run_fp8(attn, x)
+    ro, rl = reference_fp8(x)
+    check("balanced fp8 many B=%d" % B, o, lse, ro, rl, BF16_TOL)
+
+
+def test_balanced_fp8_cache_decode_matches_per_chunk_split(attn):
+    """Same E4M3 cache, balanced split against explicit 256-token chunks: the same exact
+    decode, within the float32 rounding of the two merges."""
+    x = W.decode_fp8_inputs(1960, len(RAGGED), 8, 2, 128, RAGGED, 17024, True)
+    o0, l0 = run_fp8(attn, x, 0)
+    o1, l1 = run_fp8(attn, x, 256)
+    assert (o0.float() - o1.float()).abs().max().item() <= 1e-2
+    live = torch.isfinite(l1)
+    assert torch.equal(torch.isfinite(l0), live)
+    assert (l0[live] - l1[live]).abs().max().item() <= 1e-4
 
 
 def test_balanced_and_per_chunk_splits_agree(attn):
