@@ -33,7 +33,7 @@ CSRC = os.path.join(ROOT, "exact_io_aware_prefill_amd", "csrc")
 # valid while the kernel source they were taken on is unchanged (sha256 recorded)
 TRAFFIC = {
     "prefill": {"file": os.path.join(ROOT, "profiles", "prefill_bf16_n16384_traffic.json"),
-                "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel<128, false, 1>"},
+                "src": os.path.join(CSRC, "prefill_bf16.hip"), "kernel": "prefill_bf16_kernel<128, false, 1, 3>"},
     "decode": {"file": os.path.join(ROOT, "profiles", "decode_split_s32768_traffic.json"),
                "src": os.path.join(CSRC, "decode.hip"), "kernel": "decode_split_kernel<128, false, false, false, false>",
                # the 32k decode's dispatches only (256 workgroups of 512 threads), not the
@@ -582,7 +582,7 @@ def main():
         out["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
                            "traffic": measured_traffic("prefill"),
-                           "kernel": "prefill_bf16_kernel<128, false, 1>", "avg_launch_ms": pre_ms,
+                           "kernel": "prefill_bf16_kernel<128, false, 1, 3>", "avg_launch_ms": pre_ms,
                            "algorithmic_flop_per_launch": prefill_flop}
     if do_d:
         gbs = decode_bytes / (dec_bb_ms * 1e-3) / 1e9

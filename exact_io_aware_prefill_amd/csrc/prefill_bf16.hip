@@ -143,9 +143,13 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 
 // Resident waves per SIMD the register budget is sized for.  d = 256 keeps twice
 // the Q fragments and accumulators in registers (about 330 live values), so it
-// runs two waves per SIMD and spills the excess to scratch: measured faster than
-// one wave per SIMD with every value in (accumulation) registers, whose operand
-// latency is then exposed.
+// runs two waves per SIMD and spills the excess to scratch (216 bytes per lane,
+// reloaded about three times per step in the loop): at 16/8 heads, 8k-16k
+// prompts, 27-34% faster than one wave per SIMD with every value in (accumulation)
+// registers, whose operand latency is then exposed.  Grids of at most 512
+// workgroups take the one-wave instantiation (WPS = 1, no scratch) instead:
+// 15-22% faster there (16/8 heads, 1k-4k prompts), as latency, not residency,
+// sets their time.
 template <int D> constexpr int waves_per_simd() { return D == 256 ? 2 : kWavesPerSimd; }
 
 // Chunk permutations of the LDS tiles (16-byte chunk c of key row r sits at
@@ -302,8 +306,8 @@ __device__ __forceinline__ float soft_cap(float x, float cap, float cap_k)
 // half g of the tile's key range with its own tile buffers and online-softmax
 // state, and group 1 hands its (m, l, acc) to group 0 through LDS at the end,
 // where the two are merged by the combine rule (split-KV inside one workgroup).
-template <int D, bool EXT, int KS = 1>
-__global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : waves_per_simd<D>()) void prefill_bf16_kernel(Args a)
+template <int D, bool EXT, int KS = 1, int WPS = waves_per_simd<D>()>
+__global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : WPS) void prefill_bf16_kernel(Args a)
 {
     static_assert(KS == 1 || (KS == 2 && !EXT && D <= 128), "key split: plain kernel, d <= 128");
     // rows may meet tiles with no visible key before any reference exists (window,
@@ -768,6 +772,8 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     // tile's work, which caps the gain.  Needs at least two query tiles.
     constexpr long long kSplitMaxItems = 2 * 256;
     const bool split = !ext && p.head_dim <= 128 && items <= kSplitMaxItems && a.n_qtiles >= 2;
+    // d = 256 on such grids: one wave per SIMD, no scratch (see waves_per_simd)
+    const bool one_wave = !ext && p.head_dim == 256 && items <= kSplitMaxItems;
     const dim3 grid((unsigned)items), block(kWaves * 64 * (split ? 2 : 1));
     auto launch = [&](auto dconst) {
         constexpr int DD = decltype(dconst)::value;
@@ -779,7 +785,10 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
             else
                 hipLaunchKernelGGL((prefill_bf16_kernel<DD, false>), grid, block, 0, stream, a);
         } else {
-            hipLaunchKernelGGL((prefill_bf16_kernel<DD, false>), grid, block, 0, stream, a);
+            if (one_wave)
+                hipLaunchKernelGGL((prefill_bf16_kernel<DD, false, 1, 1>), grid, block, 0, stream, a);
+            else
+                hipLaunchKernelGGL((prefill_bf16_kernel<DD, false>), grid, block, 0, stream, a);
         }
     };
     if (p.head_dim == 128)
