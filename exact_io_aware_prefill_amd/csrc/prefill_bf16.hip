@@ -147,7 +147,7 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 // reloaded about three times per step in the loop): at 16/8 heads, 8k-16k
 // prompts, 27-34% faster than one wave per SIMD with every value in (accumulation)
 // registers, whose operand latency is then exposed.  Grids of at most 512
-// workgroups take the one-wave instantiation (WPS = 1, no scratch) instead:
+// workgroups take the one-wave instantiation (WPS = 1; 8 bytes of scratch) instead:
 // 15-22% faster there (16/8 heads, 1k-4k prompts), as latency, not residency,
 // sets their time.
 template <int D> constexpr int waves_per_simd() { return D == 256 ? 2 : kWavesPerSimd; }
@@ -772,7 +772,7 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     // tile's work, which caps the gain.  Needs at least two query tiles.
     constexpr long long kSplitMaxItems = 2 * 256;
     const bool split = !ext && p.head_dim <= 128 && items <= kSplitMaxItems && a.n_qtiles >= 2;
-    // d = 256 on such grids: one wave per SIMD, no scratch (see waves_per_simd)
+    // d = 256 on such grids: one wave per SIMD (see waves_per_simd)
     const bool one_wave = !ext && p.head_dim == 256 && items <= kSplitMaxItems;
     const dim3 grid((unsigned)items), block(kWaves * 64 * (split ? 2 : 1));
     auto launch = [&](auto dconst) {
