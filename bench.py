@@ -61,6 +61,12 @@ def parse():
                     help="time one part only (profiling runs)")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 prefill measurement")
     ap.add_argument("--no-paged", action="store_true", help="skip the batched paged decode measurement")
+    ap.add_argument("--settle-ms", type=float, default=200.0,
+                    help="untimed launches of the leg's own kernel, for about this long, before each prefill "
+                         "leg's warm-up (0: none)")
+    ap.add_argument("--prefill-sweep", action="store_true",
+                    help="time only the causal prefill of the short and long prompt workloads (N = 2048, 8192, "
+                         "16384, 30720; 28/4 heads, d = 128), print one JSON line and exit (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference dispatch for HBM counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
@@ -269,6 +275,62 @@ def oracle_table(configs, budget_s: float, threads: int = 0):
     return {"threads": oracle.threads_used(), "host": host_info(), "workloads": rows}
 
 
+def settle(fn, ms: float) -> None:
+    """Untimed launches of `fn` for about `ms` milliseconds (one timed launch sets the
+    count).  From a cold start the shader clock under the prefill climbs over the
+    first few dozen launches (16k prompt: 951 TFLOP/s over launches 0-4, 1201 over
+    5-24, 1219-1227 from 25 to 400, 1211-1213 after a second), so a leg timed right
+    away would measure the climb rather than the clock a sustained run holds."""
+    import torch
+    if ms <= 0:
+        return
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    for _ in range(int(ms / max(e0.elapsed_time(e1), 1e-3))):
+        fn()
+    torch.cuda.synchronize()
+
+
+def prefill_sweep(attn, W, dev, steps: int, warmup: int) -> dict:
+    """The causal prefill alone at the prompt lengths of the short-prompt workload
+    (N = 2048) and the long-prompt sweep (8192, 16384, 30720).  Each length first runs
+    untimed launches for at least 0.3 s (and `warmup` of them), so the shader clock has
+    settled under this load, then at least `steps` launches and 0.3 s between two
+    events.  Which instantiation runs follows from the launch size: the key split at
+    N = 2048 (448 workgroups), the plain kernel above."""
+    import torch
+    out = {"metric": "causal prefill TFLOP/s by prompt length", "unit": "TFLOP/s", "steps": steps,
+           "warmup": warmup, "data": "synthetic", "results": []}
+    for cfg in (W.PREFILL_2K, W.prefill_long(8192), W.prefill_long(16384), W.prefill_long(30720)):
+        px = W.make_prefill(cfg)
+        q, k, v = (t.to(dev) for t in (px.q, px.k, px.v))
+        B, Hq, N, d = q.shape
+        o = torch.empty_like(q)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        def run(n: int) -> float:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                attn.attn_prefill(q, k, v, o, lse, True, px.scale)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+        first = run(1)
+        run(max(warmup, int(300.0 / first) + 1))
+        n = max(steps, int(300.0 / first) + 1)
+        ms = run(n)
+        flop = 2.0 * B * Hq * d * N * N
+        out["results"].append({"workload": cfg["name"], "N": N, "launches": n, "ms_per_launch": ms,
+                               "value": flop / (ms * 1e-3) / 1e12,
+                               "frac": flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+        del q, k, v, o, lse, px
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.oracle_table:
@@ -289,6 +351,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.prefill_sweep:
+        print(json.dumps(prefill_sweep(attn, W, dev, args.steps, args.warmup)), flush=True)
+        return
 
     pcfg = W.prefill_long(16384)
     px = W.make_prefill(pcfg)
@@ -323,9 +388,8 @@ def main():
     do_p = args.only in (None, "prefill")
     do_d = args.only in (None, "decode")
     # FP8 prefill of the same prompt (E4M3 inputs), timed on its own before the step
-    # loop: its launches also take the GPU's power controller through the dozen or
-    # so heavy launches it needs to settle, so the bf16 steps that follow the W
-    # warm-up steps run at the settled clock
+    # loop.  Each prefill leg first runs its own kernel untimed for --settle-ms, so
+    # its W warm-up and K timed launches see the clock a sustained run holds
     fp8 = None
     if args.only in (None, "fp8") and not args.no_fp8:
         fx = W.prefill_fp8_inputs(pcfg["seed"], B, Hq, k.shape[1], N, d)
@@ -336,6 +400,7 @@ def main():
 
         def run_fp8():
             attn.attn_prefill_fp8(q8, k8, v8, o8, l8, dsq, dsk, dsv, True, fx.scale)
+        settle(run_fp8, args.settle_ms)
         for _ in range(args.warmup):
             run_fp8()
         torch.cuda.synchronize()
@@ -353,6 +418,8 @@ def main():
                             "frac": a8 / PEAK_FP8_TFLOPS, "traffic": measured_traffic("fp8"),
                             "kernel": "prefill_fp8_kernel<128, false, false>", "algorithmic_flop_per_launch": prefill_flop}}
 
+    if do_p:
+        settle(run_prefill, args.settle_ms)
     for i in range(args.warmup):
         if do_p:
             run_prefill()
@@ -564,6 +631,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": wall * 1e3 / args.steps,
         "higher_is_better": True,
         "scaling": "weak",
