@@ -152,6 +152,10 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 // sets their time.
 template <int D> constexpr int waves_per_simd() { return D == 256 ? 2 : kWavesPerSimd; }
 
+// Waves of one key group: the key split (KS = 2) runs two 2-wave groups over a
+// 64-row query tile, the plain kernel one 4-wave group over 128 rows.
+constexpr int split_group_waves(int ks) { return ks > 1 ? 2 : kWaves; }
+
 // Chunk permutations of the LDS tiles (16-byte chunk c of key row r sits at
 // slot c ^ swz(r)).  D = 128: a row is one 256-byte bank line; the K operand
 // reads of 16 consecutive rows and the V transpose reads of 4 rows x 64 bytes
@@ -168,18 +172,20 @@ template <int D> __device__ __forceinline__ int v_swz(int r) { return D >= 128 ?
 // buffer base.  D = 256: an instruction covers 2 rows, so a lane's rows are 8
 // apart and the K permutation (r & 15) alternates; odd instructions flip bit 3 of
 // the chunk slot (`odd_xor`), the V permutation (r & 3) does not change.
-template <int D>
+template <int D, int NW = kWaves>
 struct TileLoader {
     static constexpr int RB = D * 2;                 // bytes per key row
     static constexpr int NC = D / 8;                 // 16-byte chunks per row
     static constexpr int RPI = 64 / NC;              // key rows per instruction
     static constexpr int INSTR = kBlockN * NC / 64;  // wave instructions per tile
-    static constexpr int PER_WAVE = (INSTR + kWaves - 1) / kWaves;
-    static_assert(INSTR % kWaves == 0 || INSTR < kWaves, "tile instructions split evenly over the waves");
-    // a lane's instructions fill rows 4*kWaves apart (D = 128) or 8*kWaves apart
-    // (D = 64); with kWaves a multiple of 4 those rows share their permutation
-    static_assert(kWaves % 4 == 0, "one per-lane offset needs kWaves to be a multiple of 4");
-    static_assert(D != 256 || kWaves == 4, "the d = 256 odd-instruction flip assumes 4 waves");
+    static constexpr int PER_WAVE = (INSTR + NW - 1) / NW;
+    static_assert(INSTR % NW == 0 || INSTR < NW, "tile instructions split evenly over the waves");
+    // a lane's instructions fill rows RPI * NW apart: with 4 loading waves (d <= 128)
+    // those rows share their permutation; d = 256, and 2 loading waves at d = 128
+    // (rows 8 apart), flip it on odd instructions
+    static constexpr bool FLIP = D == 256 || NW != kWaves;
+    static_assert(NW == kWaves || (NW == 2 && D <= 128), "4 loading waves, or 2 at d <= 128");
+    static_assert(D != 256 || NW == 4, "the d = 256 odd-instruction flip assumes 4 waves");
     uint32_t voff;     // per-lane byte offset from the first row an instruction fills
     uint32_t rowb;     // bytes between consecutive key rows in memory
     uint32_t odd_xor;  // D = 256: offset flip of odd instructions (0 when the permutation repeats)
@@ -191,8 +197,8 @@ struct TileLoader {
         const int r = u / NC, pos = u % NC;
         rowb = row_bytes;
         voff = (uint32_t)(lane / NC) * row_bytes + 16u * (uint32_t)(pos ^ swz(r));
-        // the lane's row in an odd instruction is r + RPI * kWaves
-        odd_xor = 16u * (uint32_t)(swz(r) ^ swz(r + RPI * kWaves));
+        // the lane's row in an odd instruction is r + RPI * NW
+        odd_xor = 16u * (uint32_t)(swz(r) ^ swz(r + RPI * NW));
     }
     // Issue the loads of the tile starting at key k0 of one head (rows rowb apart,
     // n rows) into the LDS tile `dst`.  Each instruction's descriptor starts at its
@@ -201,15 +207,15 @@ struct TileLoader {
     {
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
-            const int ins = wave + i * kWaves;
-            if (INSTR < kWaves && ins >= INSTR) break;  // wave-uniform
+            const int ins = wave + i * NW;
+            if (INSTR < NW && ins >= INSTR) break;  // wave-uniform
             const int row0 = k0 + ins * RPI;
             // (n - row0) * rowb < 2^32: the launcher bounds a head's padded rows to
             // 32-bit byte offsets.  readfirstlane keeps the descriptor in scalar registers.
             const uint32_t rec = __builtin_amdgcn_readfirstlane((uint32_t)max(n - row0, 0) * rowb);
             const __amdgpu_buffer_rsrc_t rs =
                 make_rsrc(reinterpret_cast<const char *>(head) + (long long)row0 * rowb, rec);
-            const uint32_t off = (D == 256 && (i & 1)) ? (voff ^ odd_xor) : voff;
+            const uint32_t off = (FLIP && (i & 1)) ? (voff ^ odd_xor) : voff;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t *)((char *)dst + ins * 1024), 16, off, 0, 0, 0);
         }
     }
@@ -302,19 +308,21 @@ __device__ __forceinline__ float soft_cap(float x, float cap, float cap_k)
 // EXT selects the variant with a sliding window and logit soft-capping (a separate
 // instantiation, so the plain kernel keeps its instruction schedule).  KS = 2
 // selects the key-split variant for prompts too short to fill the GPU: the
-// workgroup is two groups of 4 waves over the same 128 query rows, group g walks
+// workgroup is two groups of 2 waves over the same 64 query rows, group g walks
 // half g of the tile's key range with its own tile buffers and online-softmax
 // state, and group 1 hands its (m, l, acc) to group 0 through LDS at the end,
 // where the two are merged by the combine rule (split-KV inside one workgroup).
 template <int D, bool EXT, int KS = 1, int WPS = waves_per_simd<D>()>
-__global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : WPS) void prefill_bf16_kernel(Args a)
+__global__ __launch_bounds__(split_group_waves(KS) * 64 * KS, KS > 1 ? 2 : WPS) void prefill_bf16_kernel(Args a)
 {
     static_assert(KS == 1 || (KS == 2 && !EXT && D <= 128), "key split: plain kernel, d <= 128");
     // rows may meet tiles with no visible key before any reference exists (window,
     // or a key group whose range starts past the row): the reference is then taken
     // on the rare path instead of in the prologue
     constexpr bool REF = EXT || KS > 1;
-    constexpr int NT = kWaves * 64;  // threads of one key group
+    constexpr int NW = split_group_waves(KS);  // waves of one key group
+    constexpr int NT = NW * 64;                // threads of one key group
+    constexpr int BM = NW * kBlocks * 32;      // query rows per workgroup
     constexpr int TE = kBlockN * D;  // elements per K or V tile
     // separate LDS objects, so in-flight loads into one buffer do not make the
     // compiler wait before reading another; one set per key group
@@ -326,8 +334,8 @@ __global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : WPS) void prefill_bf
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave_wg = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in SGPRs
-    const int grp = KS > 1 ? wave_wg / kWaves : 0;  // key group
-    const int wave = KS > 1 ? wave_wg % kWaves : wave_wg;  // query block and loader slot in the group
+    const int grp = KS > 1 ? wave_wg / NW : 0;  // key group
+    const int wave = KS > 1 ? wave_wg % NW : wave_wg;  // query block and loader slot in the group
     const int gtid = KS > 1 ? tid % NT : tid;
     uint16_t *const KB0 = KB0s[grp];
     uint16_t *const KB1 = KB1s[grp];
@@ -356,7 +364,7 @@ __global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : WPS) void prefill_bf
     const int b = bg / a.Hkv, hk = bg % a.Hkv;
     const int h = hk * a.group + j;
     const int qtile = a.n_qtiles - 1 - r;
-    const int q0 = qtile * kBM;
+    const int q0 = qtile * BM;
     // this sequence's first token and length
     long long tok0;
     int N;
@@ -416,7 +424,7 @@ __global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : WPS) void prefill_bf
     const float sl2 = a.scale_log2;
     const int xlane = (lane ^ 32) << 2;  // ds_bpermute address of the other half-wave
 
-    TileLoader<D> kld, vld;
+    TileLoader<D, NW> kld, vld;
     kld.init(wave, lane, (uint32_t)(a.kv_row * 2), [](int rr) { return k_swz<D>(rr); });
     vld.init(wave, lane, (uint32_t)(a.kv_row * 2), [](int rr) { return v_swz<D>(rr); });
     const uint32_t kad = (uint32_t)(l32 * 2 * D + 16 * (hh ^ k_swz<D>(l32)));
@@ -428,7 +436,7 @@ __global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : WPS) void prefill_bf
         vad = (uint32_t)(row * 2 * D + 16 * (c ^ v_swz<D>(row)) + 8 * (q & 1));
     }
 
-    const int kend = a.causal ? min(N, q0 + kBM) : N;  // keys this tile may see
+    const int kend = a.causal ? min(N, q0 + BM) : N;  // keys this tile may see
     // with a window, the first tile that holds a key of row q0's window
     const int kbeg = (EXT && a.window >= 0) ? max(0, q0 - a.window) / kBlockN * kBlockN : 0;
     int ntiles = (kend - kbeg + kBlockN - 1) / kBlockN;  // >= 1: key q0 is visible to row q0
@@ -605,10 +613,10 @@ __global__ __launch_bounds__(kWaves * 64 * KS, KS > 1 ? 2 : WPS) void prefill_bf
         // once every wave has finished its last product); group 0 merges it by the
         // combine rule: weights c_g = 2^(m_g - M) with M the larger reference (0 for
         // a group that saw no key of the row), l = sum c_g l_g, acc = sum c_g acc_g
-        __shared__ float xml[kWaves][2][64];
+        __shared__ float xml[NW][2][64];
         __syncthreads();
         // wave w of each group uses the w-th tile buffer array (KS * TE elements)
-        static_assert(kWaves == 4 && (D / 32) * 16 * 64 * 4 <= KS * TE * 2, "one exchange slab per wave");
+        static_assert(NW <= 4 && (D / 32) * 16 * 64 * 4 <= KS * TE * 2, "one exchange slab per wave");
         uint16_t *const xbuf = wave == 0 ? &KB0s[0][0] : wave == 1 ? &KB1s[0][0] : wave == 2 ? &VB0s[0][0] : &VB1s[0][0];
         f32x16_t *const slab = reinterpret_cast<f32x16_t *>(xbuf);
         if (grp == 1) {
@@ -762,19 +770,28 @@ hipError_t launch_prefill_bf16(const PrefillParams &p, hipStream_t stream)
     if (rows * a.q_row * 2 > 0xffffffffLL || rows * a.kv_row * 2 > 0xffffffffLL) return hipErrorInvalidValue;
     a.n_items = (int)items;
     // Key split for grids that leave the GPU mostly idle: with at most
-    // kSplitMaxItems workgroups (two per compute unit on 256 compute units) the
+    // kSplitMaxItems 128-row tiles (two per compute unit on 256 compute units) the
     // longest query tiles' key walks set the time, and a second wave group that
-    // takes half of each walk shortens them, at the cost of residency (one 8-wave
-    // workgroup per compute unit; its throughput is about 82% of three 4-wave
-    // ones).  Measured at 28/4 heads, d = 128: +6% at N = 1024, +3.5% at 2048, and
-    // -14% at 3072 (672 workgroups), hence the bound.  Both groups share one
-    // compute unit, so the longest tile's compute unit still does all of that
-    // tile's work, which caps the gain.  Needs at least two query tiles.
+    // takes half of each walk shortens them.  The split runs 64-row tiles (twice
+    // the workgroups, 4 waves each, two per compute unit), which halves the
+    // longest walk again and lets a compute unit hold two workgroups that need
+    // not wait at each other's barriers.  Measured at 28/4 heads, d = 128: +6% at
+    // N = 1024 and +3.5% at 2048 for the split with 128-row tiles over none, -14%
+    // at 3072 (672 workgroups), hence the bound; 64-row tiles then +4 to +6% at
+    // N = 1024-2048, +6 to +8% at d = 64, +0 to +3% at 480-512 tiles.  Needs at
+    // least two query tiles.
     constexpr long long kSplitMaxItems = 2 * 256;
     const bool split = !ext && p.head_dim <= 128 && items <= kSplitMaxItems && a.n_qtiles >= 2;
+    long long launched = items;
+    if (split) {
+        constexpr int rows_per_tile = split_group_waves(2) * kBlocks * 32;
+        a.n_qtiles = (p.N + rows_per_tile - 1) / rows_per_tile;
+        launched = (long long)a.n_qtiles * p.B * p.Hq;
+        a.n_items = (int)launched;
+    }
     // d = 256 on such grids: one wave per SIMD (see waves_per_simd)
     const bool one_wave = !ext && p.head_dim == 256 && items <= kSplitMaxItems;
-    const dim3 grid((unsigned)items), block(kWaves * 64 * (split ? 2 : 1));
+    const dim3 grid((unsigned)launched), block(split ? split_group_waves(2) * 64 * 2 : kWaves * 64);
     auto launch = [&](auto dconst) {
         constexpr int DD = decltype(dconst)::value;
         if (ext)
