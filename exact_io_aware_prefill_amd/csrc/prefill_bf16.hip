@@ -427,13 +427,21 @@ __global__ __launch_bounds__(split_group_waves(KS) * 64 * KS, KS > 1 ? 2 : WPS) 
     TileLoader<D, NW> kld, vld;
     kld.init(wave, lane, (uint32_t)(a.kv_row * 2), [](int rr) { return k_swz<D>(rr); });
     vld.init(wave, lane, (uint32_t)(a.kv_row * 2), [](int rr) { return v_swz<D>(rr); });
-    const uint32_t kad = (uint32_t)(l32 * 2 * D + 16 * (hh ^ k_swz<D>(l32)));
+    // Operand reads address this group's buffers from group 0's, whose LDS addresses
+    // are compile-time constants (they fold into the reads' immediate offsets, as in
+    // the unsplit kernel, instead of costing an add per read and step), with the
+    // group's offset in the per-lane offsets.  A tile is 2 TE bytes, a power of two,
+    // and the reads' XOR terms stay below it, so they never reach the offset's bits.
+    const uint16_t *const KR0 = KB0s[0], *const KR1 = KB1s[0], *const VR0 = VB0s[0], *const VR1 = VB1s[0];
+    static_assert((2 * TE & (2 * TE - 1)) == 0, "tile bytes a power of two");
+    const uint32_t goff = (uint32_t)grp * 2 * TE;
+    const uint32_t kad = (uint32_t)(l32 * 2 * D + 16 * (hh ^ k_swz<D>(l32))) + goff;
     uint32_t vad;
     {
         const int j16 = lane & 15, h16 = (lane >> 4) & 1, rr = j16 >> 2, q = j16 & 3;
         const int row = 4 * hh + rr;
         const int c = 2 * h16 + (q >> 1);
-        vad = (uint32_t)(row * 2 * D + 16 * (c ^ v_swz<D>(row)) + 8 * (q & 1));
+        vad = (uint32_t)(row * 2 * D + 16 * (c ^ v_swz<D>(row)) + 8 * (q & 1)) + goff;
     }
 
     const int kend = a.causal ? min(N, q0 + BM) : N;  // keys this tile may see
@@ -491,7 +499,7 @@ __global__ __launch_bounds__(split_group_waves(KS) * 64 * KS, KS > 1 ? 2 : WPS) 
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, S[bb][kb][i]);
         return fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(xlane, __builtin_bit_cast(int, mx))));
     };
-    qk_tile<D>(S, KB0, qf, kad);
+    qk_tile<D>(S, KR0, qf, kad);
     if (!REF) {
         // The plain kernel starts from the first tile's true max: every row sees key
         // 0 (causal) or all keys < N, so it is finite, and the steps need no check
@@ -599,14 +607,14 @@ __global__ __launch_bounds__(split_group_waves(KS) * 64 * KS, KS > 1 ? 2 : WPS) 
     // step t reads K(t+1) from KB[(t+1)&1] and V(t-1) from VB[(t-1)&1];
     // it loads K(t+2) into KB[t&1] and V(t) into VB[t&1]
     for (int t = 0; t < ntiles; t += 2) {
-        step(P1, P0, t, KB1, VB1, KB0, VB0);
-        if (t + 1 < ntiles) step(P0, P1, t + 1, KB0, VB0, KB1, VB1);
+        step(P1, P0, t, KR1, VR1, KB0, VB0);
+        if (t + 1 < ntiles) step(P0, P1, t + 1, KR0, VR0, KB1, VB1);
     }
     // last product: P of tile ntiles-1 is in P0 (ntiles odd) or P1 (even), V in VB[(ntiles-1)&1]
     if (ntiles & 1)
-        pv_tile<D>(acc, VB0, P0, vad);
+        pv_tile<D>(acc, VR0, P0, vad);
     else
-        pv_tile<D>(acc, VB1, P1, vad);
+        pv_tile<D>(acc, VR1, P1, vad);
 
     if constexpr (KS > 1) {
         // group 1 hands its state to group 0 through LDS (the tile buffers are free
