@@ -328,6 +328,19 @@ def test_prefill_varlen_f32(attn, d):
     check("varlen f32 d=%d" % d, o, lse, ro, rl, F32_TOL)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_varlen_key_split(attn, d):
+    """A packed batch small enough for the key-split instantiation (at most 512 query
+    tiles of 128 rows: 16 tiles x 8 sequences x 4 heads): most of its 64-row work items
+    lie past their sequence's end and exit, the others split their key walks in two."""
+    lens = [0, 1, 63, 64, 65, 700, 2047, 1300]
+    say("case: varlen key split d=%d lengths=%s" % (d, lens))
+    x = W.prefill_packed_inputs(970 + d, lens, 4, 2, d, W.BF16)
+    o, lse = run_varlen(attn, x)
+    ro, rl = oracle.prefill_varlen(x.q, x.k, x.v, x.cu_seqlens, True, x.scale)
+    check("varlen key split d=%d" % d, o, lse, ro, rl, BF16_TOL)
+
+
 def test_prefill_varlen_one_sequence_equals_padded(attn):
     """A packed batch of one sequence runs the same arithmetic as the padded layout,
     so the outputs agree bit for bit."""
