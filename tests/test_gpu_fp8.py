@@ -273,3 +273,41 @@ def test_fp8_prefill_varlen_one_sequence_equals_padded(attn):
                               dev(x.descale_v), True, x.scale)
     torch.cuda.synchronize()
     assert torch.equal(o, op[0].permute(1, 0, 2)) and torch.equal(lse, lp[0])
+
+
+def _random_case(seed):
+    """Batch 1..3, KV heads 1/2/4/8, group 1/2/4/7, d 64/128/256, length 1..2000, causal
+    or full, padded or packed (packed lengths 0..N, one of them N); the work kept below
+    1e10 (batch x query heads x N^2 x d) for the oracle and the per-row bounds."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 4))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 7]))
+    d = int(rng.choice([64, 128, 256]))
+    causal = bool(rng.integers(0, 2))
+    packed = bool(rng.integers(0, 2))
+    N = int(rng.integers(1, 2001))
+    N = max(1, min(N, int((1e10 / (B * g * Hkv * d)) ** 0.5)))
+    lens = rng.integers(0, N + 1, size=B)
+    lens[int(rng.integers(0, B))] = N
+    return B, Hkv, g, d, N, causal, packed, lens.tolist()
+
+
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_fp8_prefill_random_shapes(attn, seed):
+    """Seeded random shapes across the FP8 kernel's layouts, head sizes and masks."""
+    B, Hkv, g, d, N, causal, packed, lens = _random_case(seed)
+    Hq = g * Hkv
+    say("case: fp8 prefill random seed=%d B=%d Hq=%d Hkv=%d d=%d N=%d causal=%s packed=%s lens=%s"
+        % (seed, B, Hq, Hkv, d, N, causal, packed, lens if packed else "-"))
+    if packed:
+        x = W.prefill_fp8_packed_inputs(7000 + seed, lens, Hq, Hkv, d, causal=causal)
+        o, lse = run_packed(attn, x)
+        ro, rl = oracle.prefill_fp8_varlen(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, x.cu_seqlens,
+                                           causal, x.scale)
+        check_fp8("fp8 random seed=%d" % seed, o, lse, ro, rl, packed_row_bounds(x))
+    else:
+        x = W.prefill_fp8_inputs(7000 + seed, B, Hq, Hkv, N, d, causal=causal)
+        o, lse = run(attn, x)
+        ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, causal, x.scale)
+        check_fp8("fp8 random seed=%d" % seed, o, lse, ro, rl, row_bounds(x))
