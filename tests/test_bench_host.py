@@ -80,3 +80,29 @@ def test_several_gpus_are_refused_with_a_message():
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_sizes_its_sample_to_the_target(monkeypatch):
+    """The oracle leg's row sample lands near its time target when each oracle call
+    carries a fixed cost (the output allocation) on top of work-proportional time:
+    the two calibration runs cancel the fixed part.  A stand-in oracle sleeps 50 ms
+    plus 3e-7 s per visible (row, key) pair of the rows it is asked for."""
+    import time
+    import types
+
+    import numpy as np
+    import oracle
+
+    N = 4096
+    x = types.SimpleNamespace(q=np.zeros((1, 2, N, 8)), k=np.zeros((1, 1, N, 8)), v=np.zeros((1, 1, N, 8)),
+                              scale=1.0)
+
+    def fake_prefill(q, k, v, causal, scale, row_step=1, **kw):
+        rows = np.arange(0, N, row_step, dtype=np.float64)
+        time.sleep(0.05 + 3e-7 * float((rows + 1).sum()))
+
+    monkeypatch.setattr(oracle, "prefill", fake_prefill)
+    for target in (0.4, 1.0):
+        r = bench.cpu_baseline(x, target)
+        wall = float(r["sample"].rsplit(", ", 1)[1].split(" s wall")[0])
+        assert 0.5 * target <= wall <= 1.6 * target, (target, r["sample"])  # the row step is an integer
