@@ -221,3 +221,83 @@ def test_decode_ext_without_options_is_the_plain_call(attn):
                              x.max_blocks, x.scale, window, 0.0, 64, ws)
         torch.cuda.synchronize()
         assert torch.equal(o, o0) and torch.equal(lse, l0), window
+
+
+# ------------------------------------------------------------------ seeded random shapes
+def _draw_options(rng, n, d):
+    """A window (-1: none, else 0..n+49) and a soft-cap (0: none, else 1..50); the scale
+    is the workloads' 1/sqrt(d) without a cap, and with one anything with |scale| sqrt(d)
+    <= 4 (scores of N(0,1) inputs spread up to 4 times the workloads', enough to
+    saturate caps 1 and 5).  Wider spreads make rows that one or two keys dominate,
+    where rounding the probabilities and O to bf16 alone can pass the 2e-2 bar (about
+    2^-9 (max|v - O| + |O|) with |v| near 4)."""
+    window = -1 if rng.random() < 0.3 else int(rng.integers(0, n + 50))
+    cap = 0.0 if rng.random() < 0.4 else float(rng.choice([1.0, 5.0, 20.0, 50.0]))
+    scale = None if cap == 0.0 else float(rng.uniform(-4.0, 4.0)) / d ** 0.5
+    return window, cap, scale
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_prefill_variants_random_shapes(attn, seed):
+    """Window and soft-cap over seeded random prefill shapes: batch 1..2, KV heads
+    1/2/4, group 1/3/4, d 64/128/256, length 1..2500, causal or full, padded or
+    packed (lengths 0..N, one of them N)."""
+    rng = np.random.default_rng(8000 + seed)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 3, 4]))
+    d = int(rng.choice([64, 128, 256]))
+    causal = bool(rng.integers(0, 2))
+    packed = bool(rng.integers(0, 2))
+    N = int(rng.integers(1, 2501))
+    N = max(1, min(N, int((1e10 / (B * g * Hkv * d)) ** 0.5)))
+    window, cap, scale = _draw_options(rng, N, d)
+    Hq = g * Hkv
+    say("case: prefill variants random seed=%d B=%d Hq=%d Hkv=%d d=%d N=%d causal=%s packed=%s window=%d cap=%g "
+        "scale=%s" % (seed, B, Hq, Hkv, d, N, causal, packed, window, cap, scale))
+    if packed:
+        lens = rng.integers(0, N + 1, size=B)
+        lens[int(rng.integers(0, B))] = N
+        x = W.prefill_packed_inputs(8100 + seed, lens.tolist(), Hq, Hkv, d, W.BF16, causal=causal, scale=scale)
+        o, lse = attn.prefill_varlen(dev(x.q), dev(x.k), dev(x.v), dev(x.cu_seqlens), x.max_seqlen, causal, x.scale,
+                                     window_left=window, softcap=cap)
+        torch.cuda.synchronize()
+        ro, rl = oracle.prefill_varlen(x.q, x.k, x.v, x.cu_seqlens, causal, x.scale, window=window, softcap=cap)
+    else:
+        x = W.prefill_inputs(8100 + seed, B, Hq, Hkv, N, d, W.BF16, causal=causal, scale=scale)
+        o, lse = run_prefill(attn, x, window, cap)
+        ro, rl = oracle.prefill(x.q, x.k, x.v, causal, x.scale, window=window, softcap=cap)
+    check("prefill variants random seed=%d" % seed, o, lse, ro, rl, BF16_TOL)
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_decode_variants_random_shapes(attn, seed):
+    """Window and soft-cap over seeded random decode batches: 1..12 sequences of
+    0..capacity tokens (capacity 64..3000), KV heads 1/2/4/8, group 1/2/4/7, d
+    64/128/256, contiguous or paged, automatic or explicit chunks."""
+    rng = np.random.default_rng(8200 + seed)
+    B = int(rng.integers(1, 13))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 7]))
+    d = int(rng.choice([64, 128, 256]))
+    cap_tokens = int(rng.integers(64, 3001))
+    paged = bool(rng.integers(0, 2))
+    chunk = int(rng.choice([0, 16, 64, 256]))
+    lens = rng.integers(0, cap_tokens + 1, size=B)
+    lens[rng.random(B) < 0.15] = 0
+    window, cap, scale = _draw_options(rng, cap_tokens, d)
+    say("case: decode variants random seed=%d B=%d Hkv=%d g=%d d=%d capacity=%d paged=%s chunk=%d window=%d cap=%g "
+        "scale=%s" % (seed, B, Hkv, g, d, cap_tokens, paged, chunk, window, cap, scale))
+    if paged:
+        x = W.decode_paged_inputs(8300 + seed, B, g * Hkv, Hkv, d, 16, 1, cap_tokens, lengths=lens.tolist())
+    else:
+        capc = -(-cap_tokens // 16) * 16
+        x = W.decode_contiguous_inputs(8300 + seed, B, g * Hkv, Hkv, capc, d, seq_lens=lens.tolist())
+    if scale is not None:
+        x.scale = scale
+    o, lse = attn.decode(dev(x.q), dev(x.k_cache), dev(x.v_cache), dev(x.block_table), dev(x.seq_lens),
+                         x.page_size, x.max_blocks, x.scale, chunk, window_left=window, softcap=cap)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode(x.q, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.scale, x.page_size,
+                           x.max_blocks, window=window, softcap=cap)
+    check("decode variants random seed=%d" % seed, o, lse, ro, rl, BF16_TOL)
