@@ -203,3 +203,28 @@ def test_balanced_decode_append(attn, d, paged):
     check("balanced append d=%d paged=%d" % (d, paged), o, lse, ro, rl, BF16_TOL)
     assert np.array_equal(kc.cpu().double().numpy(), rk), "K cache after the append differs"
     assert np.array_equal(vc.cpu().double().numpy(), rv), "V cache after the append differs"
+
+
+@pytest.mark.parametrize("seed", list(range(12)))
+def test_fp8_cache_decode_random_shapes(attn, seed):
+    """Seeded random batches over an E4M3 cache: 1..100 sequences (1 runs the per-chunk
+    split, more the balanced one), KV heads 1..8, group 1..7, d 64/128, lengths
+    0..capacity with zeros among them, contiguous or paged, automatic or explicit
+    chunks; against the oracle's plain decode of the dequantised cache."""
+    rng = np.random.default_rng(9000 + seed)
+    B = int(rng.choice([1, 2, 7, 33, 100]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 7]))
+    d = int(rng.choice([64, 128]))
+    cap = int(rng.choice([256, 1024, 3000]))
+    B = max(1, min(B, int(200e6 // (cap * Hkv * d * 4))))
+    lens = rng.integers(0, cap + 1, size=B)
+    lens[rng.random(B) < 0.15] = 0
+    paged = bool(rng.integers(0, 2))
+    chunk = int(rng.choice([0, 0, 64, 256]))
+    say("case: fp8-cache decode random seed=%d B=%d Hkv=%d g=%d d=%d cap=%d paged=%s chunk=%d"
+        % (seed, B, Hkv, g, d, cap, paged, chunk))
+    x = W.decode_fp8_inputs(9100 + seed, B, g * Hkv, Hkv, d, lens.tolist(), -(-cap // 16) * 16, paged)
+    o, lse = run_fp8(attn, x, chunk)
+    ro, rl = reference_fp8(x)
+    check("fp8-cache decode random seed=%d" % seed, o, lse, ro, rl, BF16_TOL)
