@@ -169,3 +169,58 @@ def test_fp8_cache_decode_ext_without_options_is_the_plain_kernel(attn):
     attn.attn_decode_fp8_ext(*args, o1, l1, x.page_size, x.max_blocks, x.scale, -1, 0.0, 64, ws)
     torch.cuda.synchronize()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+@pytest.mark.parametrize("seed", list(range(10)))
+def test_fp8_window_softcap_random_shapes(attn, seed):
+    """Window and soft-cap on the FP8 prefill over seeded random padded shapes: batch
+    1..2, KV heads 1/2/4, group 1/3/4, d 64/128/256, length 1..1500, causal or full;
+    the window -1 or 0..N+49, the cap 0 or 1/5/20/50."""
+    rng = np.random.default_rng(9500 + seed)
+    B = int(rng.integers(1, 3))
+    Hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 3, 4]))
+    d = int(rng.choice([64, 128, 256]))
+    causal = bool(rng.integers(0, 2))
+    N = int(rng.integers(1, 1501))
+    window = -1 if rng.random() < 0.3 else int(rng.integers(0, N + 50))
+    softcap = 0.0 if rng.random() < 0.4 else float(rng.choice([1.0, 5.0, 20.0, 50.0]))
+    say("case: fp8 ext random seed=%d B=%d Hq=%d Hkv=%d d=%d N=%d causal=%s window=%d softcap=%g"
+        % (seed, B, g * Hkv, Hkv, d, N, causal, window, softcap))
+    x = W.prefill_fp8_inputs(9600 + seed, B, g * Hkv, Hkv, N, d, causal=causal)
+    o, lse = attn.prefill_fp8(dev(x.q8), dev(x.k8), dev(x.v8), dev(x.descale_q), dev(x.descale_k), dev(x.descale_v),
+                              causal, x.scale, window_left=window, softcap=softcap)
+    torch.cuda.synchronize()
+    ro, rl = oracle.prefill_fp8(x.q8, x.k8, x.v8, x.descale_q, x.descale_k, x.descale_v, causal, x.scale,
+                                window=window, softcap=softcap)
+    check_fp8("fp8 ext random seed=%d" % seed, o, lse, ro, rl, padded_bounds(x, window, softcap))
+
+
+@pytest.mark.parametrize("seed", list(range(10)))
+def test_fp8_cache_decode_window_softcap_random_shapes(attn, seed):
+    """Window and soft-cap on the E4M3-cache decode over seeded random batches: 1..12
+    sequences of 0..capacity tokens, KV heads 1..8, group 1..7, d 64/128, contiguous or
+    paged, chunks automatic or explicit; the bf16 decode's bars."""
+    from gpu_common import BF16_TOL, check
+    rng = np.random.default_rng(9700 + seed)
+    B = int(rng.integers(1, 13))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 7]))
+    d = int(rng.choice([64, 128]))
+    cap = int(rng.integers(64, 3001))
+    paged = bool(rng.integers(0, 2))
+    chunk = int(rng.choice([0, 16, 64, 256]))
+    lens = rng.integers(0, cap + 1, size=B)
+    lens[rng.random(B) < 0.15] = 0
+    window = -1 if rng.random() < 0.3 else int(rng.integers(0, cap + 50))
+    softcap = 0.0 if rng.random() < 0.4 else float(rng.choice([1.0, 5.0, 20.0, 50.0]))
+    say("case: fp8-cache decode random seed=%d B=%d Hkv=%d g=%d d=%d cap=%d paged=%s chunk=%d window=%d softcap=%g"
+        % (seed, B, Hkv, g, d, cap, paged, chunk, window, softcap))
+    x = W.decode_fp8_inputs(9800 + seed, B, g * Hkv, Hkv, d, lens.tolist(), -(-cap // 16) * 16, paged)
+    o, lse = attn.decode_fp8(dev(x.q), dev(x.k_cache8), dev(x.v_cache8), dev(x.block_table), dev(x.seq_lens),
+                             x.page_size, x.max_blocks, dev(x.descale_k), dev(x.descale_v), x.scale, chunk,
+                             window_left=window, softcap=softcap)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_fp8(x.q, x.k_cache8, x.v_cache8, x.descale_k, x.descale_v, x.block_table, x.seq_lens,
+                               x.scale, x.page_size, x.max_blocks, window=window, softcap=softcap)
+    check("fp8-cache decode random seed=%d" % seed, o, lse, ro, rl, BF16_TOL)
