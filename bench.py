@@ -545,7 +545,7 @@ def main():
                    "dtype": "fp8-e4m3 cache, bf16 q/o",
                    "roofline": {"bound": "hbm", "achieved": bytes8 / (ms8 * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                                 "unit": "GB/s", "frac": bytes8 / (ms8 * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                                "kernels": "decode_split_kernel<128, false, false, true, false> + lse_combine_kernel<128, false>",
+                                "kernels": "decode_split_kernel<128, false, false, true, false> + lse_combine_kernel<128, false, 2>",
                                 "algorithmic_bytes_per_launch": bytes8},
                    "speedup_vs_bf16_cache": dec_bb_ms / ms8}
 
@@ -613,7 +613,7 @@ def main():
                             "values": "lengths and block table of the paged workload; K/V drawn on the device"},
                  "roofline": {"bound": "hbm", "achieved": pgbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": pgbs / PEAK_HBM_GBS, "traffic": measured_traffic("paged"),
-                              "kernels": "decode_split_kernel<128, false, false, false, true> + lse_combine_kernel<128, true>",
+                              "kernels": "decode_split_kernel<128, false, false, false, true> + lse_combine_kernel<128, true, 1>",
                               "algorithmic_bytes_per_launch": pbytes},
                  "floor": {"read_ms": pread_ms, "read_GBps": 2 * pool_bytes / (pread_ms * 1e-3) / 1e9,
                            "workgroups": pgrid,
@@ -666,7 +666,7 @@ def main():
                          "avg_ms_events_around_each_call": dec_ms,
                          "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": gbs / PEAK_HBM_GBS, "traffic": measured_traffic("decode"),
-                                      "kernels": "decode_split_kernel<128, false, false, false, false> + lse_combine_kernel<128, false>",
+                                      "kernels": "decode_split_kernel<128, false, false, false, false> + lse_combine_kernel<128, false, 2>",
                                       "algorithmic_bytes_per_launch": decode_bytes}}
         if floor is not None:
             floor["call_over_read_plus_launch"] = dec_bb_ms / floor["read_plus_launch_ms"]

@@ -724,9 +724,10 @@ __global__ __launch_bounds__(split_waves<D>() * 64, D == 64 ? 4 : 1) void decode
 }
 
 // ---------------------------------------------------------------------------
-// Combine: one workgroup of 256 threads per row (sequence x query head).  Thread
-// (sg, c) accumulates float4 column c over splits sg, sg + SG, ...  The first
-// batch of loads (partials and log-sum-exps of up to 8*SG splits) is issued
+// Combine: workgroups of 256 threads, one per row (sequence x query head) after
+// the balanced split, two per row otherwise (each taking half of the row's
+// columns).  Thread (sg, c) accumulates float4 column c over splits sg, sg + SG, ...
+// The first batch of loads (partials and log-sum-exps of 64 splits) is issued
 // before the row's split count is known: the loads stay inside the row's
 // max_splits slots, and splits outside [first, ns) get weight 0 once the count
 // arrives, so the count's load and the partials' loads are in flight together.
@@ -787,17 +788,23 @@ struct CombineArgs {
     float *lse;
 };
 
-template <int D, bool BAL = false>
+// CS > 1: each row's columns are split over CS workgroups (each reduces the row's
+// log-sum-exps itself), so twice the compute units read a few rows' partials: the
+// 32k decode's 28 rows run on 56 workgroups, 0.26 us faster per call.
+template <int D, bool BAL = false, int CS = 1>
 __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArgs a)
 {
     constexpr int C4 = D / 4;                    // float4 columns of a row
-    constexpr int SG = kCombineThreads / C4;     // split groups
-    constexpr int U = 8;                         // splits per thread per batch
-    __shared__ f32x4_t red[SG][C4];
+    constexpr int C4L = C4 / CS;                 // this workgroup's float4 columns
+    static_assert(C4L * CS == C4 && kCombineThreads % C4L == 0, "whole column slices");
+    constexpr int SG = kCombineThreads / C4L;    // split groups
+    constexpr int U = SG >= 64 ? 1 : 64 / SG;    // splits per thread per batch (64 per batch)
+    __shared__ f32x4_t red[SG][C4L];
 
-    const size_t row = blockIdx.x;
+    const size_t row = blockIdx.x / CS;
+    const int cs = blockIdx.x % CS;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int col = tid % C4, sg = tid / C4;
+    const int lcol = tid % C4L, col = cs * C4L + lcol, sg = tid / C4L;
     // descriptors over the row's max_splits slots (loads past them return zero);
     // split k is slot k of the row
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<const char *>(a.o_parts + row * a.max_splits * D),
@@ -904,12 +911,12 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
             }
         }
     }
-    red[sg][col] = acc;
+    red[sg][lcol] = acc;
     __syncthreads();
     if (sg == 0) {
-        f32x4_t sum = red[0][col];
+        f32x4_t sum = red[0][lcol];
 #pragma unroll
-        for (int s = 1; s < SG; ++s) sum += red[s][col];
+        for (int s = 1; s < SG; ++s) sum += red[s][lcol];
         if (a.o_bf16) {
             uint16_t h[4];
 #pragma unroll
@@ -922,7 +929,7 @@ __global__ __launch_bounds__(kCombineThreads) void lse_combine_kernel(CombineArg
             reinterpret_cast<f32x4_t *>(a.o)[row * C4 + col] = sum;
         }
     }
-    if (tid == 0 && a.lse) a.lse[row] = Lam;
+    if (tid == 0 && cs == 0 && a.lse) a.lse[row] = Lam;
 }
 
 template <int D>
@@ -932,7 +939,8 @@ hipError_t launch_combine(const CombineArgs &c, int rows, hipStream_t stream)
     if (c.bal_gh > 0 && c.seq_lens)
         hipLaunchKernelGGL((lse_combine_kernel<D, true>), dim3((unsigned)rows), dim3(kCombineThreads), 0, stream, c);
     else
-        hipLaunchKernelGGL((lse_combine_kernel<D, false>), dim3((unsigned)rows), dim3(kCombineThreads), 0, stream, c);
+        hipLaunchKernelGGL((lse_combine_kernel<D, false, 2>), dim3((unsigned)rows * 2u), dim3(kCombineThreads), 0, stream,
+                           c);
     return hipGetLastError();
 }
 
